@@ -1,0 +1,433 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: a hand-derived worked example,
+a closed form, an invariant of the mathematics, a library routine, or brute
+force on tiny inputs.  ``test_planted_mistakes_are_caught`` plants plausible
+mistakes into the oracle (on the CPU) and checks that some pin fails for each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+
+RNG = np.random.default_rng(1234)
+
+
+def _rand(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+def _num(x):
+    if isinstance(x, str) and x.startswith("ln"):
+        return math.log(float(x[2:]))
+    return float(x)
+
+
+def _arr(x):
+    return np.array([[_num(e) for e in row] for row in x]) if isinstance(x[0], list) \
+        else np.array([_num(e) for e in x])
+
+
+# --- 1. hand-derived worked example ---------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_worked_example(golden_dir, causal):
+    g = json.load(open(os.path.join(golden_dir, "worked_example_2q2k.json")))
+    q, k, v = _arr(g["q"]), _arr(g["k"]), _arr(g["v"])
+    O, lse = oracle.sdpa(q[None, None], k[None, None], v[None, None], causal, g["scale"])
+    want = g["causal" if causal else "non_causal"]
+    np.testing.assert_allclose(O[0, 0], _arr(want["o"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], _arr(want["lse"]), rtol=0, atol=1e-12)
+
+
+# --- 2. brute force with pure-Python loops --------------------------------
+
+def _brute(q, k, v, causal, scale):
+    """Softmax straight from its definition: e^s / sum e^s, no max shift."""
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    O = [[[[0.0] * d for _ in range(Sq)] for _ in range(Hq)] for _ in range(B)]
+    L = [[[0.0] * Sq for _ in range(Hq)] for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            kv = h * Hkv // Hq
+            for i in range(Sq):
+                ws = []
+                for j in range(Sk):
+                    if causal and j > i + Sk - Sq:
+                        ws.append(0.0)
+                        continue
+                    s = sum(q[b, h, i, t] * k[b, kv, j, t] for t in range(d)) * scale
+                    ws.append(math.exp(s))
+                tot = sum(ws)
+                if tot == 0.0:
+                    L[b][h][i] = -math.inf
+                    continue
+                L[b][h][i] = math.log(tot)
+                for c in range(d):
+                    O[b][h][i][c] = sum(ws[j] * v[b, kv, j, c] for j in range(Sk)) / tot
+    return np.array(O), np.array(L)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,Sk,d", [(1, 1, 1, 5, 5, 3), (2, 4, 2, 4, 6, 2),
+                                               (1, 3, 1, 6, 4, 4), (1, 2, 2, 1, 7, 3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(B, Hq, Hkv, Sq, Sk, d, causal):
+    rng = np.random.default_rng(B * 100 + Sq * 10 + Sk)
+    q, k, v = (rng.standard_normal(s) for s in [(B, Hq, Sq, d), (B, Hkv, Sk, d), (B, Hkv, Sk, d)])
+    scale = 0.7
+    O, lse = oracle.sdpa(q, k, v, causal, scale)
+    Ob, Lb = _brute(q, k, v, causal, scale)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(Lb))
+    fin = np.isfinite(Lb)
+    np.testing.assert_allclose(lse[fin], Lb[fin], rtol=0, atol=1e-12)
+
+
+# --- 3. library routines --------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Sq,Sk", [(16, 16), (8, 24)])
+def test_matches_torch_sdpa_and_scipy_logsumexp(causal, Sq, Sk):
+    torch = pytest.importorskip("torch")
+    from scipy.special import logsumexp
+    B, Hq, Hkv, d = 2, 4, 2, 8
+    q, k, v = _rand(B, Hq, Sq, d), _rand(B, Hkv, Sk, d), _rand(B, Hkv, Sk, d)
+    scale = 1 / math.sqrt(d)
+    O, lse = oracle.sdpa(q, k, v, causal, scale)
+    g = Hq // Hkv
+    kr, vr = np.repeat(k, g, axis=1), np.repeat(v, g, axis=1)
+    mask = None
+    if causal:
+        i, j = np.arange(Sq)[:, None], np.arange(Sk)[None, :]
+        mask = torch.from_numpy(j <= i + (Sk - Sq))
+    To = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(kr), torch.from_numpy(vr),
+        attn_mask=mask, scale=scale).numpy()
+    np.testing.assert_allclose(O, To, rtol=0, atol=1e-12)
+    S = scale * np.einsum("bhid,bhjd->bhij", q, kr)
+    if causal:
+        S = np.where(mask.numpy(), S, -np.inf)
+    np.testing.assert_allclose(lse, logsumexp(S, axis=-1), rtol=0, atol=1e-12)
+
+
+# --- 4. closed forms ------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    q, k, v = _rand(1, 2, 9, 4), _rand(1, 2, 9, 4), _rand(1, 2, 9, 4)
+    _, _, P = oracle.sdpa(q, k, v, causal, 0.5, return_probs=True)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-12)
+    assert (P >= 0).all()
+    if causal:
+        assert (P[..., np.triu_indices(9, 1)[0], np.triu_indices(9, 1)[1]] == 0).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_ones_values_give_all_ones(causal):
+    q, k = _rand(2, 4, 11, 8) * 3, _rand(2, 2, 11, 8) * 3
+    O, _ = oracle.sdpa(q, k, np.ones((2, 2, 11, 8)), causal, 0.4)
+    np.testing.assert_allclose(O, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_mean_of_visible_values(causal):
+    Sq = Sk = 13
+    v = _rand(1, 1, Sk, 5)
+    O, lse = oracle.sdpa(np.zeros((1, 1, Sq, 5)), _rand(1, 1, Sk, 5), v, causal, 1.0)
+    if causal:
+        counts = np.arange(1, Sq + 1)
+        want = np.cumsum(v[0, 0], axis=0) / counts[:, None]
+    else:
+        counts = np.full(Sq, Sk)
+        want = np.broadcast_to(v[0, 0].mean(0), (Sq, 5))
+    np.testing.assert_allclose(O[0, 0], want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], np.log(counts), rtol=0, atol=1e-12)
+
+
+def test_causal_first_row_is_first_value():
+    q, k, v = _rand(2, 3, 7, 6), _rand(2, 3, 7, 6), _rand(2, 3, 7, 6)
+    O, lse = oracle.sdpa(q, k, v, True, 0.3)
+    np.testing.assert_array_equal(O[:, :, 0], v[:, :, 0])
+    np.testing.assert_allclose(lse[:, :, 0], 0.3 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=0, atol=1e-12)
+
+
+def test_dominant_key_returns_its_value_within_bound():
+    Sk, d = 20, 8
+    q, k, v = _rand(1, 1, 4, d), _rand(1, 1, Sk, d), _rand(1, 1, Sk, d)
+    i, jstar, scale = 2, 13, 1.0
+    k[0, 0, jstar] = 12.0 * q[0, 0, i]
+    O, _ = oracle.sdpa(q, k, v, False, scale)
+    s = scale * k[0, 0] @ q[0, 0, i]
+    gaps = s[jstar] - np.delete(s, jstar)
+    assert gaps.min() > 10
+    bound = 2 * np.abs(v).max() * np.exp(-gaps).sum()
+    assert np.abs(O[0, 0, i] - v[0, 0, jstar]).max() <= bound
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_common_key_shift_moves_only_lse(causal):
+    """Adding u to every key adds scale*q.u to a row's scores: O is unchanged."""
+    q, k, v = _rand(1, 2, 10, 6), _rand(1, 2, 10, 6), _rand(1, 2, 10, 6)
+    u = 150.0 * _rand(6)                      # scores of order 1e3
+    O0, l0 = oracle.sdpa(q, k, v, causal, 1.0)
+    O1, l1 = oracle.sdpa(q, k + u, v, causal, 1.0)
+    np.testing.assert_allclose(O1, O0, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(l1, l0 + q @ u, rtol=1e-12, atol=1e-9)
+
+
+# --- 5. grouped-query attention -------------------------------------------
+
+def test_kv_head_mapping_table():
+    assert [oracle.kv_head_of(h, 32, 8) for h in range(32)] == [h // 4 for h in range(32)]
+    assert [oracle.kv_head_of(h, 6, 6) for h in range(6)] == list(range(6))      # MHA
+    assert [oracle.kv_head_of(h, 6, 1) for h in range(6)] == [0] * 6              # MQA
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 8), (8, 1)])
+def test_gqa_groups_read_their_own_kv_head(Hq, Hkv):
+    """V constant per K/V head: each query head's output names its K/V head."""
+    v = np.broadcast_to(np.arange(1, Hkv + 1, dtype=float)[None, :, None, None], (1, Hkv, 9, 4)).copy()
+    O, _ = oracle.sdpa(_rand(1, Hq, 9, 4), _rand(1, Hkv, 9, 4), v, True, 0.5)
+    want = np.array([h // (Hq // Hkv) + 1 for h in range(Hq)], dtype=float)
+    np.testing.assert_allclose(O, np.broadcast_to(want[None, :, None, None], O.shape), rtol=0, atol=1e-12)
+
+
+def test_gqa_equals_mha_on_repeated_heads():
+    q, k, v = _rand(2, 8, 6, 4), _rand(2, 2, 6, 4), _rand(2, 2, 6, 4)
+    O, l = oracle.sdpa(q, k, v, True, 0.5)
+    O2, l2 = oracle.sdpa(q, np.repeat(k, 4, axis=1), np.repeat(v, 4, axis=1), True, 0.5)
+    np.testing.assert_array_equal(O, O2)
+    np.testing.assert_array_equal(l, l2)
+
+
+# --- 6. online softmax twins (block size must not matter) ------------------
+
+@pytest.mark.parametrize("fn", [oracle.online_softmax_normalised, oracle.online_softmax_deferred])
+@pytest.mark.parametrize("block", [1, 3, 7, 32])
+@pytest.mark.parametrize("Sq,Sk,causal", [(17, 17, True), (17, 17, False), (20, 12, True), (9, 25, True)])
+def test_online_softmax_equals_definition(fn, block, Sq, Sk, causal):
+    q, k, v = _rand(Sq, 5), _rand(Sk, 5), _rand(Sk, 5)
+    O, lse = fn(q, k, v, block, causal, 0.6)
+    Od, ld = oracle.sdpa(q[None, None], k[None, None], v[None, None], causal, 0.6)
+    np.testing.assert_allclose(O, Od[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(ld[0, 0]))
+    f = np.isfinite(lse)
+    np.testing.assert_allclose(lse[f], ld[0, 0][f], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("fn", [oracle.online_softmax_normalised, oracle.online_softmax_deferred])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_online_softmax_handles_large_logits(fn, dtype):
+    """Scores near 1e3 would overflow e^s in either precision without the max shift."""
+    q, k, v = (_rand(8, 4) * 40).astype(dtype), (_rand(8, 4) * 40).astype(dtype), _rand(8, 4)
+    O, lse = fn(q, k, v, 3, True, 1.0)
+    assert np.isfinite(O).all() and np.isfinite(lse).all()
+    s = np.where(np.tril(np.ones((8, 8), bool)), q.astype(float) @ k.astype(float).T, -np.inf)
+    assert np.abs(s[np.isfinite(s)]).max() > 500
+    from scipy.special import logsumexp, softmax
+    np.testing.assert_allclose(lse, logsumexp(s, axis=1), rtol=1e-12, atol=1e-9)
+    np.testing.assert_allclose(O, softmax(s, axis=1) @ v, rtol=0, atol=1e-9)
+
+
+def test_fully_masked_rows_are_zero_with_minus_inf_lse():
+    q, k, v = _rand(1, 1, 6, 3), _rand(1, 1, 2, 3), _rand(1, 1, 2, 3)
+    O, lse = oracle.sdpa(q, k, v, True, 1.0)           # rows 0..3 see no key
+    assert not np.isnan(O).any() and not np.isnan(lse).any()
+    np.testing.assert_array_equal(O[0, 0, :4], 0.0)
+    assert np.isneginf(lse[0, 0, :4]).all() and np.isfinite(lse[0, 0, 4:]).all()
+    np.testing.assert_array_equal(O[0, 0, 4], v[0, 0, 0])
+
+
+def test_sdpa_rows_match_brute_force():
+    q, k, v = _rand(1, 2, 12, 3), _rand(1, 1, 12, 3), _rand(1, 1, 12, 3)
+    rows = np.array([[[0, 5, 11], [2, 3, 7]]])
+    O, lse = oracle.sdpa_rows(q, k, v, rows, True, 0.8)
+    Ob, Lb = _brute(q, k, v, True, 0.8)
+    for h in range(2):
+        np.testing.assert_allclose(O[0, h], Ob[0, h, rows[0, h]], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], Lb[0, h, rows[0, h]], rtol=0, atol=1e-12)
+
+
+# --- 7. split ranges and their merge --------------------------------------
+
+@pytest.mark.parametrize("bounds", [[(0, 40)], [(0, 13), (13, 14), (14, 40)],
+                                    [(0, 0), (0, 20), (20, 20), (20, 40)]])
+def test_merge_of_split_ranges_equals_whole(bounds):
+    q, k, v = _rand(3, 6), _rand(40, 6), _rand(40, 6)
+    o, lse = oracle.merge_partials(oracle.split_partials(q, k, v, bounds, 0.4))
+    Od, ld = oracle.sdpa(q[None, None], k[None, None], v[None, None], False, 0.4)
+    np.testing.assert_allclose(o, Od[0, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ld[0, 0], rtol=0, atol=1e-12)
+
+
+def test_merge_of_empty_ranges_is_zero():
+    q, k, v = _rand(2, 4), _rand(5, 4), _rand(5, 4)
+    o, lse = oracle.merge_partials(oracle.split_partials(q, k, v, [(0, 0), (3, 3)], 1.0))
+    np.testing.assert_array_equal(o, 0.0)
+    assert np.isneginf(lse).all()
+
+
+# --- 8. paged decode ------------------------------------------------------
+
+def _paged(n_lens, Hkv, d, bs, rng):
+    """A small paged cache plus the contiguous K/V it stores."""
+    pages = [-(-n // bs) for n in n_lens]
+    nb = sum(pages)
+    perm = rng.permutation(nb)
+    table = np.full((len(n_lens), max(pages)), -1, dtype=np.int32)
+    kc, vc = rng.standard_normal((nb, Hkv, bs, d)), rng.standard_normal((nb, Hkv, bs, d))
+    c = 0
+    for s, p in enumerate(pages):
+        table[s, :p] = perm[c:c + p]
+        c += p
+    return kc, vc, table
+
+
+def test_paged_decode_equals_contiguous_attention():
+    rng = np.random.default_rng(7)
+    lens, Hq, Hkv, d, bs = [37, 16, 1, 50], 6, 2, 4, 16
+    kc, vc, table = _paged(lens, Hkv, d, bs, rng)
+    q = rng.standard_normal((len(lens), Hq, d))
+    o, lse = oracle.paged_decode(q, kc, vc, table, np.array(lens), 0.5)
+    for s, n in enumerate(lens):
+        p = -(-n // bs)
+        K = kc[table[s, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+        V = vc[table[s, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+        Od, ld = oracle.sdpa(q[s][None, :, None], K[None], V[None], False, 0.5)
+        np.testing.assert_allclose(o[s], Od[0, :, 0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[s], ld[0, :, 0], rtol=0, atol=1e-12)
+
+
+def test_paged_decode_ignores_physical_placement():
+    rng = np.random.default_rng(8)
+    lens = [33, 70]
+    kc, vc, table = _paged(lens, 1, 3, 16, rng)
+    q = rng.standard_normal((2, 2, 3))
+    o, lse = oracle.paged_decode(q, kc, vc, table, np.array(lens), 1.0)
+    perm = rng.permutation(kc.shape[0])                  # new home of block b is perm[b]
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[perm], vc2[perm] = kc, vc
+    table2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    o2, lse2 = oracle.paged_decode(q, kc2, vc2, table2, np.array(lens), 1.0)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_paged_decode_is_last_row_of_causal_prefill():
+    rng = np.random.default_rng(9)
+    n, Hq, Hkv, d, bs = 45, 4, 2, 4, 16
+    kc, vc, table = _paged([n], Hkv, d, bs, rng)
+    p = -(-n // bs)
+    K = kc[table[0, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+    V = vc[table[0, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+    Q = rng.standard_normal((1, Hq, n, d))
+    O, L = oracle.sdpa(Q, K[None], V[None], True, 0.5)
+    o, lse = oracle.paged_decode(Q[:, :, -1], kc, vc, table, np.array([n]), 0.5)
+    np.testing.assert_allclose(o[0], O[0, :, -1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], L[0, :, -1], rtol=0, atol=1e-12)
+
+
+def test_paged_decode_dominant_key_finds_its_logical_position():
+    """A marker key at logical token 21 (page 1, slot 5) must return V at token 21."""
+    rng = np.random.default_rng(10)
+    n, bs, d = 40, 16, 4
+    kc, vc, table = _paged([n], 1, d, bs, rng)
+    q = rng.standard_normal((1, 1, d))
+    kc[table[0, 1], 0, 5] = 60.0 * q[0, 0] / (q[0, 0] @ q[0, 0])     # score exactly 60
+    o, _ = oracle.paged_decode(q, kc, vc, table, np.array([n]), 1.0)
+    K = kc[table[0, :3], 0].reshape(-1, d)[:n]
+    s = K @ q[0, 0]
+    gaps = 60.0 - np.delete(s, 21)
+    assert gaps.min() > 20
+    bound = 2 * np.abs(vc).max() * np.exp(-gaps).sum()
+    assert np.abs(o[0, 0] - vc[table[0, 1], 0, 5]).max() <= bound
+
+
+def test_paged_decode_empty_sequence():
+    rng = np.random.default_rng(11)
+    kc, vc, table = _paged([16], 1, 3, 16, rng)
+    o, lse = oracle.paged_decode(rng.standard_normal((2, 1, 3)), kc, vc,
+                                 np.vstack([table, table]), np.array([16, 0]), 1.0)
+    np.testing.assert_array_equal(o[1], 0.0)
+    assert np.isneginf(lse[1]).all() and np.isfinite(lse[0]).all()
+
+
+# --- 9. the pins catch planted mistakes -----------------------------------
+
+def _run_pins(golden_dir):
+    """Run a representative set of pins; return the names of those that fail."""
+    failed = []
+    checks = {
+        "worked_nc": lambda: test_worked_example(golden_dir, False),
+        "worked_c": lambda: test_worked_example(golden_dir, True),
+        "first_row": test_causal_first_row_is_first_value,
+        "gqa": lambda: test_gqa_groups_read_their_own_kv_head(8, 2),
+        "zero_q": lambda: test_zero_query_gives_mean_of_visible_values(True),
+        "shift": lambda: test_common_key_shift_moves_only_lse(True),
+        "decode": test_paged_decode_equals_contiguous_attention,
+        "marker": test_paged_decode_dominant_key_finds_its_logical_position,
+        "brute": lambda: test_brute_force_tiny(1, 3, 1, 6, 4, 4, True),
+    }
+    for name, fn in checks.items():
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_the_oracle(golden_dir):
+    assert _run_pins(golden_dir) == []
+
+
+def _attend_no_scale(q, k, v, vis, scale):
+    return _orig_attend(q, k, v, vis, 1.0)
+
+
+def _attend_transposed_mask(q, k, v, vis, scale):
+    if vis.shape[0] == vis.shape[1] and not vis.all():
+        vis = vis.T
+    return _orig_attend(q, k, v, vis, scale)
+
+
+def _attend_kv_swapped(q, k, v, vis, scale):
+    return _orig_attend(q, v, k, vis, scale)
+
+
+def _attend_lse_log2(q, k, v, vis, scale):
+    O, lse, P = _orig_attend(q, k, v, vis, scale)
+    return O, lse / math.log(2.0), P
+
+
+_orig_attend = oa._attend
+
+
+@pytest.mark.parametrize("mutant,attr", [
+    (_attend_no_scale, "_attend"),
+    (_attend_transposed_mask, "_attend"),
+    (_attend_kv_swapped, "_attend"),
+    (_attend_lse_log2, "_attend"),
+    (lambda hq, Hq, Hkv: hq % Hkv, "kv_head_of"),
+    (lambda rows, Sq, Sk, causal: oa._orig_visible(rows, Sk, Sq, causal), "_visible"),
+    (lambda rows, Sq, Sk, causal: np.arange(Sk)[None, :] <= np.asarray(rows)[:, None] if causal
+     else np.ones((len(rows), Sk), bool), "_visible"),
+])
+def test_planted_mistakes_are_caught(monkeypatch, golden_dir, mutant, attr):
+    oa._orig_visible = _orig_visible
+    monkeypatch.setattr(oa, attr, mutant)
+    if attr == "kv_head_of":
+        monkeypatch.setattr(oracle, "kv_head_of", mutant)
+    assert _run_pins(golden_dir), f"no pin caught the planted mistake in {attr}"
+
+
+_orig_visible = oa._visible
