@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact tiled attention hot path on one MI355X.
+
+One step runs the whole path once on resident synthetic inputs:
+
+  * fp32 prefill, B=1 H=1 S=128 d=64, non-causal (correctness-sized; launch bound)
+  * bf16 causal prefill, B=2 H=16 S=2048 d=128 (the headline workload)
+  * bf16 paged decode, 64 sequences x 1 token, Hq=32 Hkv=8 d=128, 16-token
+    pages, lengths uniform in [1024, 8192]
+
+Each kernel launch is bracketed by HIP events on the stream it runs on.  The
+headline `value` is the algorithmic TFLOP/s of the causal prefill (4 d FLOP per
+visible query-key pair) over the prefill launch time; decode reports the
+algorithmic KV bytes (each attended token's K and V once) over the decode
+launch time.  Before each decode launch a 512 MiB buffer is written so that
+neither L2 nor the 256 MB Infinity Cache holds cache lines from the last step
+(outside the decode's own events).  The fp64 CPU oracle is timed on a bounded
+sample of the prefill workload as a reported baseline.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+PREFILL = "causal_mha_b2_h16_s2048_d128"
+DECODE = "paged_decode_64seq_h32kv8_d128"
+FP32 = "mha1_s128_d64_f32"
+EXTRA = ["causal_gqa_h32kv8_s8192_d128_outliers", "causal_gqa_h32kv8_s32768_d128"]
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads of the prefill workload the oracle times")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1:
+        sys.exit("--steps must be >= 1")
+
+    import numpy as np
+    import torch
+
+    from exact_tiled_attention_14_amd import binding, inputs, metrics
+
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    dev = torch.device("cuda:0")
+    binding.load()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    # ---- inputs, built on the host by the seeded generator, copied once ----
+    log("generating inputs")
+    cf = inputs.workload(FP32)
+    f_q, f_k, f_v = (torch.from_numpy(getattr(cf, n)).to(dev) for n in "qkv")
+    f_o, f_l = torch.empty_like(f_q), torch.empty(cf.q.shape[:3], dtype=torch.float32, device=dev)
+
+    cp = inputs.workload(PREFILL)
+    shp = cp.shape
+    p_q, p_k, p_v = to_dev(cp.bits("q")), to_dev(cp.bits("k")), to_dev(cp.bits("v"))
+    p_o = torch.empty_like(p_q)
+    p_l = torch.empty((shp["B"], shp["Hq"], shp["Sq"]), dtype=torch.float32, device=dev)
+    log("prefill inputs ready")
+
+    cd = inputs.workload(DECODE)
+    dshp = cd.shape
+    d_q = to_dev(cd.bits("q"))
+    d_kc, d_vc = to_dev(cd.kcache_bits), to_dev(cd.vcache_bits)
+    d_bt = torch.from_numpy(cd.block_table).to(dev)
+    d_sl = torch.from_numpy(cd.seqlens).to(dev)
+    d_o = torch.empty_like(d_q)
+    d_l = torch.empty((dshp["nseq"], dshp["Hq"]), dtype=torch.float32, device=dev)
+    ws_bytes = binding.fa_decode_workspace_size(dshp["nseq"], dshp["Hq"], dshp["Hkv"], dshp["d"],
+                                                dshp["block_size"], dshp["max_blocks"])
+    d_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    log("decode inputs ready")
+
+    def run_f32():
+        binding.fa_fwd(f_q, f_k, f_v, cf.causal, cf.scale, out=f_o, lse=f_l)
+
+    def run_prefill():
+        binding.fa_fwd(p_q, p_k, p_v, True, cp.scale, out=p_o, lse=p_l)
+
+    def run_decode():
+        binding.fa_decode(d_q, d_kc, d_vc, d_bt, d_sl, cd.scale, out=d_o, lse=d_l, workspace=d_ws)
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        run_f32()
+        run_prefill()
+        flush.fill_(1)
+        run_decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    e_f = [(ev(), ev()) for _ in range(K)]
+    e_p = [(ev(), ev()) for _ in range(K)]
+    e_d = [(ev(), ev()) for _ in range(K)]
+    t_start, t_end = ev(), ev()
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(K):
+        e_f[i][0].record(stream)
+        run_f32()
+        e_f[i][1].record(stream)
+        e_p[i][0].record(stream)
+        run_prefill()
+        e_p[i][1].record(stream)
+        flush.fill_(i & 0xFF)
+        e_d[i][0].record(stream)
+        run_decode()
+        e_d[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    ms_f = [a.elapsed_time(b) for a, b in e_f]
+    ms_p = [a.elapsed_time(b) for a, b in e_p]
+    ms_d = [a.elapsed_time(b) for a, b in e_d]
+    sp, sd, sf = metrics.summarize(ms_p), metrics.summarize(ms_d), metrics.summarize(ms_f)
+
+    flops_p = metrics.prefill_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
+    tflops_p = flops_p / (sp["mean"] * 1e-3) / 1e12
+    kv_bytes = metrics.decode_kv_bytes(cd.seqlens, dshp["Hkv"], dshp["d"])
+    gbs_d = kv_bytes / (sd["mean"] * 1e-3) / 1e9
+    peak_tf = metrics.MI355X_BF16_DENSE_FLOPS / 1e12
+    peak_gb = metrics.MI355X_HBM_BYTES_PER_S / 1e9
+    log(f"prefill {sp['mean']*1e3:.1f} us -> {tflops_p:.1f} TFLOP/s; decode {sd['mean']*1e3:.1f} us -> "
+        f"{gbs_d:.0f} GB/s; fp32 {sf['mean']*1e3:.1f} us; step {ms_step:.3f} ms")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops_p, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16-rounded; paged cache with seeded lengths and block permutation)",
+        "config": {
+            "workload": PREFILL, "B": shp["B"], "Hq": shp["Hq"], "Hkv": shp["Hkv"], "S": shp["Sq"],
+            "d": shp["d"], "causal": True,
+            "step_also_runs": [FP32, DECODE],
+        },
+        "roofline": {
+            "kernel": "fwd_bf16_kernel<128,causal>",
+            "bound": "mfma",
+            "achieved": round(tflops_p, 2),
+            "peak": peak_tf,
+            "unit": "TFLOP/s",
+            "frac": round(tflops_p / peak_tf, 4),
+            "traffic": None,
+            "algorithmic_flops_per_launch": flops_p,
+            "launch_us": {k: round(v * 1e3, 2) for k, v in sp.items() if k != "n"},
+        },
+        "decode": {
+            "workload": DECODE,
+            "kernels": "decode_partial_kernel<4> + decode_combine_kernel",
+            "bound": "hbm",
+            "achieved": round(gbs_d, 1),
+            "peak": peak_gb,
+            "unit": "GB/s",
+            "frac": round(gbs_d / peak_gb, 4),
+            "traffic": None,
+            "algorithmic_kv_bytes_per_launch": kv_bytes,
+            "kv_tokens": cd.kv_tokens,
+            "launch_us": {k: round(v * 1e3, 2) for k, v in sd.items() if k != "n"},
+        },
+        "fp32_prefill_us": round(sf["mean"] * 1e3, 2),
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    # ---- larger prefill workloads, timed on their own ----
+    if not args.no_extra:
+        extra = {}
+        for name in EXTRA:
+            spec = dict(inputs.WORKLOADS[name])
+            log(f"generating {name}")
+            c = inputs.workload(name)
+            s = c.shape
+            q, k, v = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
+            del c
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            scale = 1.0 / math.sqrt(s["d"])
+            for _ in range(2):
+                binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
+            reps = max(3, min(K, 10))
+            evs = [(ev(), ev()) for _ in range(reps)]
+            torch.cuda.synchronize()
+            for a, b in evs:
+                a.record(stream)
+                binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
+                b.record(stream)
+            torch.cuda.synchronize()
+            st = metrics.summarize([a.elapsed_time(b) for a, b in evs])
+            fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
+            tf = fl / (st["mean"] * 1e-3) / 1e12
+            extra[name] = {"us": round(st["mean"] * 1e3, 1), "TFLOP/s": round(tf, 1),
+                           "frac_bf16_peak": round(tf / peak_tf, 4), "reps": reps, "causal": spec["causal"]}
+            log(f"{name}: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+        result["extra_prefill"] = extra
+
+    # ---- the fp64 oracle on the host, a bounded sample of the prefill workload ----
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((p.get("num_threads", 1) for p in threadpool_info()
+                           if p.get("user_api") == "blas"), default=1)
+        except Exception:  # threadpoolctl missing or no BLAS reported
+            threads = os.cpu_count() or 1
+        h = max(1, min(args.cpu_heads, shp["Hq"]))
+        log(f"timing the fp64 oracle on {h} heads")
+        t0 = time.perf_counter()
+        oracle.sdpa(cp.q[:1, :h], cp.k[:1, :h], cp.v[:1, :h], True, cp.scale)
+        dt = time.perf_counter() - t0
+        fl = metrics.prefill_flops(1, h, shp["Sq"], shp["Sk"], shp["d"], True)
+        result["cpu_baseline"] = {
+            "value": round(fl / dt / 1e12, 6),
+            "unit": "TFLOP/s",
+            "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"batch 0, heads 0..{h - 1} of {PREFILL} (all {shp['Sq']} rows), fp64 NumPy, "
+                      f"{dt:.2f} s; algorithmic causal FLOPs of the sample over wall time",
+            "host_cpus": os.cpu_count(),
+        }
+        log(f"oracle: {dt:.2f} s for {h} heads")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

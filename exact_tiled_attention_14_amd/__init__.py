@@ -12,6 +12,7 @@ __all__ = ["binding", "inputs", "metrics"]
 def __getattr__(name):
     # The binding loads the HIP library; import it only when asked for.
     if name in ("binding", "fa_fwd", "fa_decode", "fa_decode_workspace_size", "fa_status_string"):
-        from . import binding
-        return binding if name == "binding" else getattr(binding, name)
+        import importlib
+        mod = importlib.import_module(f"{__name__}.binding")
+        return mod if name == "binding" else getattr(mod, name)
     raise AttributeError(name)

@@ -1,0 +1,173 @@
+"""Python binding of the C ABI in ``include/fa.h`` (argument marshalling only).
+
+Every function here has the name of the C entry point it calls.  PyTorch
+supplies device memory and the current stream; all arithmetic runs in the
+HIP kernels of ``libfa.so``.  There is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # must precede the library load: it brings up the HIP runtime libfa.so binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = 0, -1, -2, -3, -4
+FA_BF16, FA_F32 = 0, 1
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero fa_status returned by the library."""
+
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status} ({fa_status_string(status)})")
+        self.status = status
+
+
+def load() -> ctypes.CDLL:
+    """Load ``libfa.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m exact_tiled_attention_14_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load().fa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, ndim, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fa_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None,
+           return_lse: bool = True):
+    """Attention forward: q [B,Hq,Sq,d], k/v [B,Hkv,Sk,d] (bf16 or fp32).
+
+    Returns ``(o, lse)``; ``lse`` is [B,Hq,Sq] fp32 (None if not requested).
+    """
+    lib = load()
+    dtype = q.dtype
+    if dtype == torch.bfloat16:
+        code = FA_BF16
+    elif dtype == torch.float32:
+        code = FA_F32
+    else:
+        raise TypeError(f"unsupported dtype {dtype}")
+    _check(q, "q", dtype, 4)
+    _check(k, "k", dtype, 4, q.device)
+    _check(v, "v", dtype, 4, q.device)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k={tuple(k.shape)} v={tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", dtype, 4, q.device)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 3, q.device)
+        if tuple(lse.shape) != (B, Hq, Sq):
+            raise ValueError("lse must be [B, Hq, Sq]")
+    st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
+                    int(bool(causal)), float(scale), code, _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd", st)
+    return out, lse
+
+
+def fa_decode_workspace_size(nseq: int, Hq: int, Hkv: int, d: int, block_size: int,
+                             max_blocks_per_seq: int) -> int:
+    return int(load().fa_decode_workspace_size(nseq, Hq, Hkv, d, block_size, max_blocks_per_seq))
+
+
+def fa_decode(q, kcache, vcache, block_table, seqlens, scale: float | None = None, out=None,
+              lse=None, workspace=None, return_lse: bool = True):
+    """Single-token decode over a paged cache.
+
+    q [nseq,Hq,d] bf16; kcache/vcache [num_blocks,Hkv,block_size,d] bf16;
+    block_table [nseq,max_blocks] int32; seqlens [nseq] int32.
+    Returns ``(o [nseq,Hq,d] bf16, lse [nseq,Hq] fp32 or None)``.
+    """
+    lib = load()
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(kcache, "kcache", torch.bfloat16, 4, dev)
+    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    _check(block_table, "block_table", torch.int32, 2, dev)
+    _check(seqlens, "seqlens", torch.int32, 1, dev)
+    nseq, Hq, d = q.shape
+    num_blocks, Hkv, bs, d2 = kcache.shape
+    if vcache.shape != kcache.shape or d2 != d:
+        raise ValueError("cache shape mismatch")
+    if block_table.shape[0] != nseq or seqlens.shape[0] != nseq:
+        raise ValueError("block_table / seqlens must have nseq rows")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_workspace_size(nseq, Hq, Hkv, d, bs, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev:
+        raise ValueError("workspace must be on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+    if lse is None and return_lse:
+        lse = torch.empty((nseq, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _check(lse, "lse", torch.float32, 2, dev)
+    st = lib.fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens),
+                       _ptr(out), _ptr(lse), nseq, Hq, Hkv, d, bs, max_blocks, num_blocks,
+                       float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                       _stream(dev))
+    if st != FA_OK:
+        raise FAError("fa_decode", st)
+    return out, lse

@@ -1,0 +1,111 @@
+// The C ABI declared in include/fa.h: host-side validation and dispatch.
+// Nothing here allocates, frees or synchronises; every launch goes to the
+// caller's stream.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Elements of a tensor must fit the 64-bit offsets the kernels use.
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+    const int64_t lim = INT64_MAX / 4;
+    int64_t x = a;
+    for (int64_t y : {b, c, d}) {
+        if (y != 0 && x > lim / y) return false;
+        x *= y;
+    }
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+        case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+        case FA_ERR_HIP: return "FA_ERR_HIP";
+        default: return "FA_UNKNOWN_STATUS";
+    }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+           int Sq, int Sk, int d, int causal, float scale, int dtype, void* stream) {
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk, d)) return FA_ERR_INVALID_ARG;
+    if (dtype == FA_BF16) {
+        if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    } else if (dtype == FA_F32) {
+        if (d != 32 && d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    } else {
+        return FA_ERR_INVALID_ARG;
+    }
+    // The grid is one workgroup per (batch, query head, query block).
+    const int64_t rows_per_wg = dtype == FA_BF16 ? 128 : 64;
+    if ((int64_t)B * Hq * ((Sq + rows_per_wg - 1) / rows_per_wg) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_decode_workspace_size(int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq) {
+    if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1) return 0;
+    if (d != 128 || block_size != 16) return 0;
+    const fa::DecodePlan pl = fa::plan_decode(nseq, Hq, Hkv, max_blocks_per_seq);
+    // partial outputs, then partial lse, each starting on a 256-byte boundary
+    const size_t o_bytes = ((size_t)pl.ws_o_elems * 4 + 255) & ~(size_t)255;
+    const size_t l_bytes = ((size_t)pl.ws_lse_elems * 4 + 255) & ~(size_t)255;
+    return o_bytes + l_bytes;
+}
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+              const int32_t* seqlens, void* o, float* lse, int nseq, int Hq, int Hkv, int d, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    if (!q || !kcache || !vcache || !block_table || !seqlens || !o) return FA_ERR_INVALID_ARG;
+    if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (d != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
+    const int g = Hq / Hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8) return FA_ERR_UNSUPPORTED;
+    if (nseq > 65535 || Hkv > 65535) return FA_ERR_UNSUPPORTED;   // grid y / z limits
+    if (!fits(num_blocks, Hkv, block_size, d) || (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return FA_ERR_INVALID_ARG;
+
+    const size_t need = fa_decode_workspace_size(nseq, Hq, Hkv, d, block_size, max_blocks_per_seq);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
+
+    fa::DecodePlan pl = fa::plan_decode(nseq, Hq, Hkv, max_blocks_per_seq);
+    const size_t o_bytes = ((size_t)pl.ws_o_elems * 4 + 255) & ~(size_t)255;
+    pl.ws_o = static_cast<float*>(workspace);
+    pl.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+
+    fa::DecodeArgs a{q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, max_blocks_per_seq,
+                     num_blocks, scale};
+    const hipError_t e = fa::launch_decode(a, pl, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Device-side helpers shared by the attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kNegInf = -__builtin_inff();
+
+// v_exp_f32: 2^x; 2^(-inf) = 0.
+__device__ __forceinline__ float exp2f_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// v_log_f32: log2(x); log2(0) = -inf.
+__device__ __forceinline__ float log2f_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// bf16 bit pattern -> the equal fp32 value.
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 values -> two bf16 (round to nearest even) packed low-first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 32x32x16 bf16 matrix-core product with fp32 accumulation, D = A B + C.
+// Operand a: lane l holds row (l % 32) of A, 8 contraction elements; operand b:
+// lane l holds column (l % 32) of B, the same 8 contraction elements.  The
+// accumulator holds D[i][j] in lane j + 32 * ((i / 4) % 2), register
+// 4 * (i / 8) + i % 4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (lane % 32 is the column) index of accumulator register r in lane half h.
+__device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+}  // namespace fa
