@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per inner step
+constexpr float kTau = 8.f;       // log2 of the growth allowed before a rescale
 
 template <int D>
 struct Tile {
@@ -84,7 +85,10 @@ __device__ __forceinline__ void load_kv(Staged<D>& st, const uint16_t* __restric
         st.k[c] = key < Sk ? val : u32x4{0, 0, 0, 0};
     }
     if (tid < Tile<D>::VGROUPS) {
-        const int cg = tid % (D / 8), kg = tid / (D / 8);
+        // Key group fastest across lanes: the transposed LDS write of one
+        // instruction then fills whole V^T rows (no bank conflicts), at the
+        // price of 64-byte rather than 256-byte contiguous global segments.
+        const int kg = tid % (kBN / 4), cg = tid / (kBN / 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int key = kv0 + 4 * kg + i;
@@ -105,7 +109,7 @@ __device__ __forceinline__ void store_kv(const Staged<D>& st, uint16_t* stage, i
         *reinterpret_cast<u32x4*>(kt + row * Tile<D>::KSTR + col * 8) = st.k[c];
     }
     if (tid < Tile<D>::VGROUPS) {
-        const int cg = tid % (D / 8), kg = tid / (D / 8);
+        const int kg = tid % (kBN / 4), cg = tid / (kBN / 4);
         uint16_t* dst = vt + (cg * 8) * Tile<D>::VSTR + vt_slot(kg);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -203,15 +207,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         const bool more = it + 1 < n_it;
         if (more) load_kv<D>(st, Kh, Vh, kv0 + kBN, Sk, tid);
 
-        // ---- S^T = K_j Q^T: two 32-key blocks ----
-        f32x16 sacc[2];
+        // ---- S^T = K_j Q^T: two 32-key blocks, their chains interleaved ----
+        // LDS operand reads run two steps ahead of the matrix-core ops that
+        // use them; the scheduling fences keep the compiler from sinking
+        // each read next to its use.
+        f32x16 sacc[2] = {f32x16{}, f32x16{}};
+        {
+            const uint16_t* kr0 = kt + l32 * T::KSTR + 8 * hh;
+            const uint16_t* kr1 = kr0 + 32 * T::KSTR;
+            constexpr int NS = D / 16;
+            bf16x8 ka[3][2];
+            ka[0][0] = *reinterpret_cast<const bf16x8*>(kr0);
+            ka[0][1] = *reinterpret_cast<const bf16x8*>(kr1);
+            ka[1][0] = *reinterpret_cast<const bf16x8*>(kr0 + 16);
+            ka[1][1] = *reinterpret_cast<const bf16x8*>(kr1 + 16);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            sacc[blk] = f32x16{};
-            const uint16_t* kr = kt + (32 * blk + l32) * T::KSTR + 8 * hh;
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s)
-                sacc[blk] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 16 * s), qf[s], sacc[blk]);
+            for (int s = 0; s < NS; ++s) {
+                if (s + 2 < NS) {
+                    ka[(s + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(kr0 + 16 * (s + 2));
+                    ka[(s + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(kr1 + 16 * (s + 2));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                sacc[0] = mfma32(ka[s % 3][0], qf[s], sacc[0]);
+                sacc[1] = mfma32(ka[s % 3][1], qf[s], sacc[1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         // ---- mask: ragged tail and (causal) blocks that straddle the diagonal ----
@@ -228,16 +248,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
 
         // ---- online softmax on this lane's query row ----
+        // The reference maximum m_run is raised (and the running sum and
+        // output rescaled by 2^(m_run - m_new)) only when some row's block
+        // maximum exceeds it by more than 2^kTau; otherwise p <= 2^kTau and
+        // the stale reference cancels in the final division, so the result is
+        // the same exact quantity with far fewer rescales.
         float mx = kNegInf;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[blk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx * scale_log2);
-        const float m_use = m_new == kNegInf ? 0.f : m_new;
-        const float alpha = exp2f_hw(m_run - m_use);
-        m_run = m_new;
+        mx = half_swap_max(mx) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = exp2f_hw(m_run - (m_new == kNegInf ? 0.f : m_new));
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+        }
+        const float m_use = m_run == kNegInf ? 0.f : m_run;
 
         bf16x8 pf[4];
         float rs = 0.f;
@@ -249,17 +279,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                 rs += p;
                 pf[2 * blk + (r >> 3)][r & 7] = (__bf16)p;
             }
-        l_run = fmaf(l_run, alpha, rs);
-#pragma unroll
-        for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+        l_run += rs;
 
-        // ---- O^T += V_j^T P^T ----
+        // ---- O^T += V_j^T P^T: d-block chains interleaved, reads one step ahead ----
+        {
+            constexpr int NDB = D / 32;
+            const uint16_t* vr = vt + l32 * T::VSTR + 8 * hh;
+            bf16x8 va[2][NDB];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-            const uint16_t* vr = vt + (32 * db + l32) * T::VSTR + 8 * hh;
+            for (int db = 0; db < NDB; ++db)
+                va[0][db] = *reinterpret_cast<const bf16x8*>(vr + 32 * db * T::VSTR);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                oacc[db] = mfma32(*reinterpret_cast<const bf16x8*>(vr + 16 * ks), pf[ks], oacc[db]);
+            for (int ks = 0; ks < 4; ++ks) {
+                if (ks + 1 < 4) {
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+                        va[(ks + 1) & 1][db] = *reinterpret_cast<const bf16x8*>(vr + 32 * db * T::VSTR + 16 * (ks + 1));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[ks & 1][db], pf[ks], oacc[db]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
 
         if (more) store_kv<D>(st, lds + ((it + 1) & 1) * T::STAGE, tid);
@@ -267,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     // ---- epilogue: one division per row, bf16 output, natural-log lse ----
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (my_q < Sq) {
         uint16_t* op = O + q_off + (int64_t)my_q * D;
