@@ -7,9 +7,11 @@
 // K/V).  Per K/V block ("Fast Inference and Training at Scale", section 6.21,
 // tiling):
 //
-//   1. K_j and V_j are staged into LDS by the waves themselves: K one block
-//      ahead of V, each in its own double buffer, global loads issued a block
-//      before the LDS write, one barrier per block.
+//   1. K_j and V_j are copied from HBM/L2 straight into LDS with the
+//      global-to-LDS load (no registers involved, 256-byte coalesced rows),
+//      K one block ahead of V, each in its own double buffer; one barrier per
+//      block.  Both tiles are row-major with XOR-swizzled 16-byte chunks, so
+//      the operand reads below hit distinct banks.
 //   2. Scores come from the matrix cores.  Each wave owns 32 query rows and
 //      computes the transposed block S^T = K_j Q^T, so that every lane holds
 //      scores of a single query row: the row maximum and row sum are in-lane
@@ -20,9 +22,10 @@
 //      by 2^(m_old - m_new) when the reference maximum moves.  A row with no
 //      visible key so far keeps m = -inf and contributes exactly zero (the
 //      -inf guard of the "Common mistakes" list).
-//   4. O^T += V_j^T P^T on the matrix cores; P is rounded to bf16 once.  V_j is
-//      written to LDS transposed, in the key order that the lanes hold P in,
-//      so each A operand is one 16-byte LDS read.
+//   4. O^T += V_j^T P^T on the matrix cores; P is rounded to bf16 once.  The
+//      V^T operand is read from the row-major V tile with the transposing LDS
+//      read (ds_read_b64_tr_b16), whose addresses also put the keys in the
+//      order in which the lanes hold P.
 //   5. After the last block the output is divided by the running sum once
 //      (the division is postponed to the end, section 1 of the FlashAttention
 //      page) and lse = (m + log2 l) ln 2 is written per row.
@@ -54,91 +57,57 @@ constexpr float kTau = 8.f;       // log2 of the growth allowed before a rescale
 
 template <int D>
 struct Tile {
-    static constexpr int KSTR = D + 8;            // K row stride in LDS (bf16), 16 B pad
-    static constexpr int VSTR = kBN + 8;          // V^T row stride in LDS (bf16)
-    static constexpr int K_ELEMS = kBN * KSTR;
-    static constexpr int V_ELEMS = D * VSTR;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int KCHUNKS = kBN * D / 8 / kThreads;   // 16-byte K loads per thread
-    static constexpr int VGROUPS = (kBN / 4) * (D / 8);       // 4-key x 8-column V groups
-    static_assert(KCHUNKS >= 1 && (kBN * D / 8) % kThreads == 0, "K tile split");
-    static_assert(VGROUPS <= kThreads, "one V group per thread at most");
+    static constexpr int ROWB = D * 2;                   // bytes per K or V row (no padding)
+    static constexpr int CHUNKS = D / 8;                 // 16-byte chunks per row
+    static constexpr int K_BYTES = kBN * ROWB;           // one K stage
+    static constexpr int V_BYTES = kBN * ROWB;           // one V stage
+    static constexpr int ROWS_PER_LOAD = 1024 / ROWB;    // rows one wave-wide 16-byte load covers
+    static constexpr int LOADS = kBN / ROWS_PER_LOAD / kWaves;   // loads per wave per tile
+    static_assert(kBN % (ROWS_PER_LOAD * kWaves) == 0, "tile split");
 };
 
-// Slot of the first of 4 consecutive keys (4g .. 4g+3) inside the V^T tile.
-// Within a 16-key chunk the key 8a + 4h + b sits at slot 8h + 4a + b, which is
-// the order in which lane half h holds the probabilities of that chunk.
-__device__ __forceinline__ int vt_slot(int g) {
-    const int w = g & 3;
-    return 16 * (g >> 2) + 4 * (((w & 1) << 1) | (w >> 1));
-}
-
+// XOR swizzles of the 16-byte chunk index within a row.  K operand reads
+// take one chunk from 16 consecutive rows; V^T operand reads take 8-byte
+// pieces of 4 consecutive chunks from 4 consecutive rows.  Both patterns land
+// on distinct banks with these maps.
 template <int D>
-struct KStage {
-    u32x4 k[Tile<D>::KCHUNKS];
-};
-struct VStage {
-    u32x4 v[4];
-};
-
+__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
 template <int D>
-__device__ __forceinline__ void load_k(KStage<D>& st, const uint16_t* __restrict__ Kh, int kv0, int Sk, int tid) {
+__device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// Copy the 64-row block starting at row kv0 of a [S, D] tensor into an LDS
+// stage with the global-to-LDS load.  Each wave issues LOADS loads; a load's
+// lane l lands at LDS byte 16 l of its 1 KiB slice, so each lane fetches the
+// logical chunk that the swizzle places at that position.  Rows past Sk
+// repeat row Sk - 1 (their scores are masked, and their p is exactly zero).
+template <int D, bool IS_K>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8_t* stage, int kv0, int Sk, int wave,
+                                         int lane) {
+    using T = Tile<D>;
 #pragma unroll
-    for (int c = 0; c < Tile<D>::KCHUNKS; ++c) {
-        const int idx = c * kThreads + tid;
-        const int row = idx / (D / 8), col = idx % (D / 8);
-        // The address is clamped to a valid row; rows past Sk are zeroed when
-        // stored, so nothing waits for the load before the LDS write.
-        st.k[c] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)min(kv0 + row, Sk - 1) * D + col * 8);
+    for (int c = 0; c < T::LOADS; ++c) {
+        const int slice = c * kWaves + wave;                       // 1 KiB slice of the stage
+        const int row = slice * T::ROWS_PER_LOAD + lane / T::CHUNKS;
+        const int pchunk = lane % T::CHUNKS;
+        const int chunk = pchunk ^ (IS_K ? swz_k<D>(row) : swz_v<D>(row));
+        const uint16_t* g = src + (int64_t)min(kv0 + row, Sk - 1) * D + chunk * 8;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)g,
+            (__attribute__((address_space(3))) void*)(stage + slice * 1024), 16, 0, 0);
     }
 }
 
-template <int D>
-__device__ __forceinline__ void store_k(const KStage<D>& st, uint16_t* kt, int kv0, int Sk, int tid) {
-#pragma unroll
-    for (int c = 0; c < Tile<D>::KCHUNKS; ++c) {
-        const int idx = c * kThreads + tid;
-        const int row = idx / (D / 8), col = idx % (D / 8);
-        *reinterpret_cast<u32x4*>(kt + row * Tile<D>::KSTR + col * 8) =
-            kv0 + row < Sk ? st.k[c] : u32x4{0, 0, 0, 0};
-    }
-}
+// s_waitcnt vmcnt(0): every global(-to-LDS) load of this wave has landed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// V staging: each thread owns 4 consecutive keys x 8 head-dim columns.  The
-// key group is the fastest-varying lane index, so the transposed LDS write of
-// one instruction fills whole V^T rows (no bank conflicts), at the price of
-// 64-byte rather than 256-byte contiguous global segments.
-template <int D>
-__device__ __forceinline__ void load_v(VStage& st, const uint16_t* __restrict__ Vh, int kv0, int Sk, int tid) {
-    if (tid < Tile<D>::VGROUPS) {
-        const int kg = tid % (kBN / 4), cg = tid / (kBN / 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            st.v[i] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)min(kv0 + 4 * kg + i, Sk - 1) * D + cg * 8);
-        }
-    }
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <int D>
-__device__ __forceinline__ void store_v(const VStage& st, uint16_t* vt, int kv0, int Sk, int tid) {
-    if (tid < Tile<D>::VGROUPS) {
-        const int kg = tid % (kBN / 4), cg = tid / (kBN / 4);
-        uint16_t* dst = vt + (cg * 8) * Tile<D>::VSTR + vt_slot(kg);
-        const int key0 = kv0 + 4 * kg;
-        u32x4 v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = key0 + i < Sk ? st.v[i] : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int w = c >> 1;
-            const int sh = (c & 1) * 16;
-            const uint32_t e0 = (v[0][w] >> sh) & 0xffffu;
-            const uint32_t e1 = (v[1][w] >> sh) & 0xffffu;
-            const uint32_t e2 = (v[2][w] >> sh) & 0xffffu;
-            const uint32_t e3 = (v[3][w] >> sh) & 0xffffu;
-            *reinterpret_cast<u32x2*>(dst + c * Tile<D>::VSTR) = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-        }
-    }
+// 8 bytes at an LDS byte address, transposed across each 16-lane group:
+// lane i of a group receives element i % 4 of the 8-byte pieces addressed by
+// lanes 4k + i / 4 (k = 0..3).
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) uint8_t*)p);
 }
 
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
@@ -148,21 +117,27 @@ __device__ __forceinline__ void store_v(const VStage& st, uint16_t* vt, int kv0,
 // After MFMA step s the callback `between(s)` is emitted, so independent
 // vector work can be interleaved with the matrix-core work.
 template <int D, typename F>
-__device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint16_t* kt, const bf16x8 (&qf)[D / 16],
+__device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint8_t* kt, const bf16x8 (&qf)[D / 16],
                                             int l32, int hh, F&& between) {
+    using T = Tile<D>;
     constexpr int NS = D / 16;
-    const uint16_t* kr0 = kt + l32 * Tile<D>::KSTR + 8 * hh;
-    const uint16_t* kr1 = kr0 + 32 * Tile<D>::KSTR;
+    // rows l32 and l32 + 32 share the swizzle (32 is a multiple of its period)
+    const uint8_t* kr0 = kt + l32 * T::ROWB;
+    const uint8_t* kr1 = kr0 + 32 * T::ROWB;
+    const int sw = swz_k<D>(l32);
+    auto rd = [&](const uint8_t* r, int s) {
+        return *reinterpret_cast<const bf16x8*>(r + 16 * ((2 * s + hh) ^ sw));
+    };
     bf16x8 ka[3][2];
-    ka[0][0] = *reinterpret_cast<const bf16x8*>(kr0);
-    ka[0][1] = *reinterpret_cast<const bf16x8*>(kr1);
-    ka[1][0] = *reinterpret_cast<const bf16x8*>(kr0 + 16);
-    ka[1][1] = *reinterpret_cast<const bf16x8*>(kr1 + 16);
+    ka[0][0] = rd(kr0, 0);
+    ka[0][1] = rd(kr1, 0);
+    ka[1][0] = rd(kr0, 1);
+    ka[1][1] = rd(kr1, 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
         if (s + 2 < NS) {
-            ka[(s + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(kr0 + 16 * (s + 2));
-            ka[(s + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(kr1 + 16 * (s + 2));
+            ka[(s + 2) % 3][0] = rd(kr0, s + 2);
+            ka[(s + 2) % 3][1] = rd(kr1, s + 2);
         }
         FA_FENCE();
         sacc[0] = mfma32(ka[s % 3][0], qf[s], sacc[0]);
@@ -171,6 +146,28 @@ __device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint16_t* k
         between(s);
         FA_FENCE();
     }
+}
+
+// V^T operand for output block db and key step ks (keys 16 ks .. +15): lane l
+// (column c = l % 32 of the block, half h = l / 32) needs V[key][c] for the
+// keys 4h + e (e = 0..3) and 8 + 4h + e, the order in which it holds P.  Two
+// transposing reads: lane s of each 16-lane group g addresses row
+// 16 ks + 4h + s / 4 (+ 8), columns 32 db + 16 (g % 2) + 4 (s % 4) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 vt_operand(const uint8_t* vt, int ks, int db, int lane) {
+    using T = Tile<D>;
+    const int s = lane & 15, g = lane >> 4, h = g >> 1;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);          // element column
+    const int row0 = 16 * ks + 4 * h + (s >> 2);
+    const int row1 = row0 + 8;
+    const int x = col >> 3, half = (col >> 2) & 1;                  // 16-byte chunk, 8-byte half
+    const uint8_t* p0 = vt + row0 * T::ROWB + 16 * (x ^ swz_v<D>(row0)) + 8 * half;
+    const uint8_t* p1 = vt + row1 * T::ROWB + 16 * (x ^ swz_v<D>(row1)) + 8 * half;
+    const s16x4 a = lds_read_tr16(p0), b = lds_read_tr16(p1);
+    const s16x4 lo = a, hi = b;
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
 }
 
 // Mask the scores of block kv0 .. kv0+63: keys past Sk, and keys above the
@@ -195,9 +192,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     using T = Tile<D>;
     constexpr int NS = D / 16;          // MFMA steps of one score block
     constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2 * T::K_ELEMS + 2 * T::V_ELEMS];
-    uint16_t* const kbuf = lds;                     // K stages 0, 1
-    uint16_t* const vbuf = lds + 2 * T::K_ELEMS;    // V^T stages 0, 1
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::K_BYTES + 2 * T::V_BYTES];
+    uint8_t* const kbuf = lds;                      // K stages 0, 1
+    uint8_t* const vbuf = lds + 2 * T::K_BYTES;     // V stages 0, 1
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -268,18 +265,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     auto needs_mask = [&](int kv0) { return (kv0 + kBN > Sk) || (CAUSAL && kv0 + kBN - 1 > qw + diag); };
 
     // ---- prologue: K_0, V_0, K_1 into LDS; scores of block 0 ----
-    KStage<D> kst;
-    VStage vst;
     if (n_it > 0) {
-        load_k<D>(kst, Kh, 0, Sk, tid);
-        load_v<D>(vst, Vh, 0, Sk, tid);
-        store_k<D>(kst, kbuf, 0, Sk, tid);
-        store_v<D>(vst, vbuf, 0, Sk, tid);
+        dma_tile<D, true>(Kh, kbuf, 0, Sk, wave, lane);
+        dma_tile<D, false>(Vh, vbuf, 0, Sk, wave, lane);
     }
-    if (n_it > 1) {
-        load_k<D>(kst, Kh, kBN, Sk, tid);
-        store_k<D>(kst, kbuf + T::K_ELEMS, kBN, Sk, tid);
-    }
+    if (n_it > 1) dma_tile<D, true>(Kh, kbuf + T::K_BYTES, kBN, Sk, wave, lane);
+    wait_dma();
     __syncthreads();
 
     f32x16 scur[2] = {f32x16{}, f32x16{}};
@@ -315,8 +306,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
         const float m_use = m_run == kNegInf ? 0.f : m_run;
 
-        if (has_next2) load_k<D>(kst, Kh, (it + 2) * kBN, Sk, tid);
-        if (has_next) load_v<D>(vst, Vh, (it + 1) * kBN, Sk, tid);
+        // K_{it+2} into the K stage freed by block it, V_{it+1} into the V stage
+        // freed by block it-1; both land while this block is computed.
+        if (has_next2) dma_tile<D, true>(Kh, kbuf + (it & 1) * T::K_BYTES, (it + 2) * kBN, Sk, wave, lane);
+        if (has_next) dma_tile<D, false>(Vh, vbuf + ((it + 1) & 1) * T::V_BYTES, (it + 1) * kBN, Sk, wave, lane);
 
         // ---- phase X: scores of block it+1 on the matrix core, exponentials of block it ----
         u32x4 pfw[4];
@@ -337,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         };
         f32x16 snxt[2] = {f32x16{}, f32x16{}};
         if (has_next) {
-            score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_ELEMS, qf, l32, hh, [&](int s) {
+            score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_BYTES, qf, l32, hh, [&](int s) {
 #pragma unroll
                 for (int c = s * (8 / NS); c < (s + 1) * (8 / NS); ++c) exp_chunk(c);
             });
@@ -351,17 +344,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (has_next && needs_mask((it + 1) * kBN)) mask_block<CAUSAL>(snxt, (it + 1) * kBN, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
-            const uint16_t* vr = vbuf + (it & 1) * T::V_ELEMS + l32 * T::VSTR + 8 * hh;
+            const uint8_t* vt = vbuf + (it & 1) * T::V_BYTES;
             bf16x8 va[2][NDB];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                va[0][db] = *reinterpret_cast<const bf16x8*>(vr + 32 * db * T::VSTR);
+            for (int db = 0; db < NDB; ++db) va[0][db] = vt_operand<D>(vt, 0, db, lane);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 if (ks + 1 < 4) {
 #pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-                        va[(ks + 1) & 1][db] = *reinterpret_cast<const bf16x8*>(vr + 32 * db * T::VSTR + 16 * (ks + 1));
+                    for (int db = 0; db < NDB; ++db) va[(ks + 1) & 1][db] = vt_operand<D>(vt, ks + 1, db, lane);
                 }
                 FA_FENCE();
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pfw[ks]);
@@ -378,8 +369,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
         if (has_next) mx_cur = half_swap_max(mxn) * scale_log2;
 
-        if (has_next2) store_k<D>(kst, kbuf + (it & 1) * T::K_ELEMS, (it + 2) * kBN, Sk, tid);
-        if (has_next) store_v<D>(vst, vbuf + ((it + 1) & 1) * T::V_ELEMS, (it + 1) * kBN, Sk, tid);
+        wait_dma();
         __syncthreads();
         scur[0] = snxt[0];
         scur[1] = snxt[1];
