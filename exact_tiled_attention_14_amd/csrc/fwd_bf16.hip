@@ -76,24 +76,47 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 // Copy the 64-row block starting at row kv0 of a [S, D] tensor into an LDS
-// stage with the global-to-LDS load.  Each wave issues LOADS loads; a load's
-// lane l lands at LDS byte 16 l of its 1 KiB slice, so each lane fetches the
-// logical chunk that the swizzle places at that position.  Rows past Sk
-// repeat row Sk - 1 (their scores are masked, and their p is exactly zero).
+// stage with the global-to-LDS load.  Load c of wave w fills the 1 KiB
+// slice c * kWaves + w of the stage, and its lane l lands at byte 16 l of
+// that slice, so each lane fetches the logical chunk that the swizzle places
+// there: row = slice * ROWS_PER_LOAD + l / CHUNKS, physical chunk l % CHUNKS.
+// The swizzles repeat every 16 (K) or 4 (V) rows, a divisor of the rows
+// between two loads of a lane, so a lane's loads share one chunk: a full
+// block is addressed as a uniform per-load base plus one loop-invariant lane
+// offset `lane_off` (in elements).  In the ragged last block rows past Sk
+// repeat row Sk - 1: their scores are masked and their p is exactly zero.
 template <int D, bool IS_K>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8_t* stage, int kv0, int Sk, int wave,
-                                         int lane) {
+__device__ __forceinline__ int dma_lane_offset(int wave, int lane) {
     using T = Tile<D>;
+    const int row = wave * T::ROWS_PER_LOAD + lane / T::CHUNKS;
+    const int chunk = (lane % T::CHUNKS) ^ (IS_K ? swz_k<D>(row) : swz_v<D>(row));
+    return row * D + chunk * 8;
+}
+
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8_t* stage, int lane_off, int kv0,
+                                         int Sk, int wave) {
+    using T = Tile<D>;
+    constexpr int ROW_STEP = kWaves * T::ROWS_PER_LOAD;   // rows between two loads of a lane
+    static_assert(ROW_STEP % 16 == 0, "a lane's loads must share one swizzled chunk");
+    if (kv0 + kBN <= Sk) {
 #pragma unroll
-    for (int c = 0; c < T::LOADS; ++c) {
-        const int slice = c * kWaves + wave;                       // 1 KiB slice of the stage
-        const int row = slice * T::ROWS_PER_LOAD + lane / T::CHUNKS;
-        const int pchunk = lane % T::CHUNKS;
-        const int chunk = pchunk ^ (IS_K ? swz_k<D>(row) : swz_v<D>(row));
-        const uint16_t* g = src + (int64_t)min(kv0 + row, Sk - 1) * D + chunk * 8;
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)g,
-            (__attribute__((address_space(3))) void*)(stage + slice * 1024), 16, 0, 0);
+        for (int c = 0; c < T::LOADS; ++c) {
+            const uint16_t* base = src + (int64_t)(kv0 + c * ROW_STEP) * D;      // uniform
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + lane_off),
+                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024),
+                                             16, 0, 0);
+        }
+    } else {
+        const int row0 = lane_off / D;
+#pragma unroll
+        for (int c = 0; c < T::LOADS; ++c) {
+            const int row = row0 + c * ROW_STEP;
+            const uint16_t* g = src + (int64_t)min(kv0 + row, Sk - 1) * D + (lane_off - row0 * D);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024),
+                                             16, 0, 0);
+        }
     }
 }
 
@@ -113,7 +136,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 #define FA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Scores of one 64-key block for this wave's 32 rows: S^T = K Q^T, the two
-// 32-key halves as interleaved MFMA chains, LDS operand reads two steps ahead.
+// 32-key halves as interleaved MFMA chains, LDS operand reads one step ahead.
 // After MFMA step s the callback `between(s)` is emitted, so independent
 // vector work can be interleaved with the matrix-core work.
 template <int D, typename F>
@@ -128,20 +151,18 @@ __device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint8_t* kt
     auto rd = [&](const uint8_t* r, int s) {
         return *reinterpret_cast<const bf16x8*>(r + 16 * ((2 * s + hh) ^ sw));
     };
-    bf16x8 ka[3][2];
+    bf16x8 ka[2][2];
     ka[0][0] = rd(kr0, 0);
     ka[0][1] = rd(kr1, 0);
-    ka[1][0] = rd(kr0, 1);
-    ka[1][1] = rd(kr1, 1);
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        if (s + 2 < NS) {
-            ka[(s + 2) % 3][0] = rd(kr0, s + 2);
-            ka[(s + 2) % 3][1] = rd(kr1, s + 2);
+        if (s + 1 < NS) {
+            ka[(s + 1) & 1][0] = rd(kr0, s + 1);
+            ka[(s + 1) & 1][1] = rd(kr1, s + 1);
         }
         FA_FENCE();
-        sacc[0] = mfma32(ka[s % 3][0], qf[s], sacc[0]);
-        sacc[1] = mfma32(ka[s % 3][1], qf[s], sacc[1]);
+        sacc[0] = mfma32(ka[s & 1][0], qf[s], sacc[0]);
+        sacc[1] = mfma32(ka[s & 1][1], qf[s], sacc[1]);
         FA_FENCE();
         between(s);
         FA_FENCE();
@@ -198,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int g = Hq / Hkv;
@@ -265,31 +286,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     auto needs_mask = [&](int kv0) { return (kv0 + kBN > Sk) || (CAUSAL && kv0 + kBN - 1 > qw + diag); };
 
     // ---- prologue: K_0, V_0, K_1 into LDS; scores of block 0 ----
+    const int k_lane_off = dma_lane_offset<D, true>(wave, lane);
+    const int v_lane_off = dma_lane_offset<D, false>(wave, lane);
     if (n_it > 0) {
-        dma_tile<D, true>(Kh, kbuf, 0, Sk, wave, lane);
-        dma_tile<D, false>(Vh, vbuf, 0, Sk, wave, lane);
+        dma_tile<D>(Kh, kbuf, k_lane_off, 0, Sk, wave);
+        dma_tile<D>(Vh, vbuf, v_lane_off, 0, Sk, wave);
     }
-    if (n_it > 1) dma_tile<D, true>(Kh, kbuf + T::K_BYTES, kBN, Sk, wave, lane);
+    if (n_it > 1) dma_tile<D>(Kh, kbuf + T::K_BYTES, k_lane_off, kBN, Sk, wave);
     wait_dma();
     __syncthreads();
 
-    f32x16 scur[2] = {f32x16{}, f32x16{}};
+    f32x16 s0[2] = {f32x16{}, f32x16{}};
     float mx_cur = kNegInf;
     if (n_it > 0) {
-        score_block<D>(scur, kbuf, qf, l32, hh, [](int) {});
-        if (needs_mask(0)) mask_block<CAUSAL>(scur, 0, Sk, my_q, diag, hh);
+        score_block<D>(s0, kbuf, qf, l32, hh, [](int) {});
+        if (needs_mask(0)) mask_block<CAUSAL>(s0, 0, Sk, my_q, diag, hh);
         float mx = kNegInf;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, scur[blk][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[blk][r]);
         mx_cur = half_swap_max(mx) * scale_log2;
     }
     // K stage 0 is rewritten (with K_2) at the end of the first iteration:
     // every wave must have finished reading it above.
     __syncthreads();
 
-    for (int it = 0; it < n_it; ++it) {
+    // One K/V block: `scur` holds this block's scores, `snxt` receives the next
+    // block's.  The loop is unrolled by two so the buffers swap roles instead
+    // of being copied.
+    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2]) __attribute__((always_inline)) {
         const bool has_next = it + 1 < n_it;
         const bool has_next2 = it + 2 < n_it;
 
@@ -308,8 +334,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         // K_{it+2} into the K stage freed by block it, V_{it+1} into the V stage
         // freed by block it-1; both land while this block is computed.
-        if (has_next2) dma_tile<D, true>(Kh, kbuf + (it & 1) * T::K_BYTES, (it + 2) * kBN, Sk, wave, lane);
-        if (has_next) dma_tile<D, false>(Vh, vbuf + ((it + 1) & 1) * T::V_BYTES, (it + 1) * kBN, Sk, wave, lane);
+        if (has_next2) dma_tile<D>(Kh, kbuf + (it & 1) * T::K_BYTES, k_lane_off, (it + 2) * kBN, Sk, wave);
+        if (has_next) dma_tile<D>(Vh, vbuf + ((it + 1) & 1) * T::V_BYTES, v_lane_off, (it + 1) * kBN, Sk, wave);
 
         // ---- phase X: scores of block it+1 on the matrix core, exponentials of block it ----
         u32x4 pfw[4];
@@ -328,7 +354,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             pfw[pk][pw] = w01;
             pfw[pk][pw + 1] = w23;
         };
-        f32x16 snxt[2] = {f32x16{}, f32x16{}};
+        snxt[0] = f32x16{};
+        snxt[1] = f32x16{};
         if (has_next) {
             score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_BYTES, qf, l32, hh, [&](int s) {
 #pragma unroll
@@ -371,8 +398,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         wait_dma();
         __syncthreads();
-        scur[0] = snxt[0];
-        scur[1] = snxt[1];
+    };
+    f32x16 s1[2];
+    for (int it = 0; it < n_it; it += 2) {
+        step(it, s0, s1);
+        if (it + 1 < n_it) step(it + 1, s1, s0);
     }
 
     // ---- epilogue: one division per row, bf16 output, natural-log lse ----
