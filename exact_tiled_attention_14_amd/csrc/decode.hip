@@ -38,6 +38,7 @@ constexpr int kD = 128;
 constexpr int kPage = 16;
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+constexpr float kTau = 8.f;   // log2 of the growth allowed before a rescale
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -103,62 +104,114 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
     }
 
     const int32_t* trow = table + (int64_t)seq * max_blocks;
-    for (int p = page0 + wave; p < page1; p += kWaves) {
+    // K and V of one page for this lane: tokens row + 4i (i = 0..3), head-dim
+    // slice 8 col .. +7.  The next page of the wave is loaded while the
+    // current one is computed.
+    auto load_page = [&](int p, u32x4 (&kk)[4], u32x4 (&vv)[4]) {
         const int bid = trow[p];
         const bool blk_ok = bid >= 0 && bid < num_blocks;
         const int64_t base = ((int64_t)(blk_ok ? bid : 0) * Hkv + kvh) * (kPage * kD) + 8 * col;
-        u32x4 kk[4], vv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t off = base + (int64_t)(row + 4 * i) * kD;
-            kk[i] = *reinterpret_cast<const u32x4*>(KC + off);
-            vv[i] = *reinterpret_cast<const u32x4*>(VC + off);
+            // every page is read exactly once: stream it past the caches
+            kk[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(KC + off));
+            vv[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(VC + off));
         }
-        const int valid = blk_ok ? min(kPage, len - p * kPage) : 0;   // tokens of this page in use
+        return blk_ok;
+    };
+
+    u32x4 kk[4], vv[4], kn[4], vn[4];
+    int p = page0 + wave;
+    bool ok_cur = p < page1 ? load_page(p, kk, vv) : false;
+    for (; p < page1; p += kWaves) {
+        const bool more = p + kWaves < page1;
+        bool ok_nxt = false;
+        if (more) ok_nxt = load_page(p + kWaves, kn, vn);
+
+        // tokens of this page in use; only a sequence's last page (or a page
+        // behind an invalid block id) is partly masked
+        const int valid = ok_cur ? min(kPage, len - p * kPage) : 0;
+        const bool partial = valid < kPage;
 
         float s[G][4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = row + 4 * i < valid;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float dot = row_sum16(dot8_bf16(kk[i], qv[h]));
-                s[h][i] = ok ? dot * scale_log2 : kNegInf;
-            }
-            if (!ok) vv[i] = u32x4{0, 0, 0, 0};
-        }
-
-        float vf[4][8];
-#pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                vf[i][2 * w] = bf16lo_to_f32(vv[i][w]);
-                vf[i][2 * w + 1] = bf16hi_to_f32(vv[i][w]);
-            }
-
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float mx = fmaxf(fmaxf(s[h][0], s[h][1]), fmaxf(s[h][2], s[h][3]));
-            const float m_new = fmaxf(m[h], mx);
-            const float m_use = m_new == kNegInf ? 0.f : m_new;
-            const float alpha = exp2f_hw(m[h] - m_use);
-            m[h] = m_new;
-            float pr[4];
-            float rs = 0.f;
+            for (int h = 0; h < G; ++h) s[h][i] = row_sum16(dot8_bf16(kk[i], qv[h]));
+        if (partial) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                pr[i] = exp2f_hw(s[h][i] - m_use);
-                rs += pr[i];
-            }
-            l[h] = fmaf(l[h], alpha, rs);
+                const bool ok = row + 4 * i < valid;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float a = acc[h][e] * alpha;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a = fmaf(pr[i], vf[i][e], a);
-                acc[h][e] = a;
+                for (int h = 0; h < G; ++h) s[h][i] = ok ? s[h][i] : kNegInf;
+                // masked slots may hold anything, NaN included: never multiply them
+                if (!ok) vv[i] = u32x4{0, 0, 0, 0};
             }
+        }
+
+        // Online softmax per lane row.  The reference maximum moves only when
+        // a row's page maximum outgrows it by 2^kTau (p <= 2^kTau otherwise;
+        // the stale reference cancels in the final division).
+        float mx[G];
+        bool grow = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            mx[h] = fmaxf(fmaxf(s[h][0], s[h][1]), fmaxf(s[h][2], s[h][3])) * scale_log2;
+            grow |= mx[h] > m[h] + kTau;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float m_new = fmaxf(m[h], mx[h]);
+                const float alpha = exp2f_hw(m[h] - (m_new == kNegInf ? 0.f : m_new));
+                m[h] = m_new;
+                l[h] *= alpha;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            }
+        }
+
+        // O += P V over the lane's tokens: P rounded to bf16 once, token pairs
+        // (0,1) and (2,3) contracted with packed dot products.
+        uint32_t v01lo[4], v01hi[4], v23lo[4], v23hi[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v01lo[w] = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x05040100u);
+            v01hi[w] = __builtin_amdgcn_perm(vv[1][w], vv[0][w], 0x07060302u);
+            v23lo[w] = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x05040100u);
+            v23hi[w] = __builtin_amdgcn_perm(vv[3][w], vv[2][w], 0x07060302u);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float m_use = m[h] == kNegInf ? 0.f : m[h];
+            const float p0 = exp2f_hw(fmaf(s[h][0], scale_log2, -m_use));
+            const float p1 = exp2f_hw(fmaf(s[h][1], scale_log2, -m_use));
+            const float p2 = exp2f_hw(fmaf(s[h][2], scale_log2, -m_use));
+            const float p3 = exp2f_hw(fmaf(s[h][3], scale_log2, -m_use));
+            l[h] += (p0 + p1) + (p2 + p3);
+            const uint32_t w01 = pack_bf16x2(p0, p1), w23 = pack_bf16x2(p2, p3);
+            const bf16x2 b01 = __builtin_bit_cast(bf16x2, w01), b23 = __builtin_bit_cast(bf16x2, w23);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t a0 = v01lo[w], a1 = v23lo[w], c0 = v01hi[w], c1 = v23hi[w];
+                float e0 = acc[h][2 * w], e1 = acc[h][2 * w + 1];
+                e0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a0), b01, e0, false);
+                e0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a1), b23, e0, false);
+                e1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c0), b01, e1, false);
+                e1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c1), b23, e1, false);
+                acc[h][2 * w] = e0;
+                acc[h][2 * w + 1] = e1;
+            }
+        }
+
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                kk[i] = kn[i];
+                vv[i] = vn[i];
+            }
+            ok_cur = ok_nxt;
         }
     }
 
