@@ -84,7 +84,10 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
     const int page1 = min(page0 + pages_per_split, n_pages);
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // The wave index is made scalar so block-table reads are scalar loads:
+    // waiting for one then does not also wait for the vector loads of the
+    // page in flight.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int row = lane >> 4;                    // token slot: tokens row, row+4, row+8, row+12
     const int col = lane & 15;                    // head-dim slice 8*col .. 8*col+7
     const int hq0 = kvh * G;
@@ -121,14 +124,12 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
         return blk_ok;
     };
 
-    u32x4 kk[4], vv[4], kn[4], vn[4];
-    int p = page0 + wave;
-    bool ok_cur = p < page1 ? load_page(p, kk, vv) : false;
-    for (; p < page1; p += kWaves) {
-        const bool more = p + kWaves < page1;
-        bool ok_nxt = false;
-        if (more) ok_nxt = load_page(p + kWaves, kn, vn);
-
+    // Process page p from (kk, vv) while the wave's next page streams into
+    // (kn, vn); the loop is unrolled by two so the buffers swap roles instead
+    // of being copied (a copy would wait for the loads in flight).
+    auto page = [&](const int p, u32x4 (&kk)[4], u32x4 (&vv)[4], const bool ok_cur, u32x4 (&kn)[4],
+                    u32x4 (&vn)[4], bool& ok_nxt) __attribute__((always_inline)) {
+        if (p + kWaves < page1) ok_nxt = load_page(p + kWaves, kn, vn);
         // tokens of this page in use; only a sequence's last page (or a page
         // behind an invalid block id) is partly masked
         const int valid = ok_cur ? min(kPage, len - p * kPage) : 0;
@@ -204,15 +205,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(
                 acc[h][2 * w + 1] = e1;
             }
         }
+    };
 
-        if (more) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kk[i] = kn[i];
-                vv[i] = vn[i];
-            }
-            ok_cur = ok_nxt;
-        }
+    u32x4 ka[4], va[4], kb[4], vb[4];
+    bool oka = false, okb = false;
+    const int p_first = page0 + wave;
+    if (p_first < page1) oka = load_page(p_first, ka, va);
+    for (int p = p_first; p < page1; p += 2 * kWaves) {
+        page(p, ka, va, oka, kb, vb, okb);
+        if (p + kWaves < page1) page(p + kWaves, kb, vb, okb, ka, va, oka);
     }
 
     // Merge the four token rows of the wave (lanes l, l^16, l^32, l^48 share a slice).
