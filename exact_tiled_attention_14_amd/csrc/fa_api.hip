@@ -67,11 +67,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 size_t fa_decode_workspace_size(int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq) {
     if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1) return 0;
     if (d != 128 || block_size != 16) return 0;
-    const fa::DecodePlan pl = fa::plan_decode(nseq, Hq, Hkv, max_blocks_per_seq);
-    // partial outputs, then partial lse, each starting on a 256-byte boundary
-    const size_t o_bytes = ((size_t)pl.ws_o_elems * 4 + 255) & ~(size_t)255;
-    const size_t l_bytes = ((size_t)pl.ws_lse_elems * 4 + 255) & ~(size_t)255;
-    return o_bytes + l_bytes;
+    return fa::decode_workspace_bytes(nseq, Hq, Hkv);
 }
 
 int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
@@ -89,7 +85,10 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     if (d != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
     const int g = Hq / Hkv;
     if (g != 1 && g != 2 && g != 4 && g != 8) return FA_ERR_UNSUPPORTED;
-    if (nseq > 65535 || Hkv > 65535) return FA_ERR_UNSUPPORTED;   // grid y / z limits
+    if (nseq > 65535 || Hkv > 65535) return FA_ERR_UNSUPPORTED;   // grid y limit of the combine step
+    // pages of all (sequence, K/V head) pairs at the table's capacity: the
+    // work split counts them in 32 bits per wave
+    if ((int64_t)nseq * Hkv * max_blocks_per_seq > INT32_MAX) return FA_ERR_UNSUPPORTED;
     if (!fits(num_blocks, Hkv, block_size, d) || (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return FA_ERR_INVALID_ARG;
 
@@ -97,14 +96,9 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
 
-    fa::DecodePlan pl = fa::plan_decode(nseq, Hq, Hkv, max_blocks_per_seq);
-    const size_t o_bytes = ((size_t)pl.ws_o_elems * 4 + 255) & ~(size_t)255;
-    pl.ws_o = static_cast<float*>(workspace);
-    pl.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-
     fa::DecodeArgs a{q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, max_blocks_per_seq,
                      num_blocks, scale};
-    const hipError_t e = fa::launch_decode(a, pl, reinterpret_cast<hipStream_t>(stream));
+    const hipError_t e = fa::launch_decode(a, workspace, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

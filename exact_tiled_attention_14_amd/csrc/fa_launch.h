@@ -30,18 +30,10 @@ struct DecodeArgs {
     float scale;
 };
 
-struct DecodePlan {
-    int pages_per_split;   // pages of one sequence handled by one workgroup
-    int n_split;           // ranges per sequence at the table's capacity
-    int64_t ws_o_elems;    // fp32 partial outputs [nseq, Hq, n_split, 128]
-    int64_t ws_lse_elems;  // fp32 partial lse     [nseq, Hq, n_split]
-    float* ws_o;
-    float* ws_lse;
-};
-
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
-DecodePlan plan_decode(int nseq, int Hq, int Hkv, int max_blocks);
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+// Bytes of device scratch launch_decode uses (256-byte aligned sections).
+size_t decode_workspace_bytes(int nseq, int Hq, int Hkv);
+hipError_t launch_decode(const DecodeArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace fa

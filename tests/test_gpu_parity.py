@@ -305,6 +305,45 @@ def test_paged_decode_empty_and_bad_block_ids(B):
     check_o(o[2], O2[0, :, 0], "bf16", "bad block id")
 
 
+@pytest.mark.parametrize("lens", [[8192], [8192, 1], [3000, 0, 0, 2000, 0, 17], [0, 0, 5]],
+                         ids=["one_long", "long_short", "empty_between", "empty_first"])
+def test_paged_decode_split_across_waves(B, lens):
+    """Ranges of the work split start and end inside sequences, cross empty
+    ones, and a single sequence is shared by many waves."""
+    lens = np.asarray(lens, dtype=np.int32)
+    d = I.make_decode(len(lens), 32, 8, 128, len_lo=1, len_hi=max(16, int(lens.max())), seed=81,
+                      poison_tail=True, seqlens=lens)
+    o, lse = run_decode(B, d)
+    O, L = oracle.paged_decode(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check_o(o, O, "bf16", f"split {lens.tolist()}")
+    check_lse(lse, L)
+
+
+def test_paged_decode_many_short_sequences(B):
+    """More sequences than one pass of the work-split scan covers."""
+    rng = np.random.default_rng(82)
+    lens = rng.integers(0, 49, size=1500).astype(np.int32)
+    lens[::97] = 0
+    d = I.make_decode(len(lens), 8, 2, 128, len_lo=1, len_hi=48, seed=82, seqlens=lens)
+    o, lse = run_decode(B, d)
+    O, L = oracle.paged_decode(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check_o(o, O, "bf16", "1500 short sequences")
+    check_lse(lse, L)
+
+
+def test_paged_decode_workspace_reuse(B):
+    """A workspace left by a larger call holds nothing the next call reads."""
+    big = I.make_decode(40, 32, 8, 128, len_lo=500, len_hi=3000, seed=83)
+    small = I.make_decode(3, 32, 8, 128, len_lo=100, len_hi=900, seed=84)
+    ws = torch.empty(B.fa_decode_workspace_size(40, 32, 8, 128, 16, big.block_table.shape[1]),
+                     dtype=torch.uint8, device=DEV)
+    run_decode(B, big, workspace=ws)
+    o, lse = run_decode(B, small, workspace=ws)
+    O, L = oracle.paged_decode(small.q, small.kcache, small.vcache, small.block_table, small.seqlens, small.scale)
+    check_o(o, O, "bf16", "workspace reuse")
+    check_lse(lse, L)
+
+
 def test_decode_equals_last_row_of_causal_prefill(B):
     n = 700
     d = I.make_decode(1, 32, 8, 128, len_lo=n, len_hi=n, seed=79)
