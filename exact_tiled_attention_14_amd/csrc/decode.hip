@@ -51,20 +51,6 @@ constexpr int kMaxWaves = 4096;        // waves of the partial kernel, at most
 constexpr int kMinPagesPerWave = 4;    // fewer waves than pages / 4 are never used
 constexpr int kSchedThreads = 1024;
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the total.
-__device__ __forceinline__ float row_sum16(float x) {
-    x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-    x += dpp<0x141>(x);   // row_half_mirror
-    x += dpp<0x140>(x);   // row_mirror
-    return x;
-}
-
 __device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b) {
     float acc = 0.f;
 #pragma unroll

@@ -55,7 +55,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
         return FA_ERR_INVALID_ARG;
     }
     // The grid is one workgroup per (batch, query head, query block).
-    const int64_t rows_per_wg = dtype == FA_BF16 ? 128 : 64;
+    const int64_t rows_per_wg = dtype == FA_BF16 ? 128 : 16;   // query rows per workgroup of each kernel
     if ((int64_t)B * Hq * ((Sq + rows_per_wg - 1) / rows_per_wg) > INT32_MAX) return FA_ERR_UNSUPPORTED;
 
     fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale};

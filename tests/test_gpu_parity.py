@@ -114,6 +114,18 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("shape", [(1, 2, 2, 1, 77, 64, True), (1, 4, 1, 333, 1000, 64, True),
+                                   (1, 2, 2, 700, 700, 128, False), (2, 3, 3, 64, 17, 32, True)],
+                         ids=["Sq1", "MQA_Sq333_Sk1000", "S700_d128", "Sk17_d32"])
+def test_fp32_edge_shapes(B, shape):
+    Bn, Hq, Hkv, Sq, Sk, d, causal = shape
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, d, causal=causal, dtype="f32", seed=30 + Sq + d)
+    o, lse = run_fwd(B, c)
+    O, L = oracle.sdpa(c.q, c.k, c.v, causal, c.scale)
+    check_o(o, O, "f32", f"f32 {shape}")
+    check_lse(lse, L, f"f32 {shape}")
+
+
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}d{}{}".format(*s[:6], "c" if s[6] else "n"))
 def test_bf16_small_shapes(B, shape):
     b, hq, hkv, sq, sk, d, causal = shape
