@@ -22,7 +22,9 @@ Everything is written from these pages:
 
 Parity status: every public function is pinned by ``tests/test_oracle_pins.py``
 against closed forms, a hand-derived worked example, library routines and
-brute force; none is "parity unpinned".
+brute force; ``sdpa_backward`` against central finite differences, fp64 torch
+autograd of a separately written forward, and the key-shift, value-sum and
+constant-value closed forms; none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
@@ -35,4 +37,5 @@ from .attention import (  # noqa: F401
     paged_decode,
     split_partials,
     merge_partials,
+    sdpa_backward,
 )

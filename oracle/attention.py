@@ -36,6 +36,7 @@ __all__ = [
     "paged_decode",
     "split_partials",
     "merge_partials",
+    "sdpa_backward",
 ]
 
 
@@ -306,3 +307,54 @@ def merge_partials(partials):
     o[live] = (np.einsum("nr,nrd->rd", w, os_)[live]) / W[live, None]
     lse[live] = M_safe[live] + np.log(W[live])
     return o, lse
+
+
+def _attend_grad(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, vis: np.ndarray, scale: float):
+    """Gradients of one head of standard attention with respect to Q, K, V.
+
+    The pages keep only O and the per-row log-sum-exp for the backward pass
+    and recompute the scores and probabilities from Q, K, V ("Fast Inference
+    and Training at Scale", section 6.21, Idea 2; "Week 13. GPUs and
+    FlashAttention", Step 2).  What is computed is the gradient of the
+    definition in ``_attend`` by the chain rule, one step per line:
+    O = P V gives dV = P^T dO and dP = dO V^T; the softmax of each row gives
+    dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik); S = scale Q K^T gives
+    dQ = scale dS K and dK = scale dS^T Q.  Masked pairs have P = 0, so they
+    get no gradient; a row with no visible key has a zero P row.
+
+    Returns (dQ [R,d], dK [Sk,d], dV [Sk,d]).
+    """
+    _, _, P = _attend(q, k, v, vis, scale)
+    dV = P.T @ do
+    dP = do @ v.T
+    D = (P * dP).sum(axis=1)                   # sum_k P_ik dP_ik per row
+    dS = P * (dP - D[:, None])
+    dQ = scale * (dS @ k)
+    dK = scale * (dS.T @ q)
+    return dQ, dK, dV
+
+
+def sdpa_backward(q, k, v, do, causal: bool, scale: float):
+    """Gradients of ``sum(dO * O)`` for ``O = softmax(scale Q K^T) V``.
+
+    q, do: [B, Hq, Sq, d]; k, v: [B, Hkv, Sk, d].  Returns
+    ``(dq [B,Hq,Sq,d], dk [B,Hkv,Sk,d], dv [B,Hkv,Sk,d])`` in fp64.  Under
+    grouped-query attention a K/V head is read by several query heads, so its
+    gradients are the sums over those heads.
+    """
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    B, Hq, Hkv, Sq, Sk, d = _check_shapes(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError(f"do {do.shape} must have the shape of q {q.shape}")
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    vis = _visible(np.arange(Sq), Sq, Sk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            kvh = kv_head_of(hq, Hq, Hkv)
+            gq, gk, gv = _attend_grad(q[b, hq], k[b, kvh], v[b, kvh], do[b, hq], vis, scale)
+            dq[b, hq] = gq
+            dk[b, kvh] += gk
+            dv[b, kvh] += gv
+    return dq, dk, dv

@@ -431,3 +431,163 @@ def test_planted_mistakes_are_caught(monkeypatch, golden_dir, mutant, attr):
 
 
 _orig_visible = oa._visible
+
+
+# --- 10. backward: gradients of the definition -----------------------------
+
+def _loss_and_grads(q, k, v, w, causal, scale):
+    """L = sum(W * O) and the oracle's gradients for dO = W."""
+    O, _ = oracle.sdpa(q, k, v, causal, scale)
+    return float((w * O).sum()), oracle.sdpa_backward(q, k, v, w, causal, scale)
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq,Sk,causal", [(2, 1, 5, 7, True), (2, 2, 6, 6, False), (3, 1, 7, 4, True),
+                                                 (1, 1, 4, 9, True)])
+def test_backward_matches_finite_differences(Hq, Hkv, Sq, Sk, causal):
+    """Central differences of L = sum(W * O) in fp64 (no use of the gradient
+    formulas): every element of Q, K and V, including rows with no visible key
+    (Sq > Sk, bottom-right causal)."""
+    rng = np.random.default_rng(Hq * 100 + Sq * 10 + Sk)
+    d, scale, h = 3, 0.7, 1e-6
+    q, k, v = _rand(1, Hq, Sq, d, rng=rng), _rand(1, Hkv, Sk, d, rng=rng), _rand(1, Hkv, Sk, d, rng=rng)
+    w = _rand(1, Hq, Sq, d, rng=rng)
+    _, grads = _loss_and_grads(q, k, v, w, causal, scale)
+    for x, g in zip((q, k, v), grads):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp, _ = _loss_and_grads(q, k, v, w, causal, scale)
+            x[idx] = old - h
+            lm, _ = _loss_and_grads(q, k, v, w, causal, scale)
+            x[idx] = old
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, atol=1e-7, rtol=1e-6)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd(causal):
+    """fp64 autograd of a forward written here with torch ops (a separate code
+    path from the oracle's hand-derived gradient), with GQA by repeating K/V heads."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    B, Hq, Hkv, Sq, Sk, d, scale = 2, 4, 2, 9, 11, 5, 0.4
+    q, k, v = _rand(B, Hq, Sq, d, rng=rng), _rand(B, Hkv, Sk, d, rng=rng), _rand(B, Hkv, Sk, d, rng=rng)
+    w = _rand(B, Hq, Sq, d, rng=rng)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+    s = scale * torch.matmul(tq, kk.transpose(-1, -2))
+    if causal:
+        i = torch.arange(Sq)[:, None]
+        j = torch.arange(Sk)[None, :]
+        s = s.masked_fill(j > i + (Sk - Sq), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), vv)
+    (o * torch.tensor(w)).sum().backward()
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, w, causal, scale)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_key_shift_and_value_sum(causal):
+    """Adding a common vector to every key moves no probability, so the
+    gradients of the keys sum to zero; the probabilities of a row sum to 1, so
+    the value gradients sum to the sum of dO over the rows that see a key."""
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, Sq, Sk, d = 1, 4, 2, 8, 6, 4
+    q, k, v = _rand(B, Hq, Sq, d, rng=rng), _rand(B, Hkv, Sk, d, rng=rng), _rand(B, Hkv, Sk, d, rng=rng)
+    do = _rand(B, Hq, Sq, d, rng=rng)
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, do, causal, 0.6)
+    np.testing.assert_allclose(dk.sum(axis=2), 0.0, atol=1e-12)
+    rows = (np.arange(Sq) + (Sk - Sq) >= 0) if causal else np.ones(Sq, bool)
+    g = Hq // Hkv
+    want = do[:, :, rows].sum(axis=2).reshape(B, Hkv, g, d).sum(axis=2)
+    np.testing.assert_allclose(dv.sum(axis=2), want, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_constant_values_give_no_score_gradient(causal):
+    """With every value row equal, O does not depend on the scores at all, so
+    dQ = dK = 0 exactly (up to rounding); dV still carries dO."""
+    rng = np.random.default_rng(6)
+    q, k = _rand(1, 2, 7, 4, rng=rng), _rand(1, 2, 7, 4, rng=rng)
+    v = np.broadcast_to(_rand(1, 2, 1, 4, rng=rng), (1, 2, 7, 4)).copy()
+    do = _rand(1, 2, 7, 4, rng=rng)
+    dq, dk, dv = oracle.sdpa_backward(q, k, v, do, causal, 0.5)
+    assert np.abs(dq).max() < 1e-12 and np.abs(dk).max() < 1e-12
+    assert np.abs(dv).max() > 0.1
+
+
+def _run_bwd_pins():
+    failed = []
+    checks = {
+        "fd": lambda: test_backward_matches_finite_differences(2, 1, 5, 7, True),
+        "shift": lambda: test_backward_key_shift_and_value_sum(True),
+        "const_v": lambda: test_backward_constant_values_give_no_score_gradient(False),
+    }
+    for name, fn in checks.items():
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(name)
+    return failed
+
+
+def test_backward_pins_pass_on_the_oracle():
+    assert _run_bwd_pins() == []
+
+
+_orig_attend_grad = oa._attend_grad
+
+
+def _grad_no_delta(q, k, v, do, vis, scale):
+    _, _, P = oa._attend(q, k, v, vis, scale)
+    dS = P * (do @ v.T)
+    return scale * (dS @ k), scale * (dS.T @ q), P.T @ do
+
+
+def _grad_no_scale(q, k, v, do, vis, scale):
+    dq, dk, dv = _orig_attend_grad(q, k, v, do, vis, scale)
+    return dq / scale, dk / scale, dv
+
+
+def _grad_dk_from_do(q, k, v, do, vis, scale):
+    _, _, P = oa._attend(q, k, v, vis, scale)
+    dP = do @ v.T
+    dS = P * (dP - (P * dP).sum(axis=1)[:, None])
+    return scale * (dS @ k), scale * (dS.T @ do), P.T @ do
+
+
+def _grad_dv_from_q(q, k, v, do, vis, scale):
+    dq, dk, _ = _orig_attend_grad(q, k, v, do, vis, scale)
+    _, _, P = oa._attend(q, k, v, vis, scale)
+    return dq, dk, P.T @ q
+
+
+def _sdpa_backward_gqa_overwrite(q, k, v, do, causal, scale):
+    q, k, v, do = (np.asarray(x, np.float64) for x in (q, k, v, do))
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    vis = oa._visible(np.arange(Sq), Sq, Sk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            kvh = oa.kv_head_of(hq, Hq, Hkv)
+            dq[b, hq], dk[b, kvh], dv[b, kvh] = oa._attend_grad(q[b, hq], k[b, kvh], v[b, kvh], do[b, hq], vis, scale)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("mutant,attr", [
+    (_grad_no_delta, "_attend_grad"),
+    (_grad_no_scale, "_attend_grad"),
+    (_grad_dk_from_do, "_attend_grad"),
+    (_grad_dv_from_q, "_attend_grad"),
+    (_sdpa_backward_gqa_overwrite, "sdpa_backward"),
+])
+def test_backward_planted_mistakes_are_caught(monkeypatch, mutant, attr):
+    monkeypatch.setattr(oa, attr, mutant)
+    if attr == "sdpa_backward":
+        monkeypatch.setattr(oracle, "sdpa_backward", mutant)
+    assert _run_bwd_pins(), f"no backward pin caught the planted mistake in {attr}"
