@@ -47,6 +47,10 @@ def load() -> ctypes.CDLL:
     lib.fa_decode_workspace_size.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_decode.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_bwd.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -120,6 +124,52 @@ def fa_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None
     if st != FA_OK:
         raise FAError("fa_fwd", st)
     return out, lse
+
+
+def fa_bwd_workspace_size(B: int, Hq: int, Sq: int) -> int:
+    return int(load().fa_bwd_workspace_size(B, Hq, Sq))
+
+
+def fa_bwd(q, k, v, o, dout, lse, causal: bool, scale: float | None = None, dq=None, dk=None, dv=None,
+           workspace=None):
+    """Attention backward (bf16): gradients of sum(dout * o) for o = fa_fwd(q, k, v).
+
+    q, o, dout [B,Hq,Sq,d]; k, v [B,Hkv,Sk,d]; lse [B,Hq,Sq] fp32 from the forward.
+    Returns ``(dq, dk, dv)`` in bf16.
+    """
+    lib = load()
+    dt = torch.bfloat16
+    _check(q, "q", dt, 4)
+    for t, n in ((k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, n, dt, 4, q.device)
+    _check(lse, "lse", torch.float32, 3, q.device)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k={tuple(k.shape)} v={tuple(v.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape or tuple(lse.shape) != (B, Hq, Sq):
+        raise ValueError("o and dout must have q's shape, lse must be [B, Hq, Sq]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    outs = []
+    for t, ref, n in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        if t is None:
+            t = torch.empty_like(ref)
+        else:
+            _check(t, n, dt, 4, q.device)
+            if t.shape != ref.shape:
+                raise ValueError(f"{n} must have the shape of {'q' if n == 'dq' else 'k'}")
+        outs.append(t)
+    dq, dk, dv = outs
+    need = fa_bwd_workspace_size(B, Hq, Sq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                    B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_bwd", st)
+    return dq, dk, dv
 
 
 def fa_decode_workspace_size(nseq: int, Hq: int, Hkv: int, d: int, block_size: int,

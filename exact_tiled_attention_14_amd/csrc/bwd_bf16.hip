@@ -1,0 +1,351 @@
+// Attention backward, bf16 in / bf16 gradients, fp32 accumulation, gfx950.
+//
+// The backward pass keeps only O and the per-row log-sum-exp from the
+// forward and recomputes the scores and probabilities block by block from
+// Q, K, V ("Fast Inference and Training at Scale", section 6.21, Idea 2;
+// "Week 13. GPUs and FlashAttention", Step 2).  With P = exp(scale S - lse)
+// exact from the stored lse, the gradients of the definition are
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
+//   dQ = scale dS K,  dK = scale dS^T Q,
+//
+// (D_i equals sum_j P_ij dP_ij because O = P V).  Three kernels, no atomics:
+//
+//   * bwd_delta_kernel: D for every query row (16 lanes per row, DPP sum).
+//   * bwd_dq_kernel: one workgroup per (batch, query head, 128-row Q block),
+//     walking the K/V blocks the rows can see, like the forward.  Each wave
+//     owns 32 query rows and computes S^T = K Q^T and dP^T = V dO^T on the
+//     matrix cores (so every lane holds one query row: its lse and D are one
+//     value), forms dS^T in registers, and accumulates dQ^T += K^T dS^T with
+//     the K tile read transposed from LDS.
+//   * bwd_dkdv_kernel: one workgroup per (batch, K/V head, 128-key block),
+//     each wave owning 32 keys, walking the query heads of the GQA group and
+//     their 32-row Q blocks that see the keys.  S = Q K^T and dP = dO V^T put
+//     one key per lane; dV^T += dO^T P and dK^T += Q^T dS take P and dS
+//     straight from registers and dO, Q read transposed from LDS.  Summing
+//     over the query heads of the group is the GQA gradient.
+//
+// LDS tiles are row-major 256-byte rows (d = 128) with 16-byte chunks
+// XOR-swizzled by 4 (row mod 4) + (row / 4 mod 4): both the row reads (16
+// rows, one chunk) and the transposing reads (4 rows, 4 chunks) of a tile
+// then hit distinct banks.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kROWB = kD * 2;          // bytes per tile row
+constexpr int kWavesB = 4;
+constexpr int kThreadsB = 64 * kWavesB;
+constexpr int kQRows = 32 * kWavesB;   // query rows per dQ workgroup
+constexpr int kKRows = 32 * kWavesB;   // keys per dK/dV workgroup
+constexpr int kKVBlk = 64;             // keys per dQ inner step
+constexpr int kQBlk = 32;              // query rows per dK/dV inner step
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
+// Copy rows r0 .. r0+ROWS-1 of a [S, 128] bf16 matrix into an LDS tile with
+// the global-to-LDS load; rows past S repeat row S-1.  Load sl fills the
+// 1 KiB slice sl (4 rows); lane l lands at byte 16 l of it and fetches the
+// logical chunk that the swizzle places there.
+template <int ROWS>
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, uint8_t* tile, int r0, int S, int wave,
+                                         int lane) {
+    const int rr = lane >> 4, ch = lane & 15;
+#pragma unroll
+    for (int sl = wave; sl < ROWS / 4; sl += kWavesB) {
+        const int row = 4 * sl + rr;
+        const uint16_t* g = src + (int64_t)min(r0 + row, S - 1) * kD + 8 * (ch ^ swz(row));
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                         (__attribute__((address_space(3))) void*)(tile + sl * 1024), 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// MFMA operand from tile row `row`: head-dim elements 16 s + 8 hh .. +7.
+__device__ __forceinline__ bf16x8 row_operand(const uint8_t* tile, int row, int s, int hh) {
+    return *reinterpret_cast<const bf16x8*>(tile + row * kROWB + 16 * ((2 * s + hh) ^ swz(row)));
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+// Transposed operand: lane l gets column 32 db + l % 32 of the tile for the
+// tile rows 16 ks + 4 h + e and 16 ks + 8 + 4 h + e (h = l / 32, e = 0..3),
+// the order in which a lane half holds a 16-row slice of an accumulator.
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, int ks, int db, int lane) {
+    const int s = lane & 15, g = lane >> 4, h = g >> 1;
+    const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);
+    const int row0 = 16 * ks + 4 * h + (s >> 2), row1 = row0 + 8;
+    const int x = col >> 3, half = (col >> 2) & 1;
+    const s16x4 a = lds_read_tr16(tile + row0 * kROWB + 16 * (x ^ swz(row0)) + 8 * half);
+    const s16x4 b = lds_read_tr16(tile + row1 * kROWB + 16 * (x ^ swz(row1)) + 8 * half);
+    const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Accumulator values -> bf16 B operands: k-step ks takes registers 8 ks .. +7
+// of a 32x32 block (rows 16 ks + 4 h + e, 16 ks + 8 + 4 h + e in lane half h).
+__device__ __forceinline__ void pack_operand(u32x4 (&out)[2], const float (&x)[16]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) out[ks][w] = pack_bf16x2(x[8 * ks + 2 * w], x[8 * ks + 2 * w + 1]);
+}
+
+// 8 head-dim elements of row `row` of a [S, 128] bf16 matrix for MFMA step s
+// (elements 16 s + 8 hh .. +7), zero for rows past S.
+__device__ __forceinline__ void load_row_operands(bf16x8 (&x)[kD / 16], const uint16_t* src, int row, int S, int hh) {
+    const uint16_t* p = src + (int64_t)min(row, S - 1) * kD + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < kD / 16; ++s) {
+        const bf16x8 v = *reinterpret_cast<const bf16x8*>(p + 16 * s);
+        x[s] = row < S ? v : bf16x8{};
+    }
+}
+
+// bf16 rows of an accumulator group written to a [S, 128] matrix: lane = row
+// (`row`, skipped past S), register 4 a + e of block db = column 32 db + 8 a + 4 hh + e.
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[kD / 32], float mul, int row, int S,
+                                           int hh) {
+    if (row >= S) return;
+    uint16_t* p = dst + (int64_t)row * kD;
+#pragma unroll
+    for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int d0 = 32 * db + 8 * a + 4 * hh;
+            const u32x2 w = {pack_bf16x2(acc[db][4 * a + 0] * mul, acc[db][4 * a + 1] * mul),
+                             pack_bf16x2(acc[db][4 * a + 2] * mul, acc[db][4 * a + 3] * mul)};
+            *reinterpret_cast<u32x2*>(p + d0) = w;
+        }
+}
+
+// D_i = sum_d dO_id O_id for every query row; one row per 16 lanes.
+__global__ __launch_bounds__(kThreadsB) void bwd_delta_kernel(const uint16_t* __restrict__ O,
+                                                              const uint16_t* __restrict__ dO,
+                                                              float* __restrict__ delta, int64_t rows) {
+    const int64_t row = (int64_t)blockIdx.x * (kThreadsB / 16) + (threadIdx.x >> 4);
+    const int t = threadIdx.x & 15;
+    float acc = 0.f;
+    if (row < rows) {
+        const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * kD + 8 * t);
+        const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * kD + 8 * t);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const uint32_t ow = o[w], gw = g[w];
+            acc = fmaf(bf16lo_to_f32(ow), bf16lo_to_f32(gw), acc);
+            acc = fmaf(bf16hi_to_f32(ow), bf16hi_to_f32(gw), acc);
+        }
+    }
+    acc = row_sum16(acc);
+    if (row < rows && t == 0) delta[row] = acc;
+}
+
+// lse (natural log) -> the log2-domain offset of exp2; a row with no visible
+// key (lse = -inf) gets +inf so that every p of it is exactly 0.
+__device__ __forceinline__ float lse_offset(float lse) { return lse == kNegInf ? __builtin_inff() : lse * kLog2e; }
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2, float scale, int n_qblk) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kKVBlk * kROWB];
+    uint8_t* const kt = lds;
+    uint8_t* const vt = lds + kKVBlk * kROWB;
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh_n = B * Hq;
+    const int rank = blockIdx.x / bh_n, rem = blockIdx.x % bh_n;
+    const int qb = CAUSAL ? n_qblk - 1 - rank : rank;     // heaviest causal blocks first
+    const int b = rem / Hq, hq = rem % Hq, kvh = hq / (Hq / Hkv);
+    const int64_t bhq = (int64_t)b * Hq + hq;
+    const uint16_t* Kh = K + ((int64_t)b * Hkv + kvh) * Sk * kD;
+    const uint16_t* Vh = V + ((int64_t)b * Hkv + kvh) * Sk * kD;
+    const int diag = Sk - Sq;
+    const int my_q = qb * kQRows + wave * 32 + l32;
+
+    bf16x8 qf[kD / 16], gf[kD / 16];
+    load_row_operands(qf, Q + bhq * Sq * kD, my_q, Sq, hh);
+    load_row_operands(gf, dO + bhq * Sq * kD, my_q, Sq, hh);
+    const float lo = my_q < Sq ? lse_offset(LSE[bhq * Sq + my_q]) : __builtin_inff();
+    const float Dq = my_q < Sq ? delta[bhq * Sq + my_q] : 0.f;
+
+    int kv_end = Sk;
+    if (CAUSAL) kv_end = min(Sk, max(0, qb * kQRows + kQRows + diag));
+    const int n_it = (kv_end + kKVBlk - 1) / kKVBlk;
+
+    f32x16 dq[kD / 32];
+#pragma unroll
+    for (int i = 0; i < kD / 32; ++i) dq[i] = f32x16{};
+
+    for (int it = 0; it < n_it; ++it) {
+        const int kv0 = it * kKVBlk;
+        __syncthreads();                                   // the previous tiles are no longer read
+        dma_rows<kKVBlk>(Kh, kt, kv0, Sk, wave, lane);
+        dma_rows<kKVBlk>(Vh, vt, kv0, Sk, wave, lane);
+        wait_vm();
+        __syncthreads();
+
+        // S^T = K Q^T and dP^T = V dO^T for keys kv0 .. kv0+63 (two 32-key blocks)
+        f32x16 st[2] = {f32x16{}, f32x16{}}, pt[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                st[blk] = mfma32(row_operand(kt, 32 * blk + l32, s, hh), qf[s], st[blk]);
+                pt[blk] = mfma32(row_operand(vt, 32 * blk + l32, s, hh), gf[s], pt[blk]);
+            }
+        }
+        // dS^T = P^T o (dP^T - D): register r of block blk is key kv0 + 32 blk + acc_row(r, hh)
+        u32x4 dsw[4];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            float ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kv0 + 32 * blk + acc_row(r, hh);
+                const bool ok = key < Sk && (!CAUSAL || key <= my_q + diag);
+                const float p = ok ? exp2f_hw(fmaf(st[blk][r], scale_log2, -lo)) : 0.f;
+                ds[r] = p * (pt[blk][r] - Dq);
+            }
+            u32x4 two[2];
+            pack_operand(two, ds);
+            dsw[2 * blk] = two[0];
+            dsw[2 * blk + 1] = two[1];
+        }
+        // dQ^T += K^T dS^T over the 64 keys (4 steps of 16)
+#pragma unroll
+        for (int ks = 0; ks < kKVBlk / 16; ++ks) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, dsw[ks]);
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) dq[db] = mfma32(tr_operand(kt, ks, db, lane), bop, dq[db]);
+        }
+    }
+    store_rows(dQ + bhq * Sq * kD, dq, scale, my_q, Sq, hh);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
+    float scale) {
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kQBlk * kROWB];
+    __shared__ float s_lo[kQBlk], s_d[kQBlk];
+    uint8_t* const qt = lds;
+    uint8_t* const gt = lds + kQBlk * kROWB;
+
+    const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int bh_n = B * Hkv;
+    const int kb = blockIdx.x / bh_n, rem = blockIdx.x % bh_n;   // key block 0 (most causal work) first
+    const int b = rem / Hkv, kvh = rem % Hkv;
+    const int g = Hq / Hkv;
+    const int64_t bhk = (int64_t)b * Hkv + kvh;
+    const int diag = Sk - Sq;
+    const int k0 = kb * kKRows;
+    const int my_k = k0 + wave * 32 + l32;
+
+    bf16x8 kf[kD / 16], vf[kD / 16];
+    load_row_operands(kf, K + bhk * Sk * kD, my_k, Sk, hh);
+    load_row_operands(vf, V + bhk * Sk * kD, my_k, Sk, hh);
+
+    f32x16 dk[kD / 32], dv[kD / 32];
+#pragma unroll
+    for (int i = 0; i < kD / 32; ++i) dk[i] = dv[i] = f32x16{};
+
+    // the first query row that sees key k0 (bottom-right causal)
+    const int q_first = CAUSAL ? max(0, k0 - diag) : 0;
+    const int qb0 = q_first / kQBlk, n_qb = (Sq + kQBlk - 1) / kQBlk;
+    for (int j = 0; j < g; ++j) {
+        const int64_t bhq = (int64_t)b * Hq + kvh * g + j;
+        const uint16_t* Qh = Q + bhq * Sq * kD;
+        const uint16_t* Gh = dO + bhq * Sq * kD;
+        for (int qb = qb0; qb < n_qb; ++qb) {
+            const int q0 = qb * kQBlk;
+            __syncthreads();                               // the previous tiles are no longer read
+            dma_rows<kQBlk>(Qh, qt, q0, Sq, wave, lane);
+            dma_rows<kQBlk>(Gh, gt, q0, Sq, wave, lane);
+            if (tid < kQBlk) {
+                const int q = q0 + tid;
+                s_lo[tid] = q < Sq ? lse_offset(LSE[bhq * Sq + q]) : __builtin_inff();
+                s_d[tid] = q < Sq ? delta[bhq * Sq + q] : 0.f;
+            }
+            wait_vm();
+            __syncthreads();
+
+            // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
+            f32x16 st = f32x16{}, pt = f32x16{};
+#pragma unroll
+            for (int s = 0; s < kD / 16; ++s) {
+                st = mfma32(row_operand(qt, l32, s, hh), kf[s], st);
+                pt = mfma32(row_operand(gt, l32, s, hh), vf[s], pt);
+            }
+            float p[16], ds[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int qi = acc_row(r, hh), q = q0 + qi;
+                const bool ok = q < Sq && my_k < Sk && (!CAUSAL || my_k <= q + diag);
+                p[r] = ok ? exp2f_hw(fmaf(st[r], scale_log2, -s_lo[qi])) : 0.f;
+                ds[r] = p[r] * (pt[r] - s_d[qi]);
+            }
+            u32x4 pw[2], dsw[2];
+            pack_operand(pw, p);
+            pack_operand(dsw, ds);
+            // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows (2 steps of 16)
+#pragma unroll
+            for (int ks = 0; ks < kQBlk / 16; ++ks) {
+                const bf16x8 bp = __builtin_bit_cast(bf16x8, pw[ks]), bd = __builtin_bit_cast(bf16x8, dsw[ks]);
+#pragma unroll
+                for (int db = 0; db < kD / 32; ++db) {
+                    dv[db] = mfma32(tr_operand(gt, ks, db, lane), bp, dv[db]);
+                    dk[db] = mfma32(tr_operand(qt, ks, db, lane), bd, dk[db]);
+                }
+            }
+        }
+    }
+    store_rows(dK + bhk * Sk * kD, dk, scale, my_k, Sk, hh);
+    store_rows(dV + bhk * Sk * kD, dv, 1.f, my_k, Sk, hh);
+}
+
+template <bool CAUSAL>
+hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+    const float scale_log2 = a.scale * kLog2e;
+    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(kThreadsB), 0, stream,
+                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_qblk = (a.Sq + kQRows - 1) / kQRows;
+    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)), dim3(kThreadsB), 0,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
+                       scale_log2, a.scale, n_qblk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_kblk = (a.Sk + kKRows - 1) / kKRows;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hkv * n_kblk)), dim3(kThreadsB), 0,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv,
+                       a.Sq, a.Sk, scale_log2, a.scale);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+    return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+}
+
+}  // namespace fa

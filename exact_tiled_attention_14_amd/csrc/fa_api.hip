@@ -64,6 +64,36 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Sq) {
+    if (B < 1 || Hq < 1 || Sq < 1 || !fits(B, Hq, Sq, 4)) return 0;
+    return ((size_t)B * Hq * Sq * sizeof(float) + 255) & ~(size_t)255;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    for (const void* p : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+        if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(lse) & 3u) return FA_ERR_INVALID_ARG;
+    if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk, d)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * ((Sq + 127) / 128) > INT32_MAX || (int64_t)B * Hkv * ((Sk + 127) / 128) > INT32_MAX ||
+        ((int64_t)B * Hq * Sq + 15) / 16 > INT32_MAX)
+        return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_bwd_workspace_size(B, Hq, Sq);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
+
+    fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, Sq, Sk, d,
+                  causal, scale};
+    const hipError_t e = fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_size(int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq) {
     if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1) return 0;
     if (d != 128 || block_size != 16) return 0;

@@ -178,6 +178,17 @@ def make_prefill(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, *, causal:
 
 # --- paged decode ----------------------------------------------------------
 
+def make_grad_out(shape, *, seed: int = 0, dtype: str = "bf16") -> np.ndarray:
+    """Seeded N(0,1) upstream gradient dO of the given shape (bf16-exact
+    fp32 for dtype "bf16"), from its own stream: the backward workloads pair
+    it with ``make_prefill`` inputs of the same seed."""
+    (rg,) = _streams(seed + 0x9E3779B9, 1)
+    g = _normal(rg, tuple(shape))
+    if dtype == "bf16":
+        _round_bf16_inplace(g)
+    return g
+
+
 @dataclass
 class DecodeCase:
     """One paged decode step: one new query token per sequence.

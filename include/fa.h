@@ -49,7 +49,7 @@ typedef enum {
     FA_OK = 0,
     FA_ERR_INVALID_ARG = -1,   /* null pointer, bad size, misalignment, scale not finite and > 0 */
     FA_ERR_UNSUPPORTED = -2,   /* valid request outside the built kernel set (head dim, dtype, page size) */
-    FA_ERR_WORKSPACE = -3,     /* decode workspace missing or smaller than fa_decode_workspace_size() */
+    FA_ERR_WORKSPACE = -3,     /* workspace missing, misaligned or smaller than the matching *_workspace_size() */
     FA_ERR_HIP = -4            /* the HIP runtime reported an error at launch */
 } fa_status;
 
@@ -84,6 +84,47 @@ typedef enum {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
            int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_size - bytes of scratch that fa_bwd needs: one fp32 per
+ * query row (the row sums D = rowsum(dO * O)), rounded up to 256 bytes.
+ * Returns 0 for sizes fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Sq);
+
+/*
+ * fa_bwd - attention backward: gradients of sum(dout * o) with respect to
+ * q, k and v, where o = softmax(scale q k^T) v as computed by fa_fwd.
+ *
+ * Passage: "Fast Inference and Training at Scale", section 6.21, Idea 2
+ * (the backward pass recomputes the probabilities block by block instead of
+ * loading them); "Week 13. GPUs and FlashAttention", Step 2 (only O and the
+ * per-row logsumexp are kept from the forward).  The probabilities are
+ * P = exp(scale q k^T - lse) from the stored lse, and
+ * dv = P^T dout, dS = P * (dout v^T - rowsum(dout * o)),
+ * dq = scale dS k, dk = scale dS^T q; under grouped-query attention dk and
+ * dv of a K/V head sum over its Hq/Hkv query heads.
+ *
+ *   q, o, dout  [B, Hq,  Sq, d]   bf16   (read)
+ *   k, v        [B, Hkv, Sk, d]   bf16   (read)
+ *   lse         [B, Hq,  Sq]      fp32   (read; natural log, as fa_fwd writes it;
+ *                                        -inf marks a row with no visible key)
+ *   dq          [B, Hq,  Sq, d]   bf16   (written)
+ *   dk, dv      [B, Hkv, Sk, d]   bf16   (written)
+ *   workspace   caller-owned device scratch of at least
+ *               fa_bwd_workspace_size(B, Hq, Sq) bytes, 256-byte aligned
+ *
+ *   Sizes, causal and scale as for fa_fwd (bottom-right causal alignment).
+ *   Supported: d == 128; anything else returns FA_ERR_UNSUPPORTED.  All
+ *   tensor pointers 16-byte aligned, lse 4-byte aligned.  dq, dk, dv must
+ *   not overlap the inputs.  Deterministic: no atomics.
+ *
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+           const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+           int Sk, int d, int causal, float scale, void* workspace, size_t workspace_bytes,
+           void* stream);
 
 /*
  * fa_decode_workspace_size - bytes of scratch that fa_decode needs.

@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_decode", "fa_decode_workspace_size", "fa_fwd", "fa_status_string"]
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
+                           "fa_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -90,3 +91,28 @@ def _dec(lib, q=16, kc=32, vc=48, bt=64, sl=80, o=96, nseq=2, Hq=8, Hkv=2, d=128
 ])
 def test_decode_rejects_before_launch(lib, kw, status):
     assert _dec(lib, **kw) == status
+
+
+def _bwd(lib, q=16, k=32, v=48, o=64, g=80, lse=96, dq=112, dk=128, dv=144, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=128,
+         causal=1, scale=0.1, ws=256, wsb=1 << 20):
+    P = ctypes.c_void_p
+    return lib.fa_bwd(P(q), P(k), P(v), P(o), P(g), P(lse), P(dq), P(dk), P(dv), B, Hq, Hkv, Sq, Sk, d, causal,
+                      scale, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(lse=0), -1), (dict(dv=0), -1), (dict(B=0), -1), (dict(Sk=0), -1),
+    (dict(Hq=3, Hkv=2), -1), (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(scale=float("nan")), -1),
+    (dict(o=72), -1), (dict(dk=136), -1), (dict(lse=98), -1),
+    (dict(d=64), -2),
+    (dict(ws=0), -3), (dict(wsb=16), -3), (dict(ws=264), -3),
+])
+def test_bwd_rejects_before_launch(lib, kw, status):
+    assert _bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_size_is_one_float_per_row(lib):
+    f = lib.fa_bwd_workspace_size
+    assert f(2, 16, 2048) == 2 * 16 * 2048 * 4
+    assert f(1, 1, 3) == 256
+    assert f(0, 16, 2048) == 0 and f(1, 0, 1) == 0 and f(1, 1, 0) == 0
