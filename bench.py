@@ -60,6 +60,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads per oracle call when timing the CPU baseline")
     args = ap.parse_args()
 
@@ -216,6 +217,42 @@ def main():
         "fp32_prefill_us": round(sf["mean"] * 1e3, 2),
         "wall_s_timed_region": round(wall, 4),
     }
+
+    # ---- attention backward on the headline shape, timed on its own ----
+    if not args.no_backward:
+        log("backward: inputs")
+        g_do = to_dev(inputs.bf16_bits(inputs.make_grad_out(cp.q.shape, seed=2)))
+        binding.fa_fwd(p_q, p_k, p_v, True, cp.scale, out=p_o, lse=p_l)
+        b_dq, b_dk, b_dv = torch.empty_like(p_q), torch.empty_like(p_k), torch.empty_like(p_v)
+        b_ws = torch.empty(binding.fa_bwd_workspace_size(shp["B"], shp["Hq"], shp["Sq"]), dtype=torch.uint8,
+                           device=dev)
+
+        def run_bwd():
+            binding.fa_bwd(p_q, p_k, p_v, p_o, g_do, p_l, True, cp.scale, dq=b_dq, dk=b_dk, dv=b_dv, workspace=b_ws)
+
+        for _ in range(2):
+            run_bwd()
+        reps = max(5, min(K, 20))
+        evs = [(ev(), ev()) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for a, b in evs:
+            a.record(stream)
+            run_bwd()
+            b.record(stream)
+        torch.cuda.synchronize()
+        st = metrics.summarize([a.elapsed_time(b) for a, b in evs])
+        fl = metrics.backward_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
+        tf = fl / (st["mean"] * 1e-3) / 1e12
+        result["backward"] = {
+            "workload": PREFILL, "kernels": "bwd_delta_kernel + bwd_dq_kernel<causal> + bwd_dkdv_kernel<causal>",
+            "bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+            "frac": round(tf / peak_tf, 4), "algorithmic_flops_per_launch": fl,
+            "note": "algorithmic = 5 products of 2d FLOP per visible pair; the kernels execute 7 (S and dP are "
+                    "recomputed in both the dQ and the dK/dV kernel)",
+            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
+        }
+        log(f"backward: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
+        del g_do, b_dq, b_dk, b_dv, b_ws
 
     # ---- larger prefill workloads, timed on their own ----
     if not args.no_extra:

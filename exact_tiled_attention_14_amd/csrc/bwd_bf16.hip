@@ -25,6 +25,11 @@
 //     straight from registers and dO, Q read transposed from LDS.  Summing
 //     over the query heads of the group is the GQA gradient.
 //
+// The LDS helpers take __restrict__ stage pointers: the compiler then does
+// not make a read of one stage wait for the global-to-LDS prefetch into the
+// other (the kernels' own wait and barrier before each step already order
+// every read after the loads of its stage).
+//
 // LDS tiles are row-major 256-byte rows (d = 128) with 16-byte chunks
 // XOR-swizzled by 4 (row mod 4) + (row / 4 mod 4): both the row reads (16
 // rows, one chunk) and the transposing reads (4 rows, 4 chunks) of a tile
@@ -54,11 +59,13 @@ __device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2)
 // 1 KiB slice sl (4 rows); lane l lands at byte 16 l of it and fetches the
 // logical chunk that the swizzle places there.
 template <int ROWS>
-__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, uint8_t* tile, int r0, int S, int wave,
-                                         int lane) {
+__device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, uint8_t* __restrict__ tile, int r0, int S,
+                                         int wave, int lane) {
+    static_assert(ROWS % (4 * kWavesB) == 0, "every wave issues the same number of loads");
     const int rr = lane >> 4, ch = lane & 15;
 #pragma unroll
-    for (int sl = wave; sl < ROWS / 4; sl += kWavesB) {
+    for (int i = 0; i < ROWS / 4 / kWavesB; ++i) {
+        const int sl = wave + i * kWavesB;
         const int row = 4 * sl + rr;
         const uint16_t* g = src + (int64_t)min(r0 + row, S - 1) * kD + 8 * (ch ^ swz(row));
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -69,11 +76,11 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, uint8
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // MFMA operand from tile row `row`: head-dim elements 16 s + 8 hh .. +7.
-__device__ __forceinline__ bf16x8 row_operand(const uint8_t* tile, int row, int s, int hh) {
+__device__ __forceinline__ bf16x8 row_operand(const uint8_t* __restrict__ tile, int row, int s, int hh) {
     return *reinterpret_cast<const bf16x8*>(tile + row * kROWB + 16 * ((2 * s + hh) ^ swz(row)));
 }
 
-__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
+__device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* __restrict__ p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) uint8_t*)p);
 }
@@ -81,7 +88,7 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 // Transposed operand: lane l gets column 32 db + l % 32 of the tile for the
 // tile rows 16 ks + 4 h + e and 16 ks + 8 + 4 h + e (h = l / 32, e = 0..3),
 // the order in which a lane half holds a 16-row slice of an accumulator.
-__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* tile, int ks, int db, int lane) {
+__device__ __forceinline__ bf16x8 tr_operand(const uint8_t* __restrict__ tile, int ks, int db, int lane) {
     const int s = lane & 15, g = lane >> 4, h = g >> 1;
     const int col = 32 * db + 16 * (g & 1) + 4 * (s & 3);
     const int row0 = 16 * ks + 4 * h + (s >> 2), row1 = row0 + 8;
@@ -159,9 +166,8 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2, float scale, int n_qblk) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kKVBlk * kROWB];
-    uint8_t* const kt = lds;
-    uint8_t* const vt = lds + kKVBlk * kROWB;
+    // two stages of (K tile, V tile): the next block lands while this one is used
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kKVBlk * kROWB];
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,13 +195,22 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int i = 0; i < kD / 32; ++i) dq[i] = f32x16{};
 
+    if (n_it > 0) {
+        dma_rows<kKVBlk>(Kh, lds[0], 0, Sk, wave, lane);
+        dma_rows<kKVBlk>(Vh, lds[0] + kKVBlk * kROWB, 0, Sk, wave, lane);
+    }
     for (int it = 0; it < n_it; ++it) {
         const int kv0 = it * kKVBlk;
-        __syncthreads();                                   // the previous tiles are no longer read
-        dma_rows<kKVBlk>(Kh, kt, kv0, Sk, wave, lane);
-        dma_rows<kKVBlk>(Vh, vt, kv0, Sk, wave, lane);
+        // block it has landed for every wave, and every wave is done with block it-1,
+        // whose stage the next block goes to
         wait_vm();
         __syncthreads();
+        if (it + 1 < n_it) {
+            dma_rows<kKVBlk>(Kh, lds[(it + 1) & 1], kv0 + kKVBlk, Sk, wave, lane);
+            dma_rows<kKVBlk>(Vh, lds[(it + 1) & 1] + kKVBlk * kROWB, kv0 + kKVBlk, Sk, wave, lane);
+        }
+        const uint8_t* kt = lds[it & 1];
+        const uint8_t* vt = kt + kKVBlk * kROWB;
 
         // S^T = K Q^T and dP^T = V dO^T for keys kv0 .. kv0+63 (two 32-key blocks)
         f32x16 st[2] = {f32x16{}, f32x16{}}, pt[2] = {f32x16{}, f32x16{}};
@@ -241,10 +256,9 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
     float scale) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * kQBlk * kROWB];
-    __shared__ float s_lo[kQBlk], s_d[kQBlk];
-    uint8_t* const qt = lds;
-    uint8_t* const gt = lds + kQBlk * kROWB;
+    // two stages of (Q tile, dO tile) and of the rows' lse offsets and D
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kQBlk * kROWB];
+    __shared__ float s_lo[2][kQBlk], s_d[2][kQBlk];
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -268,50 +282,97 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     // the first query row that sees key k0 (bottom-right causal)
     const int q_first = CAUSAL ? max(0, k0 - diag) : 0;
     const int qb0 = q_first / kQBlk, n_qb = (Sq + kQBlk - 1) / kQBlk;
-    for (int j = 0; j < g; ++j) {
-        const int64_t bhq = (int64_t)b * Hq + kvh * g + j;
-        const uint16_t* Qh = Q + bhq * Sq * kD;
-        const uint16_t* Gh = dO + bhq * Sq * kD;
-        for (int qb = qb0; qb < n_qb; ++qb) {
-            const int q0 = qb * kQBlk;
-            __syncthreads();                               // the previous tiles are no longer read
-            dma_rows<kQBlk>(Qh, qt, q0, Sq, wave, lane);
-            dma_rows<kQBlk>(Gh, gt, q0, Sq, wave, lane);
-            if (tid < kQBlk) {
-                const int q = q0 + tid;
-                s_lo[tid] = q < Sq ? lse_offset(LSE[bhq * Sq + q]) : __builtin_inff();
-                s_d[tid] = q < Sq ? delta[bhq * Sq + q] : 0.f;
-            }
-            wait_vm();
-            __syncthreads();
+    // the (query head, Q block) steps of this workgroup, flattened so that
+    // the next step's tiles are loaded while the current one is computed
+    const int per_head = max(0, n_qb - qb0);
+    const int n_steps = g * per_head;
+    auto step_src = [&](int t, int64_t& bhq, int& q0) {
+        bhq = (int64_t)b * Hq + kvh * g + t / per_head;
+        q0 = (qb0 + t % per_head) * kQBlk;
+    };
+    // The next step's Q and dO rows are loaded into registers while the
+    // current step computes (each thread holds two 16-byte chunks of each
+    // tile: chunk c = tid + 256 i is row c / 16, logical chunk c % 16) and
+    // written to the other LDS stage, swizzled, at the start of the next
+    // step; the raw lse and D of the rows (lanes < kQBlk, row clamped to
+    // Sq-1) likewise.  Staging through registers instead of global-to-LDS
+    // loads keeps the compiler from waiting for the prefetch before the
+    // first LDS read of the step.
+    constexpr int kChunks = kQBlk * kD / 8 / kThreadsB;    // 16-byte chunks per thread per tile
+    u32x4 qn[kChunks], gn[kChunks];
+    float lse_next = 0.f, d_next = 0.f;
+    auto fetch = [&](int t) {
+        int64_t bhq;
+        int q0;
+        step_src(t, bhq, q0);
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = tid + kThreadsB * i, row = c >> 4, ch = c & 15;
+            const int64_t at = (bhq * Sq + min(q0 + row, Sq - 1)) * kD + 8 * ch;
+            qn[i] = *reinterpret_cast<const u32x4*>(Q + at);
+            gn[i] = *reinterpret_cast<const u32x4*>(dO + at);
+        }
+        if (tid < kQBlk) {
+            const int64_t at = bhq * Sq + min(q0 + tid, Sq - 1);
+            lse_next = LSE[at];
+            d_next = delta[at];
+        }
+    };
+    if (n_steps > 0) fetch(0);
+    for (int t = 0; t < n_steps; ++t) {
+        const int stage = t & 1;
+        int64_t bhq_unused;
+        int q0;
+        step_src(t, bhq_unused, q0);
+        uint8_t* const qt = lds[stage];
+        uint8_t* const gt = qt + kQBlk * kROWB;
+#pragma unroll
+        for (int i = 0; i < kChunks; ++i) {
+            const int c = tid + kThreadsB * i, row = c >> 4, ch = c & 15;
+            const int off = row * kROWB + 16 * (ch ^ swz(row));
+            *reinterpret_cast<u32x4*>(qt + off) = qn[i];
+            *reinterpret_cast<u32x4*>(gt + off) = gn[i];
+        }
+        if (tid < kQBlk) {
+            const bool row_ok = q0 + tid < Sq;
+            s_lo[stage][tid] = row_ok ? lse_offset(lse_next) : __builtin_inff();
+            s_d[stage][tid] = row_ok ? d_next : 0.f;
+        }
+        // step t's tiles and row values are in place, and every wave is done
+        // with step t-1 (the other stage, rewritten at the start of step t+1)
+        __syncthreads();
+        if (t + 1 < n_steps) fetch(t + 1);
+        const float* lo_s = s_lo[stage];
+        const float* d_s = s_d[stage];
 
-            // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
-            f32x16 st = f32x16{}, pt = f32x16{};
+        // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
+        f32x16 st = f32x16{}, pt = f32x16{};
 #pragma unroll
-            for (int s = 0; s < kD / 16; ++s) {
-                st = mfma32(row_operand(qt, l32, s, hh), kf[s], st);
-                pt = mfma32(row_operand(gt, l32, s, hh), vf[s], pt);
-            }
-            float p[16], ds[16];
+        for (int s = 0; s < kD / 16; ++s) {
+            st = mfma32(row_operand(qt, l32, s, hh), kf[s], st);
+            pt = mfma32(row_operand(gt, l32, s, hh), vf[s], pt);
+        }
+        float p[16], ds[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int qi = acc_row(r, hh), q = q0 + qi;
-                const bool ok = q < Sq && my_k < Sk && (!CAUSAL || my_k <= q + diag);
-                p[r] = ok ? exp2f_hw(fmaf(st[r], scale_log2, -s_lo[qi])) : 0.f;
-                ds[r] = p[r] * (pt[r] - s_d[qi]);
-            }
-            u32x4 pw[2], dsw[2];
-            pack_operand(pw, p);
-            pack_operand(dsw, ds);
-            // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows (2 steps of 16)
+        for (int r = 0; r < 16; ++r) {
+            const int qi = acc_row(r, hh), q = q0 + qi;
+            const bool ok = q < Sq && my_k < Sk && (!CAUSAL || my_k <= q + diag);
+            const float lo = lo_s[qi], dd = d_s[qi];
+            const float e = exp2f_hw(fmaf(st[r], scale_log2, -lo));
+            p[r] = ok ? e : 0.f;
+            ds[r] = p[r] * (pt[r] - dd);
+        }
+        u32x4 pw[2], dsw[2];
+        pack_operand(pw, p);
+        pack_operand(dsw, ds);
+        // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows (2 steps of 16)
 #pragma unroll
-            for (int ks = 0; ks < kQBlk / 16; ++ks) {
-                const bf16x8 bp = __builtin_bit_cast(bf16x8, pw[ks]), bd = __builtin_bit_cast(bf16x8, dsw[ks]);
+        for (int ks = 0; ks < kQBlk / 16; ++ks) {
+            const bf16x8 bp = __builtin_bit_cast(bf16x8, pw[ks]), bd = __builtin_bit_cast(bf16x8, dsw[ks]);
 #pragma unroll
-                for (int db = 0; db < kD / 32; ++db) {
-                    dv[db] = mfma32(tr_operand(gt, ks, db, lane), bp, dv[db]);
-                    dk[db] = mfma32(tr_operand(qt, ks, db, lane), bd, dk[db]);
-                }
+            for (int db = 0; db < kD / 32; ++db) {
+                dv[db] = mfma32(tr_operand(gt, ks, db, lane), bp, dv[db]);
+                dk[db] = mfma32(tr_operand(qt, ks, db, lane), bd, dk[db]);
             }
         }
     }

@@ -37,6 +37,12 @@ def prefill_flops(B: int, Hq: int, Sq: int, Sk: int, d: int, causal: bool) -> in
     return 4 * d * B * Hq * visible_pairs(Sq, Sk, causal)
 
 
+def backward_flops(B: int, Hq: int, Sq: int, Sk: int, d: int, causal: bool) -> int:
+    """Algorithmic FLOPs of the attention backward: five products of 2 d FLOP
+    per visible (query, key) pair (S recomputed, dP = dO V^T, dV, dK, dQ)."""
+    return 10 * d * B * Hq * visible_pairs(Sq, Sk, causal)
+
+
 def prefill_min_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int,
                       in_bytes: int = 2, out_bytes: int = 2, with_lse: bool = True) -> int:
     reads = (B * Hq * Sq * d + 2 * B * Hkv * Sk * d) * in_bytes

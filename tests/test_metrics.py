@@ -66,3 +66,10 @@ def test_summarize():
     s = M.summarize([1.0, 2.0, 3.0, 4.0, 5.0])
     assert s["mean"] == 3.0 and s["p50"] == 3.0
     assert s["ci95"] == pytest.approx(2.776 * np.std([1, 2, 3, 4, 5], ddof=1) / np.sqrt(5), rel=1e-3)
+
+
+def test_backward_flops_are_five_products_per_pair():
+    from exact_tiled_attention_14_amd import metrics as M
+    for causal in (False, True):
+        f = M.prefill_flops(2, 16, 2048, 2048, 128, causal)
+        assert M.backward_flops(2, 16, 2048, 2048, 128, causal) * 2 == 5 * f
