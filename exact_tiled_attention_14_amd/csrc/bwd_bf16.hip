@@ -256,8 +256,10 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
     float scale) {
-    // two stages of (Q tile, dO tile) and of the rows' lse offsets and D
+    // two stages of (Q tile, dO tile) and of the rows' lse offsets and D, and
+    // the K and V rows of this workgroup's keys (operands of S and dP)
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kQBlk * kROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2][kKRows * kROWB];
     __shared__ float s_lo[2][kQBlk], s_d[2][kQBlk];
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -271,9 +273,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     const int k0 = kb * kKRows;
     const int my_k = k0 + wave * 32 + l32;
 
-    bf16x8 kf[kD / 16], vf[kD / 16];
-    load_row_operands(kf, K + bhk * Sk * kD, my_k, Sk, hh);
-    load_row_operands(vf, V + bhk * Sk * kD, my_k, Sk, hh);
+    dma_rows<kKRows>(K + bhk * Sk * kD, kv_lds[0], k0, Sk, wave, lane);
+    dma_rows<kKRows>(V + bhk * Sk * kD, kv_lds[1], k0, Sk, wave, lane);
+    wait_vm();
+    __syncthreads();
+    const int krow = wave * 32 + l32;          // this lane's key row in kv_lds
 
     f32x16 dk[kD / 32], dv[kD / 32];
 #pragma unroll
@@ -349,8 +353,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         f32x16 st = f32x16{}, pt = f32x16{};
 #pragma unroll
         for (int s = 0; s < kD / 16; ++s) {
-            st = mfma32(row_operand(qt, l32, s, hh), kf[s], st);
-            pt = mfma32(row_operand(gt, l32, s, hh), vf[s], pt);
+            st = mfma32(row_operand(qt, l32, s, hh), row_operand(kv_lds[0], krow, s, hh), st);
+            pt = mfma32(row_operand(gt, l32, s, hh), row_operand(kv_lds[1], krow, s, hh), pt);
         }
         float p[16], ds[16];
 #pragma unroll
