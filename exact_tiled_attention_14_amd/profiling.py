@@ -67,6 +67,18 @@ def _run(args) -> None:
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
         launches.append(("prefill", lambda: binding.fa_fwd(q, k, v, True, c.scale, out=o, lse=lse)))
+    if args.workload in ("backward", "all"):
+        c = inputs.workload(PREFILL)
+        bq, bk, bv = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
+        bo = torch.empty_like(bq)
+        bl = torch.empty(bq.shape[:3], dtype=torch.float32, device=dev)
+        binding.fa_fwd(bq, bk, bv, True, c.scale, out=bo, lse=bl)
+        bg = to_dev(inputs.bf16_bits(inputs.make_grad_out(c.q.shape, seed=2)))
+        grads = (torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv))
+        bws = torch.empty(binding.fa_bwd_workspace_size(*bq.shape[:3]), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        launches.append(("backward", lambda: binding.fa_bwd(bq, bk, bv, bo, bg, bl, True, c.scale, dq=grads[0],
+                                                            dk=grads[1], dv=grads[2], workspace=bws)))
     if args.workload in ("decode", "all"):
         d = inputs.workload(DECODE)
         s = d.shape
@@ -218,7 +230,7 @@ def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--workload", choices=["prefill", "decode", "all"], default="all")
+    r.add_argument("--workload", choices=["prefill", "decode", "backward", "all"], default="all")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--copy-mib", type=int, default=1024)
     s = sub.add_parser("summarize")
