@@ -8,7 +8,12 @@ One step runs the whole path once on resident synthetic inputs:
   * bf16 paged decode, 64 sequences x 1 token, Hq=32 Hkv=8 d=128, 16-token
     pages, lengths uniform in [1024, 8192]
 
-Each kernel launch is bracketed by HIP events on the stream it runs on.  The
+Each call is timed with HIP events that its own kernel launches record
+(fa_time_next_call: the first kernel's start to the last kernel's end, on the
+stream the kernels run on; the events skip the system-scope cache fence), the
+interval a kernel trace reports.  A spin kernel queued ahead of each timed
+loop lets the host enqueue every timed launch before the GPU gets there (the
+JSON's `host_lead` says whether it did).  The
 headline `value` is the algorithmic TFLOP/s of the causal prefill (4 d FLOP per
 visible query-key pair) over the prefill launch time; decode reports the
 algorithmic KV bytes (each attended token's K and V once) over the decode
@@ -47,6 +52,33 @@ EXTRA = ["causal_gqa_h32kv8_s8192_d128_outliers", "causal_gqa_h32kv8_s32768_d128
 PROFILE_PREFILL = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_b2_h16_s2048_d128.md")
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "decode_paged_64seq_h32kv8_d128.md")
 CPU_MIN_SECONDS = 10.0
+
+
+def gpu_lead(stream, ms):
+    """Queue a spin of about `ms` milliseconds on the stream (assuming a shader
+    clock near 2.4 GHz) so that the host enqueues the timed launches before the
+    GPU reaches them: the events then time the kernels, not the host's Python
+    and argument checks between launches.  Returns (start, end) events around
+    the spin."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(int(ms * 2.4e6))
+    b.record(stream)
+    return a, b
+
+
+def lead_report(lead, host_s):
+    """Whether the host finished enqueueing before the GPU finished the spin."""
+    spin_ms = lead[0].elapsed_time(lead[1])
+    return {"spin_ms": round(spin_ms, 3), "host_enqueue_ms": round(host_s * 1e3, 3),
+            "host_ahead": bool(host_s * 1e3 < spin_ms)}
+
+
+def kernel_events(n):
+    """n (start, stop) pairs of timing events for fa_time_next_call."""
+    from exact_tiled_attention_14_amd import binding
+    return [(binding.TimingEvent(), binding.TimingEvent()) for _ in range(n)]
 
 
 def log(msg):
@@ -132,33 +164,33 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    e_f = [(ev(), ev()) for _ in range(K)]
-    e_p = [(ev(), ev()) for _ in range(K)]
-    e_d = [(ev(), ev()) for _ in range(K)]
+    e_f, e_p, e_d = kernel_events(K), kernel_events(K), kernel_events(K)
     t_start, t_end = ev(), ev()
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
+    lead = gpu_lead(stream, 2.0 + 0.6 * K)
+    host0 = time.perf_counter()
     t_start.record(stream)
     for i in range(K):
-        e_f[i][0].record(stream)
+        binding.fa_time_next_call(*e_f[i])
         run_f32()
-        e_f[i][1].record(stream)
-        e_p[i][0].record(stream)
+        binding.fa_time_next_call(*e_p[i])
         run_prefill()
-        e_p[i][1].record(stream)
         flush.fill_(i & 0xFF)
-        e_d[i][0].record(stream)
+        binding.fa_time_next_call(*e_d[i])
         run_decode()
-        e_d[i][1].record(stream)
     t_end.record(stream)
+    host_s = time.perf_counter() - host0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
+    lead_main = lead_report(lead, host_s)
+    log(f"host lead: {lead_main}")
 
-    ms_f = [a.elapsed_time(b) for a, b in e_f]
-    ms_p = [a.elapsed_time(b) for a, b in e_p]
-    ms_d = [a.elapsed_time(b) for a, b in e_d]
+    ms_f = [a.elapsed_ms(b) for a, b in e_f]
+    ms_p = [a.elapsed_ms(b) for a, b in e_p]
+    ms_d = [a.elapsed_ms(b) for a, b in e_d]
     sp, sd, sf = metrics.summarize(ms_p), metrics.summarize(ms_d), metrics.summarize(ms_f)
 
     flops_p = metrics.prefill_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
@@ -199,6 +231,8 @@ def main():
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_flops_per_launch": flops_p,
             "launch_us": {k: round(v * 1e3, 2) for k, v in sp.items() if k != "n"},
+            "launch_timing": "HIP events recorded by the kernel launch itself (hipExtLaunchKernel; "
+                             "no system-scope fence), first kernel start to last kernel end",
         },
         "decode": {
             "workload": DECODE,
@@ -216,6 +250,7 @@ def main():
         },
         "fp32_prefill_us": round(sf["mean"] * 1e3, 2),
         "wall_s_timed_region": round(wall, 4),
+        "host_lead": lead_main,
     }
 
     # ---- attention backward on the headline shape, timed on its own ----
@@ -233,14 +268,17 @@ def main():
         for _ in range(2):
             run_bwd()
         reps = max(5, min(K, 20))
-        evs = [(ev(), ev()) for _ in range(reps)]
+        evs = kernel_events(reps)
         torch.cuda.synchronize()
+        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
+        host0 = time.perf_counter()
         for a, b in evs:
-            a.record(stream)
+            binding.fa_time_next_call(a, b)
             run_bwd()
-            b.record(stream)
+        host_s = time.perf_counter() - host0
         torch.cuda.synchronize()
-        st = metrics.summarize([a.elapsed_time(b) for a, b in evs])
+        lead_bwd = lead_report(lead, host_s)
+        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
         fl = metrics.backward_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
         tf = fl / (st["mean"] * 1e-3) / 1e12
         result["backward"] = {
@@ -250,6 +288,7 @@ def main():
             "note": "algorithmic = 5 products of 2d FLOP per visible pair; the kernels execute 7 (S and dP are "
                     "recomputed in both the dQ and the dK/dV kernel)",
             "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
+            "host_lead": lead_bwd,
         }
         log(f"backward: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
         del g_do, b_dq, b_dk, b_dv, b_ws
@@ -270,18 +309,21 @@ def main():
             for _ in range(2):
                 binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
             reps = max(3, min(K, 10))
-            evs = [(ev(), ev()) for _ in range(reps)]
+            evs = kernel_events(reps)
             torch.cuda.synchronize()
+            lead = gpu_lead(stream, 2.0 + 0.3 * reps)
+            host0 = time.perf_counter()
             for a, b in evs:
-                a.record(stream)
+                binding.fa_time_next_call(a, b)
                 binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
-                b.record(stream)
+            host_s = time.perf_counter() - host0
             torch.cuda.synchronize()
-            st = metrics.summarize([a.elapsed_time(b) for a, b in evs])
+            st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
             fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
             tf = fl / (st["mean"] * 1e-3) / 1e12
             extra[name] = {"us": round(st["mean"] * 1e3, 1), "TFLOP/s": round(tf, 1),
-                           "frac_bf16_peak": round(tf / peak_tf, 4), "reps": reps, "causal": spec["causal"]}
+                           "frac_bf16_peak": round(tf / peak_tf, 4), "reps": reps, "causal": spec["causal"],
+                           "host_lead": lead_report(lead, host_s)}
             log(f"{name}: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
             del q, k, v, o, lse
             torch.cuda.empty_cache()

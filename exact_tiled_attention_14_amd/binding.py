@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_time_next_call.argtypes = [vp, vp]
+    lib.fa_time_next_call.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -59,6 +61,73 @@ def load() -> ctypes.CDLL:
 
 def fa_status_string(status: int) -> str:
     return load().fa_status_string(int(status)).decode()
+
+
+_hip_rt = None
+
+
+def _hip():
+    """The HIP runtime already in the process (the one libfa.so is bound to)."""
+    global _hip_rt
+    if _hip_rt is None:
+        load()
+        lib = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        vp = ctypes.c_void_p
+        lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+        lib.hipEventRecord.argtypes = [vp, vp]
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+        lib.hipEventDestroy.argtypes = [vp]
+        for fn in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime", "hipEventDestroy"):
+            getattr(lib, fn).restype = ctypes.c_int
+        _hip_rt = lib
+    return _hip_rt
+
+
+class TimingEvent:
+    """A HIP timing event for fa_time_next_call.  It is created without the
+    system-scope fence (hipEventDisableSystemFence), so that recording it
+    does not write back and invalidate the caches between kernels: it is for
+    measuring, not for making results visible to the host."""
+
+    FLAGS = 0x20000000   # hipEventDisableSystemFence
+
+    def __init__(self):
+        self.handle = ctypes.c_void_p()
+        st = _hip().hipEventCreateWithFlags(ctypes.byref(self.handle), self.FLAGS)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    def record(self, stream=None):
+        """Record on a torch stream (default: the current one)."""
+        s = stream if stream is not None else torch.cuda.current_stream()
+        st = _hip().hipEventRecord(self.handle, ctypes.c_void_p(s.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_ms(self, stop: "TimingEvent") -> float:
+        """Milliseconds from this event to `stop`; both must have completed."""
+        ms = ctypes.c_float()
+        st = _hip().hipEventElapsedTime(ctypes.byref(ms), self.handle, stop.handle)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return float(ms.value)
+
+    def __del__(self):
+        if self.handle and _hip_rt is not None:
+            _hip_rt.hipEventDestroy(self.handle)
+            self.handle = ctypes.c_void_p()
+
+
+def fa_time_next_call(start: TimingEvent | None = None, stop: TimingEvent | None = None) -> None:
+    """Attach two TimingEvents to the kernels of the next fa_fwd / fa_bwd /
+    fa_decode call on this thread: after it, ``start.elapsed_ms(stop)`` is
+    the time from its first kernel's start to its last kernel's end.
+    ``None, None`` clears."""
+    if (start is None) != (stop is None):
+        raise ValueError("fa_time_next_call takes two events or none")
+    st = load().fa_time_next_call(None if start is None else start.handle, None if stop is None else stop.handle)
+    if st != FA_OK:
+        raise FAError("fa_time_next_call", st)
 
 
 def _ptr(t):

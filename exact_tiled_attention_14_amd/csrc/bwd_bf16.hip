@@ -388,19 +388,19 @@ template <bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
     const float scale_log2 = a.scale * kLog2e;
     const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(kThreadsB), 0, stream,
+    launch_kernel<false>(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(kThreadsB), 0, stream,
                        (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qblk = (a.Sq + kQRows - 1) / kQRows;
-    hipLaunchKernelGGL((bwd_dq_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)), dim3(kThreadsB), 0,
+    launch_kernel<false>((bwd_dq_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)), dim3(kThreadsB), 0,
                        stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
                        scale_log2, a.scale, n_qblk);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kblk = (a.Sk + kKRows - 1) / kKRows;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hkv * n_kblk)), dim3(kThreadsB), 0,
+    launch_kernel((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hkv * n_kblk)), dim3(kThreadsB), 0,
                        stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv,
                        a.Sq, a.Sk, scale_log2, a.scale);

@@ -602,18 +602,18 @@ hipError_t launch_g(const DecodeArgs& a, char* ws, const Layout& L, hipStream_t 
     const int inline_sched = a.nseq <= kInlineSeqs ? 1 : 0;
     hipError_t e;
     if (!inline_sched) {
-        hipLaunchKernelGGL(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a.seqlens, a.nseq, a.Hkv,
+        launch_kernel<false>(decode_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a.seqlens, a.nseq, a.Hkv,
                            a.max_blocks, max_waves, hdr, prefix, wtab);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((decode_partial_kernel<G>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+    launch_kernel<false>((decode_partial_kernel<G>), dim3((unsigned)wgs), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.kcache, (const uint16_t*)a.vcache, a.block_table,
                        a.seqlens, hdr, wtab, (uint16_t*)a.o, a.lse, wo, wl, prefix, inline_sched, max_waves,
                        a.nseq, a.Hq, a.Hkv, a.max_blocks, a.num_blocks, a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((decode_combine_kernel<G>), dim3(a.Hkv, a.nseq), dim3(G * kD), 0, stream, wo, wl, a.seqlens,
+    launch_kernel((decode_combine_kernel<G>), dim3(a.Hkv, a.nseq), dim3(G * kD), 0, stream, wo, wl, a.seqlens,
                        hdr, prefix, (uint16_t*)a.o, a.lse, a.Hq, a.Hkv, a.max_blocks);
     return hipGetLastError();
 }

@@ -22,9 +22,28 @@ bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
     return true;
 }
 
+// Clears the timing events of fa_time_next_call when an entry point returns,
+// whether or not it launched anything.
+struct TimingScope {
+    ~TimingScope() { fa::call_timing() = fa::CallTiming{}; }
+};
+
 }  // namespace
 
+namespace fa {
+CallTiming& call_timing() {
+    static thread_local CallTiming t;
+    return t;
+}
+}  // namespace fa
+
 extern "C" {
+
+int fa_time_next_call(void* start_event, void* stop_event) {
+    if ((start_event == nullptr) != (stop_event == nullptr)) return FA_ERR_INVALID_ARG;
+    fa::call_timing() = fa::CallTiming{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
+    return FA_OK;
+}
 
 const char* fa_status_string(int status) {
     switch (status) {
@@ -39,6 +58,7 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Sq, int Sk, int d, int causal, float scale, int dtype, void* stream) {
+    TimingScope timing_scope;
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
@@ -72,6 +92,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Sq) {
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream) {
+    TimingScope timing_scope;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
@@ -104,6 +125,7 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
               const int32_t* seqlens, void* o, float* lse, int nseq, int Hq, int Hkv, int d, int block_size,
               int max_blocks_per_seq, int num_blocks, float scale, void* workspace, size_t workspace_bytes,
               void* stream) {
+    TimingScope timing_scope;
     if (!q || !kcache || !vcache || !block_table || !seqlens || !o) return FA_ERR_INVALID_ARG;
     if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_blocks < 1)
         return FA_ERR_INVALID_ARG;

@@ -2,10 +2,34 @@
 // Arguments reaching these functions have already been validated.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fa {
+
+// Events that the next API call on this thread records at its kernel
+// boundaries (set by fa_time_next_call; every entry point clears them when it
+// returns).
+struct CallTiming {
+    hipEvent_t start = nullptr;
+    hipEvent_t stop = nullptr;
+};
+CallTiming& call_timing();
+
+// Every kernel of the library is launched through here.  With timing events
+// set, the first launch of a call records `start` when its kernel begins and
+// the launch marked LAST records `stop` when its kernel ends, so the two
+// events span exactly the call's kernels.  Launch errors are read with
+// hipGetLastError, as after hipLaunchKernelGGL.
+template <bool LAST = true, typename... Params, typename... Args>
+inline void launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t stream,
+                          Args... args) {
+    CallTiming& t = call_timing();
+    hipEvent_t start = t.start;
+    t.start = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, start, LAST ? t.stop : nullptr, 0u, args...);
+}
 
 struct FwdArgs {
     const void* q;

@@ -441,7 +441,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     // Two workgroups fit on a CU; if the whole grid is resident at once, pair
     // heavy and light causal Q blocks on the same CU.
     const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)num_cus()) ? 1 : 0;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
+    launch_kernel((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                        a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, xcd_groups, mirror);
     return hipGetLastError();

@@ -140,7 +140,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int n_qblk = (a.Sq + kRowsF - 1) / kRowsF;
     const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)n_wg), dim3(64 * kWavesF), 0, stream,
+    launch_kernel((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)n_wg), dim3(64 * kWavesF), 0, stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                        a.Hq, a.Hkv, a.Sq, a.Sk, a.scale * kLog2e, n_qblk);
     return hipGetLastError();

@@ -177,6 +177,25 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               int num_blocks, float scale, void* workspace, size_t workspace_bytes,
               void* stream);
 
+/*
+ * fa_time_next_call - kernel-boundary timing of the next call on this thread.
+ *
+ * Measurement hook, not part of any attention computation.  start_event and
+ * stop_event are hipEvent_t handles (created by the caller with timing
+ * enabled; the library does not own them), both non-NULL, or both NULL to
+ * clear.  The next fa_fwd, fa_bwd or fa_decode call made on the same host
+ * thread launches its kernels with these events attached
+ * (hipExtLaunchKernel): start_event records when the call's first kernel
+ * begins executing and stop_event when its last kernel ends, so the elapsed
+ * time between them is the call's GPU time without the stream markers that a
+ * separate hipEventRecord pair adds.  That call clears the setting when it
+ * returns, whatever its status; a call that fails validation records neither
+ * event.
+ *
+ * Returns FA_OK, or FA_ERR_INVALID_ARG when exactly one handle is NULL.
+ */
+int fa_time_next_call(void* start_event, void* stop_event);
+
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
-                           "fa_status_string"]
+                           "fa_status_string", "fa_time_next_call"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -116,3 +116,16 @@ def test_bwd_workspace_size_is_one_float_per_row(lib):
     assert f(2, 16, 2048) == 2 * 16 * 2048 * 4
     assert f(1, 1, 3) == 256
     assert f(0, 16, 2048) == 0 and f(1, 0, 1) == 0 and f(1, 1, 0) == 0
+
+
+def test_time_next_call_takes_two_events_or_none(lib):
+    """The timing hook is host state only: it checks that both handles or
+    neither are given; an entry point that fails validation clears it."""
+    V = ctypes.c_void_p
+    assert lib.fa_time_next_call(V(0x1000), None) == -1
+    assert lib.fa_time_next_call(None, V(0x1000)) == -1
+    assert lib.fa_time_next_call(None, None) == 0
+    # set, then consumed by a call that is rejected before any launch
+    assert lib.fa_time_next_call(V(0x1000), V(0x2000)) == 0
+    assert _bwd(lib, B=0) == -1
+    assert lib.fa_time_next_call(None, None) == 0
