@@ -176,6 +176,20 @@ def make_prefill(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int, *, causal:
                        meta=dict(outliers=n_out))
 
 
+def make_rotation(d: int, *, seed: int = 0) -> np.ndarray:
+    """A seeded random orthogonal d x d matrix (Haar distributed: QR of a
+    Gaussian matrix with the signs of R's diagonal moved into Q), rounded to
+    bf16 values (fp32 array).  The incoherent processing of the FP8 forward
+    multiplies Q and K by it; it is an input like any other random draw."""
+    (rr,) = _streams(seed + 0x51ED, 1)
+    g = rr.standard_normal((d, d))
+    qm, r = np.linalg.qr(g)
+    qm = qm * np.sign(np.diag(r))[None, :]
+    out = qm.astype(np.float32)
+    _round_bf16_inplace(out)
+    return out
+
+
 # --- paged decode ----------------------------------------------------------
 
 def make_grad_out(shape, *, seed: int = 0, dtype: str = "bf16") -> np.ndarray:

@@ -20,6 +20,14 @@ Everything is written from these pages:
 * "FlashAttention scaling, multi-GPU training and weight quantization"
   (itimpress.au), section 1 (rescaling postponed to the end of the inner loop).
 
+The FP8 forward's reference lives in ``oracle.fp8``: the E4M3 encoding, the
+power-of-two block scales and the rotation of Q and K ("FlashAttention
+scaling, multi-GPU training and weight quantization", section 1, FP8 support:
+block quantization and incoherent processing), and the exact attention of the
+dequantized tensors.  It is pinned by ``tests/test_oracle_fp8_pins.py``
+(format landmarks, brute-force rounding, exhaustive scale search, lossless
+round trips, rotation invariance, planted mistakes).
+
 Parity status: every public function is pinned by ``tests/test_oracle_pins.py``
 against closed forms, a hand-derived worked example, library routines and
 brute force; ``sdpa_backward`` against central finite differences, fp64 torch
@@ -39,3 +47,4 @@ from .attention import (  # noqa: F401
     merge_partials,
     sdpa_backward,
 )
+from . import fp8  # noqa: F401,E402

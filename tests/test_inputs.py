@@ -91,3 +91,13 @@ def test_decode_subset_keeps_the_logical_sequence():
         mine = sub.kcache[sub.block_table[i, :p]]
         np.testing.assert_array_equal(full, mine)
         assert sub.seqlens[i] == n
+
+
+def test_rotation_is_seeded_orthogonal_and_bf16_exact():
+    R = I.make_rotation(128, seed=3)
+    assert R.dtype == np.float32 and R.shape == (128, 128)
+    np.testing.assert_array_equal(R, I.make_rotation(128, seed=3))
+    assert not np.array_equal(R, I.make_rotation(128, seed=4))
+    np.testing.assert_array_equal(R, I.round_to_bf16(R))
+    # orthogonal up to the bf16 rounding of its entries (relative 2^-9)
+    assert np.abs(R.astype(np.float64) @ R.T - np.eye(128)).max() < 8e-3
