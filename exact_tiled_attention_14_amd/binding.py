@@ -51,6 +51,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_quantize_fp8_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_quantize_fp8_bytes.restype = sz
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.fa_quantize_fp8.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_time_next_call.argtypes = [vp, vp]
     lib.fa_time_next_call.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -192,6 +198,79 @@ def fa_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None
                     int(bool(causal)), float(scale), code, _stream(q.device))
     if st != FA_OK:
         raise FAError("fa_fwd", st)
+    return out, lse
+
+
+FA_FP8_ROWS, FA_FP8_VBLOCKS = 0, 1
+
+
+def fa_quantize_fp8(x, block_rows: int, layout: int = FA_FP8_ROWS, rot=None):
+    """FP8 (E4M3) block quantization of a bf16 [B,H,S,d] tensor.
+
+    ``layout`` FA_FP8_ROWS gives codes [B,H,S,d]; FA_FP8_VBLOCKS (for V,
+    block_rows 64, no rotation) gives [B,H,ceil(S/64),d,64], each 64-key block
+    d-major with the key order include/fa.h states.  ``rot`` is a bf16 [d,d]
+    matrix the rows are multiplied by first.  Returns ``(codes, scales)``,
+    scales [B,H,ceil(S/block_rows)] uint8 E8M0 bytes.
+    """
+    lib = load()
+    _check(x, "x", torch.bfloat16, 4)
+    B, H, S, d = x.shape
+    if rot is not None:
+        _check(rot, "rot", torch.bfloat16, 2, x.device)
+        if tuple(rot.shape) != (d, d):
+            raise ValueError("rot must be [d, d]")
+    nbytes = int(lib.fa_quantize_fp8_bytes(B, H, S, d, int(layout)))
+    if nbytes == 0:
+        raise FAError("fa_quantize_fp8_bytes", FA_ERR_UNSUPPORTED)
+    nblk = -(-S // block_rows)
+    if layout == FA_FP8_VBLOCKS:
+        codes = torch.empty((B, H, -(-S // 64), d, 64), dtype=torch.uint8, device=x.device)
+    else:
+        codes = torch.empty((B, H, S, d), dtype=torch.uint8, device=x.device)
+    assert codes.numel() == nbytes
+    scales = torch.empty((B, H, nblk), dtype=torch.uint8, device=x.device)
+    st = lib.fa_quantize_fp8(_ptr(x), _ptr(rot), _ptr(codes), _ptr(scales), B, H, S, d, int(block_rows),
+                             int(layout), _stream(x.device))
+    if st != FA_OK:
+        raise FAError("fa_quantize_fp8", st)
+    return codes, scales
+
+
+def fa_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, scale: float | None = None, out=None,
+               lse=None):
+    """Attention forward on FP8 inputs from fa_quantize_fp8: q8 [B,Hq,Sq,d]
+    (128-row scale blocks), k8 [B,Hkv,Sk,d] (64-row blocks), v8 in
+    FA_FP8_VBLOCKS layout.  Returns ``(o bf16 [B,Hq,Sq,d], lse fp32 [B,Hq,Sq])``."""
+    lib = load()
+    u8 = torch.uint8
+    _check(q8, "q8", u8, 4)
+    _check(k8, "k8", u8, 4, q8.device)
+    _check(v8, "v8", u8, 5, q8.device)
+    B, Hq, Sq, d = q8.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    nk = -(-Sk // 64)
+    if tuple(k8.shape) != (B, Hkv, Sk, d) or tuple(v8.shape) != (B, Hkv, nk, d, 64):
+        raise ValueError(f"shape mismatch q8={tuple(q8.shape)} k8={tuple(k8.shape)} v8={tuple(v8.shape)}")
+    for t, n, shp in ((q_scale, "q_scale", (B, Hq, -(-Sq // 128))), (k_scale, "k_scale", (B, Hkv, nk)),
+                      (v_scale, "v_scale", (B, Hkv, nk))):
+        _check(t, n, u8, 3, q8.device)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n} must be {shp}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=q8.device)
+    else:
+        _check(out, "out", torch.bfloat16, 4, q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
+    else:
+        _check(lse, "lse", torch.float32, 3, q8.device)
+    st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                        _ptr(lse), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _stream(q8.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd_fp8", st)
     return out, lse
 
 

@@ -115,6 +115,45 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_quantize_fp8_bytes(int B, int H, int S, int d, int layout) {
+    if (B < 1 || H < 1 || S < 1 || d != 128 || !fits(B, H, S, d)) return 0;
+    if (layout == FA_FP8_ROWS) return (size_t)B * H * S * d;
+    if (layout == FA_FP8_VBLOCKS) return (size_t)B * H * ((S + 63) / 64) * 64 * d;
+    return 0;
+}
+
+int fa_quantize_fp8(const void* x, const void* rot, void* x8, uint8_t* scales, int B, int H, int S, int d,
+                    int block_rows, int layout, void* stream) {
+    TimingScope timing_scope;
+    if (!x || !x8 || !scales) return FA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || S < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (layout != FA_FP8_ROWS && layout != FA_FP8_VBLOCKS) return FA_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x8) || (rot && !aligned16(rot))) return FA_ERR_INVALID_ARG;
+    if (!fits(B, H, S, d)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if (layout == FA_FP8_ROWS && block_rows != 64 && block_rows != 128) return FA_ERR_UNSUPPORTED;
+    if (layout == FA_FP8_VBLOCKS && (block_rows != 64 || rot != nullptr)) return FA_ERR_UNSUPPORTED;
+    fa::QuantArgs a{x, rot, x8, scales, (int64_t)B * H, S, block_rows, layout};
+    return fa::launch_quant_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
+               const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
+               float scale, void* stream) {
+    TimingScope timing_scope;
+    if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk + 63, d)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * ((Sq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale};
+    return fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 size_t fa_decode_workspace_size(int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq) {
     if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1) return 0;
     if (d != 128 || block_size != 16) return 0;

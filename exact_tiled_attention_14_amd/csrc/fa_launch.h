@@ -70,6 +70,33 @@ struct DecodeArgs {
     float scale;
 };
 
+// FP8 block quantization of a [BH, S, 128] bf16 tensor.
+struct QuantArgs {
+    const void* x;
+    const void* rot;       // [128, 128] bf16 or nullptr
+    void* x8;
+    uint8_t* scales;       // [BH, ceil(S / block_rows)] E8M0 bytes
+    int64_t BH;
+    int S, block_rows;
+    int layout;            // 0 rows, 1 d-major 64-key V blocks
+};
+
+struct Fp8FwdArgs {
+    const void* q8;
+    const void* k8;
+    const void* v8;        // d-major 64-key blocks
+    const uint8_t* q_scale;
+    const uint8_t* k_scale;
+    const uint8_t* v_scale;
+    void* o;
+    float* lse;
+    int B, Hq, Hkv, Sq, Sk;
+    int causal;
+    float scale;
+};
+
+hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);

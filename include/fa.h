@@ -58,6 +58,11 @@ typedef enum {
     FA_F32 = 1                 /* q, k, v, o are fp32 */
 } fa_dtype;
 
+typedef enum {
+    FA_FP8_ROWS = 0,           /* row-major [B, H, S, d] codes, one scale per block_rows rows */
+    FA_FP8_VBLOCKS = 1         /* V: per 64-key block, d-major rows of 64 codes (see fa_quantize_fp8) */
+} fa_fp8_layout;
+
 /*
  * fa_fwd - prefill / full-sequence attention forward.
  *
@@ -176,6 +181,74 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
               int num_blocks, float scale, void* workspace, size_t workspace_bytes,
               void* stream);
+
+/*
+ * fa_quantize_fp8_bytes - bytes of the E4M3 codes fa_quantize_fp8 writes
+ * for a [B, H, S, d] input in `layout` (FA_FP8_VBLOCKS pads S up to a
+ * multiple of 64); 0 for invalid or unsupported arguments (d != 128).
+ */
+size_t fa_quantize_fp8_bytes(int B, int H, int S, int d, int layout);
+
+/*
+ * fa_quantize_fp8 - block quantization to FP8 for fa_fwd_fp8.
+ *
+ * Passage: "FlashAttention scaling, multi-GPU training and weight
+ * quantization", section 1 (FP8 support): tiles scaled independently (block
+ * quantization); Q and K multiplied by a random orthogonal matrix before
+ * quantization (incoherent processing), which leaves Q K^T unchanged.
+ *
+ *   x      [B, H, S, d] bf16, device, read-only.
+ *   rot    [d, d] bf16 orthogonal matrix or NULL: with rot each row is
+ *          replaced by x_row * rot before quantization (pass the same rot for
+ *          Q and K; never for V).  The product runs in fp32 on bf16 values.
+ *   x8     output codes, fa_quantize_fp8_bytes(...) bytes.  Encoding: OCP
+ *          E4M3 (bias 7, no infinities, largest finite 448), round to nearest
+ *          even.  FA_FP8_ROWS: row-major [B, H, S, d].  FA_FP8_VBLOCKS: for
+ *          each (b, h) and 64-key block j, 64 * d bytes: row c (c = 0..d-1)
+ *          holds 64 codes of head-dim index c; its byte p = 32 h + t holds
+ *          key 64 j + 32 (t / 16) + 8 ((t % 16) / 4) + 4 h + t % 4 (h = 0, 1;
+ *          t = 0..31), the order in which the attention kernel holds P.
+ *          Keys past S hold code 0.
+ *   scales [B, H, ceil(S / block_rows)] bytes, output: the E8M0 byte e + 127
+ *          of each block's scale 2^e, e the smallest integer with
+ *          amax <= 448 * 2^e (amax = largest |value| of the block after the
+ *          rotation; 0 gives e = 0), clamped to [-127, 127].  A value's code
+ *          is round(value / 2^e).
+ *   block_rows  FA_FP8_ROWS: 128 for Q, 64 for K (what fa_fwd_fp8 reads);
+ *          FA_FP8_VBLOCKS: 64, with rot NULL.
+ *
+ * x, x8 and rot must be 16-byte aligned.  d must be 128, else
+ * FA_ERR_UNSUPPORTED.  Runs on `stream`; allocates nothing.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_quantize_fp8(const void* x, const void* rot, void* x8, uint8_t* scales, int B, int H, int S, int d,
+                    int block_rows, int layout, void* stream);
+
+/*
+ * fa_fwd_fp8 - attention forward on FP8 inputs (FP8 matrix-core products).
+ *
+ * Passage: "FlashAttention scaling, multi-GPU training and weight
+ * quantization", section 1 (FP8 support on FP8 matrix units, block
+ * quantization); the algorithm is that of fa_fwd.
+ *
+ *   q8  [B, Hq, Sq, 128] codes, FA_FP8_ROWS, q_scale per 128-row block
+ *       ([B, Hq, ceil(Sq / 128)] E8M0 bytes).
+ *   k8  [B, Hkv, Sk, 128] codes, FA_FP8_ROWS, k_scale per 64-row block.
+ *   v8  FA_FP8_VBLOCKS codes of V, v_scale per 64-key block.
+ *   o   [B, Hq, Sq, 128] bf16 output; lse [B, Hq, Sq] fp32 natural-log
+ *       log-sum-exp of the scaled scores, or NULL.
+ *
+ * Computes attention of the dequantized inputs (code value times block
+ * scale); the scores are exact products of the dequantized values summed in
+ * fp32.  P is rounded to E4M3 (ties to even) before the product with V, the
+ * running sum adds the unrounded probabilities, and O is rounded to bf16
+ * once.  Causal masking is bottom-right aligned as in fa_fwd.  Pointers
+ * 16-byte aligned (lse 4-byte); d must be 128, else FA_ERR_UNSUPPORTED.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
+               const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+               int causal, float scale, void* stream);
 
 /*
  * fa_time_next_call - kernel-boundary timing of the next call on this thread.

@@ -29,7 +29,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
-                           "fa_status_string", "fa_time_next_call"]
+                           "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string",
+                           "fa_time_next_call"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -129,3 +130,40 @@ def test_time_next_call_takes_two_events_or_none(lib):
     assert lib.fa_time_next_call(V(0x1000), V(0x2000)) == 0
     assert _bwd(lib, B=0) == -1
     assert lib.fa_time_next_call(None, None) == 0
+
+
+def _quant(lib, x=16, rot=0, x8=32, sc=48, B=1, H=2, S=100, d=128, rows=64, layout=0):
+    P = ctypes.c_void_p
+    return lib.fa_quantize_fp8(P(x), P(rot) if rot else None, P(x8), P(sc), B, H, S, d, rows, layout, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=0), -1), (dict(x8=0), -1), (dict(sc=0), -1), (dict(S=0), -1), (dict(layout=2), -1),
+    (dict(x=24), -1), (dict(x8=40), -1), (dict(rot=72), -1),
+    (dict(d=64), -2), (dict(rows=32), -2), (dict(layout=1, rows=128), -2), (dict(layout=1, rot=256), -2),
+])
+def test_quantize_fp8_rejects_before_launch(lib, kw, status):
+    assert _quant(lib, **kw) == status
+
+
+def _fwd8(lib, q=16, k=32, v=48, qs=1, ks=2, vs=3, o=64, lse=0, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=128, causal=1,
+          scale=0.1):
+    P = ctypes.c_void_p
+    return lib.fa_fwd_fp8(P(q), P(k), P(v), P(qs), P(ks), P(vs), P(o), P(lse) if lse else None, B, Hq, Hkv, Sq, Sk,
+                          d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(vs=0), -1), (dict(o=0), -1), (dict(B=0), -1), (dict(Hq=3, Hkv=2), -1),
+    (dict(causal=2), -1), (dict(scale=-1.0), -1), (dict(v=40), -1), (dict(lse=98), -1),
+    (dict(d=64), -2),
+])
+def test_fwd_fp8_rejects_before_launch(lib, kw, status):
+    assert _fwd8(lib, **kw) == status
+
+
+def test_quantize_fp8_bytes(lib):
+    f = lib.fa_quantize_fp8_bytes
+    assert f(2, 16, 2048, 128, 0) == 2 * 16 * 2048 * 128
+    assert f(1, 2, 100, 128, 1) == 2 * 2 * 64 * 128      # V blocks pad 100 keys to 128
+    assert f(1, 2, 100, 64, 0) == 0 and f(1, 2, 100, 128, 5) == 0 and f(0, 1, 1, 128, 0) == 0

@@ -1,0 +1,300 @@
+"""GPU parity of the FP8 path (fa_quantize_fp8, fa_fwd_fp8) against the fp64
+oracle (oracle/fp8.py), which quantizes the same inputs itself.
+
+Quantization: codes and scales are integer results decided in fp32 on both
+sides (the oracle's rounding is exact on bf16 inputs), so without rotation
+they must match bit for bit.  With the rotation inside the quantizer the GPU
+sums the 128 products of a row in fp32 on the matrix cores and the oracle in
+fp64, so an element whose rotated value lies within the fp32 summation bound
+(gamma_128 sum |x_k R_kn|, gamma_128 = 128 u / (1 - 128 u), u = 2^-24) of an
+E4M3 rounding midpoint may take either neighbouring code: the test accepts a
+differing code only at such elements (found from the oracle's values alone)
+and only as the other neighbour.  The attention parity tests on small shapes
+therefore rotate Q and K on the host (then round to bf16) and quantize
+without rotation, so both sides hold identical codes; the full-size test runs
+the rotation inside the quantizer, and there lse is allowed the largest score
+move the ambiguous elements can cause (ambiguous_slack: one code step times
+scale times max|other operand|, summed over one row's ambiguous elements).
+
+Attention: the GPU computes the scores of the dequantized inputs exactly
+(E4M3 products are exact in fp32) but rounds P to E4M3 before the product with
+V.  With p rounded to nearest, |p~ - p| <= 2^-4 p for p in the normal range
+(relative RMS about 2^-4 / sqrt(3) * 0.74 = 0.027 for values spread over a
+binade), and O = sum p~ v / sum p (the running sum adds unrounded p), so
+|dO| <= 2^-4 max|v| and, for values of either sign, the relative RMS error
+of O is about 0.027.  The tests use rel-RMS <= 4e-2 and
+max |dO| <= 2^-4 max|v| + 2^-8 max|O| (the second term for the bf16 output
+and the subnormal part of P); lse does not depend on the rounded P and keeps
+the 1e-3 bound.
+"""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from oracle import fp8 as F  # noqa: E402
+from exact_tiled_attention_14_amd import inputs as I  # noqa: E402
+
+DEV = "cuda:0"
+REL_RMS, LSE_TOL = 4e-2, 1e-3
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_tiled_attention_14_amd import binding
+    binding.load()
+    return binding
+
+
+def _bf(x):
+    bits = I.bf16_bits(np.asarray(x, np.float32))
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def _np(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def unblock_v(codes):
+    """[B,H,nblk,d,64] d-major blocks -> [B,H,nblk*64,d] in key order."""
+    c = codes.cpu().numpy()
+    Bn, H, nb, d, _ = c.shape
+    p = np.arange(64)
+    h, t = p // 32, p % 32
+    key = 32 * (t // 16) + 8 * ((t % 16) // 4) + 4 * h + t % 4
+    out = np.zeros((Bn, H, nb, 64, d), np.uint8)
+    out[:, :, :, key, :] = np.transpose(c, (0, 1, 2, 4, 3))
+    return out.reshape(Bn, H, nb * 64, d)
+
+
+def ambiguous_slack(x, rot, rows, other_max, scale):
+    """Largest move of any score that the codes of rotated elements near an
+    E4M3 rounding midpoint can cause (0 without rotation).  A score pairs one
+    row of this operand with one row of the other, so the bound is, over rows,
+    the largest sum of scale * (one code step) * max|other operand| over the
+    row's ambiguous elements.  Uses only the oracle's values.  Asserts that no
+    block scale itself is ambiguous."""
+    if rot is None:
+        return 0.0
+    x = np.asarray(x, np.float64)
+    R = np.asarray(rot, np.float64)
+    u = 2.0 ** -24
+    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R))   # bound on an fp32 sum of the 128 products
+    _, ex = F.quantize_blocks(x, rows, rot=R)
+    S = x.shape[-2]
+    s = np.ldexp(1.0, ex)[..., np.arange(S) // rows][..., None]
+    t, terr = np.abs(x @ R) / s, err / s
+    # the scale of every block is decided with room to spare: its largest
+    # value stays inside (224, 448] whichever way the fp32 sums round
+    starts = np.arange(0, S, rows)
+    hi_max = np.maximum.reduceat((t + terr).max(-1), starts, axis=-1)
+    lo_max = np.maximum.reduceat((t - terr).max(-1), starts, axis=-1)
+    assert (hi_max <= 448).all() and (lo_max > 224).all(), "a block scale is ambiguous"
+    grid = F.e4m3_values()
+    pos = np.unique(np.abs(grid[np.isfinite(grid)]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    k = np.clip(np.searchsorted(mids, t), 1, len(mids) - 1)
+    near = np.minimum(np.abs(t - mids[k - 1]), np.abs(t - mids[k])) <= terr
+    if not near.any():
+        return 0.0
+    j = np.clip(np.searchsorted(pos, t), 1, len(pos) - 1)
+    step = np.where(near, (pos[j] - pos[j - 1]) * s, 0.0)
+    return float(scale * step.sum(-1).max() * other_max)
+
+
+def check_fp8_o(got, want, v_deq, label, slack=0.0, max_abs=True):
+    assert np.isfinite(got).all(), f"{label}: non-finite output"
+    err = got - want
+    rr = float(np.sqrt((err ** 2).sum() / max((want ** 2).sum(), 1e-300)))
+    ma = float(np.abs(err).max())
+    bound = 2.0 ** -4 * float(np.abs(v_deq).max()) + 2.0 ** -8 * float(np.abs(want).max()) \
+        + 2.0 * float(np.abs(v_deq).max()) * np.expm1(2 * slack)
+    print(f"{label}: rel_rms={rr:.3e} max_abs={ma:.3e} (bound {bound:.3e})", flush=True)
+    assert rr <= REL_RMS, f"{label}: rel_rms {rr:.3e}"
+    if max_abs:
+        assert ma <= bound, f"{label}: max_abs {ma:.3e} > {bound:.3e}"
+
+
+def check_lse(got, want, label, slack=0.0):
+    ninf = np.isneginf(want)
+    assert (np.isneginf(got) == ninf).all(), f"{label}: -inf pattern differs"
+    d = float(np.abs(got[~ninf] - want[~ninf]).max()) if (~ninf).any() else 0.0
+    if slack:
+        print(f"{label}: lse {d:.3e}, allowed {LSE_TOL + slack:.3e} (ambiguous rotated codes)", flush=True)
+    assert d <= LSE_TOL + slack, f"{label}: lse {d:.3e}"
+
+
+# --- quantization ---------------------------------------------------------------
+
+@pytest.mark.parametrize("S,rows", [(200, 64), (200, 128), (64, 64), (1, 128), (383, 128)])
+def test_quantize_rows_bit_exact(B, S, rows):
+    c = I.make_prefill(1, 3, 3, S, S, 128, causal=True, seed=100 + S)
+    x = c.q * np.float32(np.linspace(0.01, 40, 3))[None, :, None, None]     # several scale exponents
+    x = I.round_to_bf16(x.astype(np.float32))
+    codes, sc = B.fa_quantize_fp8(_bf(x), rows)
+    want_c, want_e = F.quantize_blocks(x, rows)
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+    assert np.array_equal(sc.cpu().numpy().astype(np.int64) - 127, want_e)
+
+
+@pytest.mark.parametrize("S", [64, 200, 1])
+def test_quantize_v_blocks_bit_exact(B, S):
+    c = I.make_prefill(2, 2, 2, S, S, 128, causal=True, seed=200 + S)
+    codes, sc = B.fa_quantize_fp8(_bf(c.v), 64, layout=B.FA_FP8_VBLOCKS)
+    got = unblock_v(codes)
+    want_c, want_e = F.quantize_blocks(c.v, 64)
+    assert np.array_equal(got[:, :, :S], want_c)
+    assert (got[:, :, S:] == 0).all()
+    assert np.array_equal(sc.cpu().numpy().astype(np.int64) - 127, want_e)
+
+
+def ambiguous_mask(x, rot, rows):
+    """Elements whose rotated value lies within the fp32 summation bound of
+    an E4M3 rounding midpoint (either neighbouring code is then valid)."""
+    x = np.asarray(x, np.float64)
+    R = np.asarray(rot, np.float64)
+    u = 2.0 ** -24
+    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R))
+    _, ex = F.quantize_blocks(x, rows, rot=R)
+    S = x.shape[-2]
+    s = np.ldexp(1.0, ex)[..., np.arange(S) // rows][..., None]
+    t, terr = np.abs(x @ R) / s, err / s
+    grid = F.e4m3_values()
+    pos = np.unique(np.abs(grid[np.isfinite(grid)]))
+    mids = (pos[:-1] + pos[1:]) / 2
+    k = np.clip(np.searchsorted(mids, t), 1, len(mids) - 1)
+    return np.minimum(np.abs(t - mids[k - 1]), np.abs(t - mids[k])) <= terr
+
+
+def test_quantize_rotated(B):
+    """Rotation inside the quantizer: scales equal the oracle's, and codes
+    equal them except at elements the oracle itself finds ambiguous, where the
+    GPU's code is the other neighbour of the rotated value."""
+    c = I.make_prefill(1, 4, 4, 1000, 1000, 128, causal=True, seed=300, outlier_frac=0.001)
+    R = I.make_rotation(128, seed=300)
+    codes, sc = B.fa_quantize_fp8(_bf(c.k), 64, rot=_bf(R))
+    want_c, want_e = F.quantize_blocks(c.k, 64, rot=R)
+    assert np.array_equal(sc.cpu().numpy().astype(np.int64) - 127, want_e)
+    got = codes.cpu().numpy()
+    diff = got != want_c
+    amb = ambiguous_mask(c.k, R, 64)
+    print(f"rotated codes differing: {int(diff.sum())} of {diff.size} ({int(amb.sum())} ambiguous)", flush=True)
+    assert not (diff & ~amb).any()
+    # the other neighbour: the two values are adjacent on the E4M3 grid
+    a, b_ = F.e4m3_decode(got[diff]), F.e4m3_decode(want_c[diff])
+    grid = F.e4m3_values()
+    fin = grid[np.isfinite(grid)]
+    assert all(((fin > min(x, y)) & (fin < max(x, y))).sum() == 0 for x, y in zip(a, b_))
+    assert (np.sign(a) * np.sign(b_) >= 0).all()
+
+
+# --- attention -----------------------------------------------------------------------
+
+def run_fp8(Bm, c, rot):
+    R = _bf(rot) if rot is not None else None
+    q8, qs = Bm.fa_quantize_fp8(_bf(c.q), 128, rot=R)
+    k8, ks = Bm.fa_quantize_fp8(_bf(c.k), 64, rot=R)
+    v8, vs = Bm.fa_quantize_fp8(_bf(c.v), 64, layout=Bm.FA_FP8_VBLOCKS)
+    o, lse = Bm.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, c.causal, c.scale)
+    torch.cuda.synchronize()
+    return _np(o), lse.cpu().numpy().astype(np.float64)
+
+
+def oracle_fp8(c, rot, heads=None):
+    """Oracle output, lse, dequantized V and the score slack of ambiguous
+    rotated codes (0 without rotation)."""
+    q, k, v = c.q, c.k, c.v
+    if heads is not None:
+        (b, h), g = heads, c.q.shape[1] // c.k.shape[1]
+        q, k, v = q[b:b + 1, h:h + 1], k[b:b + 1, h // g:h // g + 1], v[b:b + 1, h // g:h // g + 1]
+    q8, qe = F.quantize_blocks(q, 128, rot=rot)
+    k8, ke = F.quantize_blocks(k, 64, rot=rot)
+    v8, ve = F.quantize_blocks(v, 64)
+    O, L = F.sdpa_fp8(q8, qe, k8, ke, v8, ve, c.causal, c.scale)
+    slack = 0.0
+    if rot is not None:
+        qmax = float(np.abs(F.dequantize_blocks(q8, qe, 128)).max())
+        kmax = float(np.abs(F.dequantize_blocks(k8, ke, 64)).max())
+        slack = ambiguous_slack(k, rot, 64, qmax, c.scale) + ambiguous_slack(q, rot, 128, kmax, c.scale)
+    return O, L, F.dequantize_blocks(v8, ve, 64), slack
+
+
+SHAPES = [
+    (1, 2, 2, 150, 150, True),
+    (2, 4, 2, 200, 333, True),
+    (1, 4, 1, 333, 200, True),     # rows with no visible key
+    (1, 2, 2, 100, 260, False),
+    (1, 2, 2, 1, 77, True),
+    (1, 8, 2, 640, 640, True),
+]
+
+
+@pytest.mark.parametrize("rotate", [False, True], ids=["plain", "prerotated"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}{}".format(*s[:5], "c" if s[5] else "n"))
+def test_fp8_forward_small_shapes(B, shape, rotate):
+    """The kernel against the oracle on identical codes.  `prerotated`: Q
+    and K are rotated on the host (and rounded to bf16) before both sides
+    quantize them, so the incoherent-processing regime is covered with codes
+    that both sides decide exactly alike."""
+    Bn, Hq, Hkv, Sq, Sk, causal = shape
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=causal, seed=400 + Sq + Sk)
+    if rotate:
+        R = I.make_rotation(128, seed=400 + Sq).astype(np.float64)
+        c.q = I.round_to_bf16((c.q @ R).astype(np.float32))
+        c.k = I.round_to_bf16((c.k @ R).astype(np.float32))
+    o, lse = run_fp8(B, c, None)
+    O, L, vd, _ = oracle_fp8(c, None)
+    check_fp8_o(o, O, vd, f"fp8 {shape} prerotated={rotate}")
+    check_lse(lse, L, f"fp8 {shape}")
+
+
+def test_fp8_forward_headline_shape(B):
+    """B2 H16 S2048 causal, rotation inside the quantizer (the benchmark's
+    path); four heads compared in full.  A rotated element within the fp32
+    summation bound of an E4M3 midpoint may take either code, so lse is
+    allowed the score slack of such elements (ambiguous_slack) and O is held
+    to the relative RMS bound, which a few one-step code differences cannot
+    move."""
+    c = I.workload("causal_mha_b2_h16_s2048_d128")
+    rot = I.make_rotation(128, seed=2)
+    o, lse = run_fp8(B, c, rot)
+    for b, h in ((0, 0), (0, 15), (1, 7), (1, 9)):
+        O, L, vd, slack = oracle_fp8(c, rot, heads=(b, h))
+        check_fp8_o(o[b:b + 1, h:h + 1], O, vd, f"fp8 headline b{b} h{h}", slack, max_abs=False)
+        check_lse(lse[b:b + 1, h:h + 1], L, f"fp8 headline b{b} h{h}", slack)
+
+
+def test_rotation_reduces_error_with_key_outliers(B):
+    """Incoherent processing: with 0.1 % of K entries scaled by 20, the FP8
+    output is closer to the exact attention of the unquantized inputs when
+    Q and K are rotated first."""
+    c = I.make_prefill(1, 8, 2, 2048, 2048, 128, causal=True, seed=500, outlier_frac=0.001, outlier_scale=20.0)
+    O_exact, _ = oracle.sdpa(c.q[:, :2], c.k[:, :1], c.v[:, :1], True, c.scale)
+    errs = {}
+    for rotate in (False, True):
+        rot = I.make_rotation(128, seed=500) if rotate else None
+        o, _ = run_fp8(B, c, rot)
+        e = o[:, :2] - O_exact
+        errs[rotate] = float(np.sqrt((e ** 2).sum() / (O_exact ** 2).sum()))
+    print(f"rel-RMS vs unquantized: plain {errs[False]:.3e}, rotated {errs[True]:.3e}", flush=True)
+    assert errs[True] < errs[False]
+
+
+def test_fp8_binding_errors(B):
+    x = torch.zeros((1, 2, 8, 64), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(B.FAError):
+        B.fa_quantize_fp8(x, 64)
+    x = torch.zeros((1, 2, 8, 128), dtype=torch.bfloat16, device=DEV)
+    r = torch.zeros((128, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(B.FAError) as e:
+        B.fa_quantize_fp8(x, 64, layout=B.FA_FP8_VBLOCKS, rot=r)
+    assert e.value.status == B.FA_ERR_UNSUPPORTED
+    with pytest.raises(B.FAError) as e:
+        B.fa_quantize_fp8(x, 32)
+    assert e.value.status == B.FA_ERR_UNSUPPORTED
