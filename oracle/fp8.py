@@ -20,8 +20,9 @@ taken here are:
   round(x / s); the value a code stands for is its E4M3 value times s.  A
   power of two keeps x / s and the dequantisation exact.
 * Block: ``block_rows`` consecutive rows of one (batch, head) slice.
-* Rotation: x -> x R with one d x d orthogonal matrix R for Q and K; V is not
-  rotated (rotating it would change O).
+* Rotation: every row vector x -> R x (the rows times R^T) with one d x d
+  orthogonal matrix R for Q and K, so that (q R^T)(k R^T)^T = q k^T and the
+  scores are unchanged; V is not rotated (that would change O).
 
 Functions here quantize and dequantize from these definitions and compute the
 attention of the dequantized tensors with :func:`oracle.sdpa`.
@@ -99,23 +100,25 @@ def e4m3_encode(x) -> np.ndarray:
 def block_scale_exponent(amax) -> np.ndarray:
     """e with 2^e the block scale: the smallest integer such that
     amax <= 448 * 2^e.  Integer logic on amax = M 2^E (M in [1, 2)):
-    448 = 1.75 * 2^8, so e = E - 8, plus one when M > 1.75; e = 0 for 0."""
+    448 = 1.75 * 2^8, so e = E - 8, plus one when M > 1.75; e = 0 for 0.
+    The scale is stored as an E8M0 byte, so e is clamped to [-127, 127]."""
     a = np.asarray(amax, dtype=np.float64)
     f, e2 = np.frexp(a)                     # a = f 2^e2, f in [0.5, 1): M = 2f, E = e2 - 1
-    e = (e2 - 1) - 8 + (2.0 * f > 1.75)
+    e = np.clip((e2 - 1) - 8 + (2.0 * f > 1.75), -127, 127)
     return np.where(a > 0, e, 0).astype(np.int64)
 
 
 def quantize_blocks(x, block_rows: int, rot=None):
     """Quantize [..., S, d] per block of ``block_rows`` rows.
 
-    ``rot`` (d x d, optional) multiplies every row first (x -> x rot).
+    ``rot`` (d x d, optional) rotates every row first (x -> rot x, i.e. the
+    rows times rot^T).
     Returns (codes uint8 [..., S, d], scale exponents int64 [..., nblk]);
     the value of element (r, c) is e4m3(codes) * 2^exp[r // block_rows].
     """
     x = np.asarray(x, dtype=np.float64)
     if rot is not None:
-        x = x @ np.asarray(rot, dtype=np.float64)
+        x = x @ np.asarray(rot, dtype=np.float64).T
     S = x.shape[-2]
     nblk = -(-S // block_rows)
     pad = nblk * block_rows - S

@@ -100,7 +100,7 @@ def _scale_exp_brute(a):
     e = -160
     while a > 448.0 * 2.0 ** e:
         e += 1
-    return e
+    return max(e, -127)          # E8M0 range
 
 
 def test_block_scale_rule_by_search():
@@ -111,9 +111,10 @@ def test_block_scale_rule_by_search():
     a = np.concatenate([a, special])
     e = F.block_scale_exponent(a)
     assert [int(x) for x in e] == [_scale_exp_brute(float(x)) for x in a]
-    pos = a > 0
+    pos = a > 448.0 * 2.0 ** -128            # below that the E8M0 floor 2^-127 applies
     r = a[pos] / np.ldexp(1.0, e[pos])
     assert np.all(r <= 448) and np.all(r > 224)
+    assert e[a == 2.0 ** -130][0] == -127
 
 
 def test_quantize_blocks_invariants():
@@ -177,9 +178,9 @@ def test_rotation_leaves_scores_unchanged():
     np.testing.assert_allclose(L1, L2, atol=1e-10)
     kr = k[0, 0, 5] @ R
     assert np.abs(kr).max() < 0.9 * 200.0
-    # quantize with the rotation = quantize the rotated rows
+    # quantize with the rotation = quantize the rotated rows (each row x -> R x)
     c1, e1 = F.quantize_blocks(k, 8, rot=R)
-    c2, e2 = F.quantize_blocks(k @ R, 8)
+    c2, e2 = F.quantize_blocks(k @ R.T, 8)
     assert np.array_equal(c1, c2) and np.array_equal(e1, e2)
 
 
