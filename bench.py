@@ -51,6 +51,7 @@ EXTRA = ["causal_gqa_h32kv8_s8192_d128_outliers", "causal_gqa_h32kv8_s32768_d128
 # per launch; used only while the kernel source still has the recorded hash
 PROFILE_PREFILL = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_b2_h16_s2048_d128.md")
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "decode_paged_64seq_h32kv8_d128.md")
+PROFILE_FP8 = os.path.join(ROOT, "profiles", "fwd_fp8_causal_mha_b2_h16_s2048_d128.md")
 CPU_MIN_SECONDS = 10.0
 
 
@@ -93,6 +94,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads per oracle call when timing the CPU baseline")
     args = ap.parse_args()
 
@@ -292,6 +294,62 @@ def main():
         }
         log(f"backward: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
         del g_do, b_dq, b_dk, b_dv, b_ws
+
+    # ---- FP8 forward on the headline shape: quantize (rotated Q, K; V blocks), then attend ----
+    if not args.no_fp8:
+        log("fp8: quantize + forward")
+        rot = to_dev(inputs.bf16_bits(inputs.make_rotation(shp["d"], seed=2)))
+
+        def run_fp8(evs=None):
+            names = ("quant_q", "quant_k", "quant_v", "fwd_fp8")
+            calls = (lambda: binding.fa_quantize_fp8(p_q, 128, rot=rot),
+                     lambda: binding.fa_quantize_fp8(p_k, 64, rot=rot),
+                     lambda: binding.fa_quantize_fp8(p_v, 64, layout=binding.FA_FP8_VBLOCKS))
+            outs = []
+            for n, fn in zip(names[:3], calls):
+                if evs is not None:
+                    binding.fa_time_next_call(*evs[n])
+                outs.append(fn())
+            (q8, qs), (k8, ks), (v8, vs) = outs
+            if evs is not None:
+                binding.fa_time_next_call(*evs["fwd_fp8"])
+            binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, cp.scale, out=p_o, lse=p_l)
+
+        for _ in range(2):
+            run_fp8()
+        reps = max(5, min(K, 20))
+        names = ("quant_q", "quant_k", "quant_v", "fwd_fp8")
+        evs = [{n: (binding.TimingEvent(), binding.TimingEvent()) for n in names} for _ in range(reps)]
+        torch.cuda.synchronize()
+        lead = gpu_lead(stream, 2.0 + 0.5 * reps)
+        host0 = time.perf_counter()
+        for i in range(reps):
+            flush.fill_(i & 0xFF)        # cold caches, as in the step
+            run_fp8(evs[i])
+        host_s = time.perf_counter() - host0
+        torch.cuda.synchronize()
+        st = {n: metrics.summarize([e[n][0].elapsed_ms(e[n][1]) for e in evs]) for n in names}
+        tf8 = flops_p / (st["fwd_fp8"]["mean"] * 1e-3) / 1e12
+        peak8 = metrics.MI355X_FP8_DENSE_FLOPS / 1e12
+        bh_q, bh_kv = shp["B"] * shp["Hq"], shp["B"] * shp["Hkv"]
+        qbytes = {"quant_q": metrics.fp8_quantize_bytes(bh_q, shp["Sq"], shp["d"], 128),
+                  "quant_k": metrics.fp8_quantize_bytes(bh_kv, shp["Sk"], shp["d"], 64),
+                  "quant_v": metrics.fp8_quantize_bytes(bh_kv, shp["Sk"], shp["d"], 64)}
+        result["fp8"] = {
+            "workload": PREFILL, "kernel": "fwd_fp8_kernel<causal>", "bound": "mfma",
+            "achieved": round(tf8, 1), "peak": peak8, "unit": "TFLOP/s", "frac": round(tf8 / peak8, 4),
+            "vs_bf16_kernel": round(sp["mean"] / st["fwd_fp8"]["mean"], 3),
+            "traffic": profiling.current_traffic(PROFILE_FP8),
+            "algorithmic_flops_per_launch": flops_p,
+            "launch_us": {k: round(v * 1e3, 2) for k, v in st["fwd_fp8"].items() if k != "n"},
+            "quantize": {n: {"us": round(st[n]["mean"] * 1e3, 2), "bytes": qbytes[n],
+                             "GB/s": round(qbytes[n] / (st[n]["mean"] * 1e-3) / 1e9, 1)} for n in qbytes},
+            "note": "E4M3 Q, K (rotated by a seeded orthogonal matrix) and V with power-of-two block scales; "
+                    "caches flushed before each quantize + forward sequence",
+            "host_lead": lead_report(lead, host_s),
+        }
+        log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q/k/v "
+            f"{st['quant_q']['mean']*1e3:.1f}/{st['quant_k']['mean']*1e3:.1f}/{st['quant_v']['mean']*1e3:.1f} us")
 
     # ---- larger prefill workloads, timed on their own ----
     if not args.no_extra:

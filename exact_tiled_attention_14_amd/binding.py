@@ -210,7 +210,7 @@ def fa_quantize_fp8(x, block_rows: int, layout: int = FA_FP8_ROWS, rot=None):
     ``layout`` FA_FP8_ROWS gives codes [B,H,S,d]; FA_FP8_VBLOCKS (for V,
     block_rows 64, no rotation) gives [B,H,ceil(S/64),d,64], each 64-key block
     d-major with the key order include/fa.h states.  ``rot`` is a bf16 [d,d]
-    matrix the rows are multiplied by first.  Returns ``(codes, scales)``,
+    orthogonal matrix R; each row x becomes R x first.  Returns ``(codes, scales)``,
     scales [B,H,ceil(S/block_rows)] uint8 E8M0 bytes.
     """
     lib = load()

@@ -12,9 +12,9 @@
 // matrix cores' scaled products take directly.
 //
 //   * quant_rows_kernel: rows of a [S, 128] slice, optionally rotated
-//     (x -> x R on the matrix cores: x R = (R^T x^T)^T with R^T staged in LDS
-//     once per workgroup; without R the identity is staged, which is exact),
-//     written row-major.
+//     (each row x -> R x on the matrix cores as D = R X^T, R's rows being the
+//     A operand, staged in LDS once per workgroup; without R the identity is
+//     staged, which is exact), written row-major.
 //   * quant_v_kernel: 64-key blocks of V (no rotation), written d-major: per
 //     block 128 rows (one per head-dim index) of 64 bytes, the keys of a row in
 //     the order in which the attention kernel's lanes hold P (see include/fa.h),
@@ -65,43 +65,37 @@ __device__ __forceinline__ float block_max(float x, float* red, int wave, int la
 }
 
 // R rows per block (64 or 128).  Wave w computes rows 32 (w % (R / 32)) ..
-// +31 of the block against NB = R / 32 of the four 32-column blocks of R^T:
-// D = R^T x^T, so lane l holds column-block entries n = 8 a + 4 h + e (h =
-// l / 32) of block row l % 32, four consecutive columns per register group:
-// exactly one 4-byte store per group.
+// +31 of the block against NB = R / 32 of the four 32-row blocks of the
+// rotation: D = Rot X^T, so lane l holds entries n = 8 a + 4 h + e (h = l / 32)
+// of the rotated block row l % 32, four consecutive columns per register
+// group: exactly one 4-byte store per group.
 template <int R>
 __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t* __restrict__ X,
                                                                const uint16_t* __restrict__ rot,
                                                                uint8_t* __restrict__ X8, uint8_t* __restrict__ scales,
                                                                int S, int nblk, int64_t total) {
     constexpr int NB = R / 32;                 // column blocks per wave
-    __shared__ __attribute__((aligned(16))) uint16_t rt[kQD * kQD];   // R^T, swizzled (below)
+    __shared__ __attribute__((aligned(16))) uint16_t rt[kQD * kQD];   // R, swizzled (below)
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // stage R^T (or the identity) once; 16-byte chunk c of row n sits at
+    // stage R (or the identity) once; 16-byte chunk c of row n sits at
     // chunk c ^ (n % 16), so the operand reads (32 rows, one chunk) spread
     // over all banks
     for (int c = tid; c < kQD * kQD / 8; c += kQThreads) {
-        const int k = c / (kQD / 8), n0 = 8 * (c % (kQD / 8));
-        uint16_t u[8];
+        const int n = c / (kQD / 8), ch = c % (kQD / 8);
+        u32x4 v;
         if (rot != nullptr) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(rot + k * kQD + n0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u[2 * i] = (uint16_t)(v[i] & 0xFFFFu);
-                u[2 * i + 1] = (uint16_t)(v[i] >> 16);
-            }
+            v = *reinterpret_cast<const u32x4*>(rot + n * kQD + 8 * ch);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) u[i] = (n0 + i == k) ? (uint16_t)0x3F80 : (uint16_t)0;
+            for (int i = 0; i < 4; ++i) {
+                const int k0 = 8 * ch + 2 * i;
+                v[i] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int n = n0 + i;
-            rt[n * kQD + 8 * ((k >> 3) ^ (n & 15)) + (k & 7)] = u[i];
-        }
+        *reinterpret_cast<u32x4*>(rt + n * kQD + 8 * (ch ^ (n & 15))) = v;
     }
     __syncthreads();
 
@@ -203,7 +197,7 @@ int quant_grid(int64_t total) {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
         n = 256;
-    return (int)std::min<int64_t>(total, (int64_t)4 * n);
+    return (int)std::min<int64_t>(total, (int64_t)2 * n);
 }
 
 }  // namespace

@@ -21,6 +21,7 @@ import numpy as np
 
 # MI355X published peaks (AMD specification; dense, no sparsity).
 MI355X_BF16_DENSE_FLOPS = 2.5e15
+MI355X_FP8_DENSE_FLOPS = 5.0e15
 MI355X_FP32_VECTOR_FLOPS = 157.3e12
 MI355X_HBM_BYTES_PER_S = 8.0e12
 
@@ -48,6 +49,12 @@ def prefill_min_bytes(B: int, Hq: int, Hkv: int, Sq: int, Sk: int, d: int,
     reads = (B * Hq * Sq * d + 2 * B * Hkv * Sk * d) * in_bytes
     writes = B * Hq * Sq * d * out_bytes + (B * Hq * Sq * 4 if with_lse else 0)
     return reads + writes
+
+
+def fp8_quantize_bytes(BH: int, S: int, d: int, block_rows: int) -> int:
+    """Bytes a block quantizer must move: bf16 input read once, one code byte
+    and one scale byte per block written."""
+    return BH * S * d * 2 + BH * S * d + BH * (-(-S // block_rows))
 
 
 def decode_kv_bytes(seqlens, Hkv: int, d: int, elem_bytes: int = 2) -> int:

@@ -79,6 +79,19 @@ def _run(args) -> None:
         torch.cuda.synchronize()
         launches.append(("backward", lambda: binding.fa_bwd(bq, bk, bv, bo, bg, bl, True, c.scale, dq=grads[0],
                                                             dk=grads[1], dv=grads[2], workspace=bws)))
+    if args.workload in ("fp8", "all"):
+        c = inputs.workload(PREFILL)
+        fq, fk, fv = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
+        rot = to_dev(inputs.bf16_bits(inputs.make_rotation(c.q.shape[-1], seed=2)))
+        q8, qs = binding.fa_quantize_fp8(fq, 128, rot=rot)
+        k8, ks = binding.fa_quantize_fp8(fk, 64, rot=rot)
+        v8, vs = binding.fa_quantize_fp8(fv, 64, layout=binding.FA_FP8_VBLOCKS)
+        fo = torch.empty_like(fq)
+        fl = torch.empty(fq.shape[:3], dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        launches.append(("fp8_quantize_q", lambda: binding.fa_quantize_fp8(fq, 128, rot=rot)))
+        launches.append(("fp8_forward", lambda: binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale, out=fo,
+                                                                   lse=fl)))
     if args.workload in ("decode", "all"):
         d = inputs.workload(DECODE)
         s = d.shape
@@ -230,7 +243,7 @@ def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--workload", choices=["prefill", "decode", "backward", "all"], default="all")
+    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "all"], default="all")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--copy-mib", type=int, default=1024)
     s = sub.add_parser("summarize")

@@ -198,9 +198,10 @@ size_t fa_quantize_fp8_bytes(int B, int H, int S, int d, int layout);
  * quantization (incoherent processing), which leaves Q K^T unchanged.
  *
  *   x      [B, H, S, d] bf16, device, read-only.
- *   rot    [d, d] bf16 orthogonal matrix or NULL: with rot each row is
- *          replaced by x_row * rot before quantization (pass the same rot for
- *          Q and K; never for V).  The product runs in fp32 on bf16 values.
+ *   rot    [d, d] bf16 orthogonal matrix R or NULL: with R each row vector
+ *          x is replaced by R x (the row times R^T) before quantization; pass
+ *          the same R for Q and K (scores are unchanged), never for V.  The
+ *          product runs on the matrix cores, bf16 values, fp32 sums.
  *   x8     output codes, fa_quantize_fp8_bytes(...) bytes.  Encoding: OCP
  *          E4M3 (bias 7, no infinities, largest finite 448), round to nearest
  *          even.  FA_FP8_ROWS: row-major [B, H, S, d].  FA_FP8_VBLOCKS: for

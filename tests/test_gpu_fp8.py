@@ -6,7 +6,7 @@ sides (the oracle's rounding is exact on bf16 inputs), so without rotation
 they must match bit for bit.  With the rotation inside the quantizer the GPU
 sums the 128 products of a row in fp32 on the matrix cores and the oracle in
 fp64, so an element whose rotated value lies within the fp32 summation bound
-(gamma_128 sum |x_k R_kn|, gamma_128 = 128 u / (1 - 128 u), u = 2^-24) of an
+(gamma_128 sum_k |R_nk x_k|, gamma_128 = 128 u / (1 - 128 u), u = 2^-24) of an
 E4M3 rounding midpoint may take either neighbouring code: the test accepts a
 differing code only at such elements (found from the oracle's values alone)
 and only as the other neighbour.  The attention parity tests on small shapes
@@ -85,11 +85,11 @@ def ambiguous_slack(x, rot, rows, other_max, scale):
     x = np.asarray(x, np.float64)
     R = np.asarray(rot, np.float64)
     u = 2.0 ** -24
-    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R))   # bound on an fp32 sum of the 128 products
+    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R).T)   # bound on an fp32 sum of the 128 products
     _, ex = F.quantize_blocks(x, rows, rot=R)
     S = x.shape[-2]
     s = np.ldexp(1.0, ex)[..., np.arange(S) // rows][..., None]
-    t, terr = np.abs(x @ R) / s, err / s
+    t, terr = np.abs(x @ R.T) / s, err / s
     # the scale of every block is decided with room to spare: its largest
     # value stays inside (224, 448] whichever way the fp32 sums round
     starts = np.arange(0, S, rows)
@@ -160,11 +160,11 @@ def ambiguous_mask(x, rot, rows):
     x = np.asarray(x, np.float64)
     R = np.asarray(rot, np.float64)
     u = 2.0 ** -24
-    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R))
+    err = 128 * u / (1 - 128 * u) * (np.abs(x) @ np.abs(R).T)
     _, ex = F.quantize_blocks(x, rows, rot=R)
     S = x.shape[-2]
     s = np.ldexp(1.0, ex)[..., np.arange(S) // rows][..., None]
-    t, terr = np.abs(x @ R) / s, err / s
+    t, terr = np.abs(x @ R.T) / s, err / s
     grid = F.e4m3_values()
     pos = np.unique(np.abs(grid[np.isfinite(grid)]))
     mids = (pos[:-1] + pos[1:]) / 2
@@ -246,8 +246,8 @@ def test_fp8_forward_small_shapes(B, shape, rotate):
     c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=causal, seed=400 + Sq + Sk)
     if rotate:
         R = I.make_rotation(128, seed=400 + Sq).astype(np.float64)
-        c.q = I.round_to_bf16((c.q @ R).astype(np.float32))
-        c.k = I.round_to_bf16((c.k @ R).astype(np.float32))
+        c.q = I.round_to_bf16((c.q @ R.T).astype(np.float32))
+        c.k = I.round_to_bf16((c.k @ R.T).astype(np.float32))
     o, lse = run_fp8(B, c, None)
     O, L, vd, _ = oracle_fp8(c, None)
     check_fp8_o(o, O, vd, f"fp8 {shape} prerotated={rotate}")
