@@ -205,12 +205,13 @@ def make_grad_out(shape, *, seed: int = 0, dtype: str = "bf16") -> np.ndarray:
 
 @dataclass
 class DecodeCase:
-    """One paged decode step: one new query token per sequence.
+    """One paged decode step: one new query token per sequence, or Sq new
+    tokens per sequence (``q`` [nseq, Sq, Hq, d]) for a multi-query step.
 
     The caches are kept as bf16 bit patterns (uint16) because they are large;
     :meth:`subset` extracts a few sequences with their pages as fp32 values.
     """
-    q: np.ndarray            # [nseq, Hq, d] float32 (bf16-exact)
+    q: np.ndarray            # [nseq, Hq, d] or [nseq, Sq, Hq, d] float32 (bf16-exact)
     kcache_bits: np.ndarray  # [num_blocks, Hkv, block_size, d] uint16 (bf16; NaN allowed in tails)
     vcache_bits: np.ndarray  # same
     block_table: np.ndarray  # [nseq, max_blocks] int32, -1 past a sequence's blocks
@@ -220,9 +221,12 @@ class DecodeCase:
 
     @property
     def shape(self):
-        nseq, Hq, d = self.q.shape
+        if self.q.ndim == 4:
+            nseq, Sq, Hq, d = self.q.shape
+        else:
+            (nseq, Hq, d), Sq = self.q.shape, 1
         nb, Hkv, bs, _ = self.kcache_bits.shape
-        return dict(nseq=nseq, Hq=Hq, Hkv=Hkv, d=d, block_size=bs, num_blocks=nb,
+        return dict(nseq=nseq, Sq=Sq, Hq=Hq, Hkv=Hkv, d=d, block_size=bs, num_blocks=nb,
                     max_blocks=self.block_table.shape[1])
 
     @property
@@ -273,8 +277,10 @@ def _normal_bf16_bits(rng, shape) -> np.ndarray:
 def make_decode(nseq: int, Hq: int, Hkv: int, d: int, *, len_lo: int, len_hi: int,
                 block_size: int = 16, seed: int = 0, scale: float | None = None,
                 max_blocks: int | None = None, poison_tail: bool = False,
-                seqlens: np.ndarray | None = None) -> DecodeCase:
-    """Seeded paged-cache decode inputs (see the module recipe)."""
+                seqlens: np.ndarray | None = None, sq: int = 0) -> DecodeCase:
+    """Seeded paged-cache decode inputs (see the module recipe).  ``sq`` > 0
+    gives ``sq`` new query tokens per sequence (q [nseq, sq, Hq, d]); the
+    cache holds them as the last ``sq`` tokens of each sequence."""
     rq, rl, rp, rk, rv = _streams(seed, 5)
     if seqlens is None:
         seqlens = rl.integers(len_lo, len_hi, size=nseq, endpoint=True)
@@ -302,7 +308,7 @@ def make_decode(nseq: int, Hq: int, Hkv: int, d: int, *, len_lo: int, len_hi: in
                 last = table[s, pages[s] - 1]
                 kc[last, :, n % block_size:, :] = nan_bits
                 vc[last, :, n % block_size:, :] = nan_bits
-    q = _normal(rq, (nseq, Hq, d))
+    q = _normal(rq, (nseq, sq, Hq, d) if sq > 0 else (nseq, Hq, d))
     _round_bf16_inplace(q)
     return DecodeCase(q=q, kcache_bits=kc, vcache_bits=vc, block_table=table, seqlens=seqlens,
                       scale=float(scale if scale is not None else 1.0 / math.sqrt(d)), seed=seed)
@@ -324,6 +330,11 @@ WORKLOADS = {
                                           check_rows=512),
     "paged_decode_64seq_h32kv8_d128": dict(kind="decode", seed=5, nseq=64, Hq=32, Hkv=8, d=128,
                                            len_lo=1024, len_hi=8192, block_size=16),
+    # multi-query verify step: the decode workload with 8 new tokens per
+    # sequence (7 draft tokens + 1), so a K/V head's 4 query heads x 8 tokens
+    # fill one 32-row matrix-core tile
+    "paged_verify_64seq_q8_h32kv8_d128": dict(kind="decode", seed=6, nseq=64, Hq=32, Hkv=8, d=128,
+                                              len_lo=1024, len_hi=8192, block_size=16, sq=8),
 }
 
 

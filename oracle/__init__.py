@@ -43,6 +43,7 @@ from .attention import (  # noqa: F401
     online_softmax_deferred,
     gather_pages,
     paged_decode,
+    paged_multi_query,
     split_partials,
     merge_partials,
     sdpa_backward,

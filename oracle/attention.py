@@ -34,6 +34,7 @@ __all__ = [
     "online_softmax_deferred",
     "gather_pages",
     "paged_decode",
+    "paged_multi_query",
     "split_partials",
     "merge_partials",
     "sdpa_backward",
@@ -268,6 +269,41 @@ def paged_decode(q, kcache, vcache, block_table, seqlens, scale: float):
             vis = np.ones((len(heads), n), dtype=bool)
             oo, ll, _ = _attend(q[s, heads], K, V, vis, scale)
             o[s, heads], lse[s, heads] = oo, ll
+    return o, lse
+
+
+def paged_multi_query(q, kcache, vcache, block_table, seqlens, scale: float):
+    """Sq new query tokens per sequence attending to the paged cache.
+
+    "Fast Inference and Training at Scale", section 6.5 Speculative Decoding
+    (the target model verifies the draft tokens in one forward pass, all of
+    their queries at once) with the cache of sections 6.1 and 6.3; "Week 13.
+    GPUs and FlashAttention", Step 1 (a verify pass carries B (gamma + 1)
+    tokens).  The cache already holds the Sq new tokens' K and V as the last
+    Sq of the sequence's ``seqlens[s]`` tokens; new token t sits at position
+    seqlens[s] - Sq + t and sees the keys up to and including its own
+    position (causal, bottom-right aligned).  A token whose position is
+    negative (seqlens[s] < Sq) sees no key: O = 0, lse = -inf.  This is
+    :func:`sdpa` with causal masking on the gathered sequence.
+
+    q: [nseq, Sq, Hq, d]; kcache, vcache: [num_blocks, Hkv, block_size, d];
+    block_table: [nseq, max_blocks] int; seqlens: [nseq] int.
+    Returns (o [nseq, Sq, Hq, d], lse [nseq, Sq, Hq]).
+    """
+    q = _as64(q)
+    nseq, Sq, Hq, d = q.shape
+    Hkv, bs = kcache.shape[1], kcache.shape[2]
+    o = np.zeros((nseq, Sq, Hq, d))
+    lse = np.full((nseq, Sq, Hq), -np.inf)
+    for s in range(nseq):
+        n = int(seqlens[s])
+        if n <= 0:
+            continue
+        K = np.stack([_as64(gather_pages(kcache, block_table[s], n, kv, bs)) for kv in range(Hkv)])[None]
+        V = np.stack([_as64(gather_pages(vcache, block_table[s], n, kv, bs)) for kv in range(Hkv)])[None]
+        oo, ll = sdpa(q[s].transpose(1, 0, 2)[None], K, V, True, scale)      # [1, Hq, Sq, d]
+        o[s] = oo[0].transpose(1, 0, 2)
+        lse[s] = ll[0].T
     return o, lse
 
 

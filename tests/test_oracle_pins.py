@@ -362,6 +362,79 @@ def test_paged_decode_empty_sequence():
     assert np.isneginf(lse[1]).all() and np.isfinite(lse[0]).all()
 
 
+# --- 8b. multi-query paged attention (verify / chunked steps) -------------
+
+def test_paged_multi_query_is_last_rows_of_causal_prefill():
+    """The Sq new tokens of a sequence get exactly the last Sq rows of a causal
+    prefill over the whole gathered sequence (their K, V are the last Sq
+    cached tokens)."""
+    rng = np.random.default_rng(12)
+    n, Sq, Hq, Hkv, d, bs = 45, 5, 4, 2, 4, 16
+    kc, vc, table = _paged([n], Hkv, d, bs, rng)
+    p = -(-n // bs)
+    K = kc[table[0, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+    V = vc[table[0, :p]].transpose(1, 0, 2, 3).reshape(Hkv, p * bs, d)[:, :n]
+    Q = rng.standard_normal((1, Hq, n, d))
+    O, L = oracle.sdpa(Q, K[None], V[None], True, 0.5)
+    q = Q[0, :, n - Sq:].transpose(1, 0, 2)[None]              # [1, Sq, Hq, d]
+    o, lse = oracle.paged_multi_query(q, kc, vc, table, np.array([n]), 0.5)
+    np.testing.assert_allclose(o[0], O[0, :, n - Sq:].transpose(1, 0, 2), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], L[0, :, n - Sq:].T, rtol=0, atol=1e-12)
+
+
+def test_paged_multi_query_with_one_token_is_decode():
+    rng = np.random.default_rng(13)
+    lens, Hq, Hkv, d, bs = [37, 16, 1, 50], 6, 2, 4, 16
+    kc, vc, table = _paged(lens, Hkv, d, bs, rng)
+    q = rng.standard_normal((len(lens), Hq, d))
+    o1, l1 = oracle.paged_decode(q, kc, vc, table, np.array(lens), 0.7)
+    o2, l2 = oracle.paged_multi_query(q[:, None], kc, vc, table, np.array(lens), 0.7)
+    np.testing.assert_allclose(o2[:, 0], o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2[:, 0], l1, rtol=0, atol=1e-12)
+
+
+def test_paged_multi_query_first_token_sees_all_but_the_new():
+    """Closed form of the mask: new token 0 sees the n - Sq + 1 first keys,
+    so with equal scores (q = 0) its output is the mean of those values."""
+    rng = np.random.default_rng(14)
+    n, Sq, d, bs = 40, 6, 3, 16
+    kc, vc, table = _paged([n], 1, d, bs, rng)
+    o, lse = oracle.paged_multi_query(np.zeros((1, Sq, 1, d)), kc, vc, table, np.array([n]), 1.0)
+    V = vc[table[0, :3], 0].reshape(-1, d)[:n]
+    for t in range(Sq):
+        seen = n - Sq + t + 1
+        np.testing.assert_allclose(o[0, t, 0], V[:seen].mean(axis=0), atol=1e-12)
+        np.testing.assert_allclose(lse[0, t, 0], np.log(seen), atol=1e-12)
+
+
+def test_paged_multi_query_short_sequence_rows_see_nothing():
+    rng = np.random.default_rng(15)
+    kc, vc, table = _paged([3], 1, 3, 16, rng)
+    o, lse = oracle.paged_multi_query(rng.standard_normal((1, 5, 2, 3)), kc, vc, table, np.array([3]), 1.0)
+    # positions 3 - 5 + t < 0 for t < 2
+    assert np.isneginf(lse[0, :2]).all() and np.isfinite(lse[0, 2:]).all()
+    np.testing.assert_array_equal(o[0, :2], 0.0)
+
+
+def test_multi_query_planted_mistakes_are_caught(monkeypatch):
+    """A verify step computed without the causal mask among the new tokens,
+    or with the new tokens aligned to the start of the cache, fails a pin."""
+    orig = oa.sdpa
+    for mutant in (lambda q, k, v, causal, scale, **kw: orig(q, k, v, False, scale, **kw),
+                   lambda q, k, v, causal, scale, **kw: orig(q, k[:, :, :q.shape[2]], v[:, :, :q.shape[2]], causal,
+                                                             scale, **kw)):
+        monkeypatch.setattr(oa, "sdpa", mutant)
+        caught = 0
+        for fn in (test_paged_multi_query_is_last_rows_of_causal_prefill,
+                   test_paged_multi_query_first_token_sees_all_but_the_new):
+            try:
+                fn()
+            except AssertionError:
+                caught += 1
+        monkeypatch.setattr(oa, "sdpa", orig)
+        assert caught, "no multi-query pin caught the planted mistake"
+
+
 # --- 9. the pins catch planted mistakes -----------------------------------
 
 def _run_pins(golden_dir):
@@ -376,6 +449,8 @@ def _run_pins(golden_dir):
         "shift": lambda: test_common_key_shift_moves_only_lse(True),
         "decode": test_paged_decode_equals_contiguous_attention,
         "marker": test_paged_decode_dominant_key_finds_its_logical_position,
+        "multi_query": test_paged_multi_query_is_last_rows_of_causal_prefill,
+        "mq_mask": test_paged_multi_query_first_token_sees_all_but_the_new,
         "brute": lambda: test_brute_force_tiny(1, 3, 1, 6, 4, 4, True),
     }
     for name, fn in checks.items():
