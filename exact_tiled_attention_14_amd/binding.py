@@ -57,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.fa_quantize_fp8.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
+    lib.fa_decode_multi_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_decode_multi_workspace_size.restype = sz
+    lib.fa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode_multi.restype = i
     lib.fa_time_next_call.argtypes = [vp, vp]
     lib.fa_time_next_call.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -368,4 +372,54 @@ def fa_decode(q, kcache, vcache, block_table, seqlens, scale: float | None = Non
                        _stream(dev))
     if st != FA_OK:
         raise FAError("fa_decode", st)
+    return out, lse
+
+
+def fa_decode_multi_workspace_size(nseq: int, Sq: int, Hq: int, Hkv: int, d: int, block_size: int,
+                                   max_blocks_per_seq: int) -> int:
+    return int(load().fa_decode_multi_workspace_size(nseq, Sq, Hq, Hkv, d, block_size, max_blocks_per_seq))
+
+
+def fa_decode_multi(q, kcache, vcache, block_table, seqlens, scale: float | None = None, out=None, lse=None,
+                    workspace=None):
+    """Sq new tokens per sequence against a paged cache (verify step).
+
+    q [nseq,Sq,Hq,d] bf16 (token t of sequence s at position seqlens[s]-Sq+t,
+    causal); caches, block_table and seqlens as for fa_decode.
+    Returns ``(o [nseq,Sq,Hq,d] bf16, lse [nseq,Sq,Hq] fp32)``.
+    """
+    lib = load()
+    _check(q, "q", torch.bfloat16, 4)
+    dev = q.device
+    _check(kcache, "kcache", torch.bfloat16, 4, dev)
+    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    _check(block_table, "block_table", torch.int32, 2, dev)
+    _check(seqlens, "seqlens", torch.int32, 1, dev)
+    nseq, Sq, Hq, d = q.shape
+    num_blocks, Hkv, bs, d2 = kcache.shape
+    if vcache.shape != kcache.shape or d2 != d:
+        raise ValueError("cache shape mismatch")
+    if block_table.shape[0] != nseq or seqlens.shape[0] != nseq:
+        raise ValueError("block_table / seqlens must have nseq rows")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = fa_decode_multi_workspace_size(nseq, Sq, Hq, Hkv, d, bs, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev:
+        raise ValueError("workspace must be on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 4, dev)
+    if lse is None:
+        lse = torch.empty((nseq, Sq, Hq), dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, 3, dev)
+    st = lib.fa_decode_multi(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(out),
+                             _ptr(lse), nseq, Sq, Hq, Hkv, d, bs, max_blocks, num_blocks, float(scale),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != FA_OK:
+        raise FAError("fa_decode_multi", st)
     return out, lse

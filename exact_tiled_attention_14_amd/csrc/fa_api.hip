@@ -193,4 +193,41 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+size_t fa_decode_multi_workspace_size(int nseq, int Sq, int Hq, int Hkv, int d, int block_size,
+                                      int max_blocks_per_seq) {
+    if (nseq < 1 || Sq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1) return 0;
+    if (d != 128 || block_size != 16) return 0;
+    return fa::decode_mq_workspace_bytes(nseq, Hkv, max_blocks_per_seq);
+}
+
+int fa_decode_multi(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, float* lse, int nseq, int Sq, int Hq, int Hkv, int d,
+                    int block_size, int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    TimingScope timing_scope;
+    if (!q || !kcache || !vcache || !block_table || !seqlens || !o) return FA_ERR_INVALID_ARG;
+    if (nseq < 1 || Sq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (!fits(nseq, Sq, Hq, d) || !fits(num_blocks, Hkv, block_size, d) ||
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return FA_ERR_INVALID_ARG;
+    if (d != 128 || block_size != 16) return FA_ERR_UNSUPPORTED;
+    const int g = Hq / Hkv;
+    if ((g != 1 && g != 2 && g != 4 && g != 8) || g * Sq > 32) return FA_ERR_UNSUPPORTED;
+    const int64_t nchunk = (max_blocks_per_seq + 127) / 128;
+    if (nchunk * nseq * Hkv > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_decode_multi_workspace_size(nseq, Sq, Hq, Hkv, d, block_size, max_blocks_per_seq);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
+    fa::DecodeMqArgs a{q, kcache, vcache, block_table, seqlens, o, lse, nseq, Sq, Hq, Hkv, max_blocks_per_seq,
+                       num_blocks, scale};
+    return fa::launch_decode_mq(a, workspace, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
+                                                                                                  : FA_ERR_HIP;
+}
+
 }  // extern "C"

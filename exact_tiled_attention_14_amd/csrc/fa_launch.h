@@ -70,6 +70,21 @@ struct DecodeArgs {
     float scale;
 };
 
+struct DecodeMqArgs {
+    const void* q;         // [nseq, Sq, Hq, 128]
+    const void* kcache;
+    const void* vcache;
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    void* o;               // [nseq, Sq, Hq, 128]
+    float* lse;            // [nseq, Sq, Hq] or nullptr
+    int nseq, Sq, Hq, Hkv, max_blocks, num_blocks;
+    float scale;
+};
+
+size_t decode_mq_workspace_bytes(int nseq, int Hkv, int max_blocks);
+hipError_t launch_decode_mq(const DecodeMqArgs& a, void* workspace, hipStream_t stream);
+
 // FP8 block quantization of a [BH, S, 128] bf16 tensor.
 struct QuantArgs {
     const void* x;

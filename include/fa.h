@@ -183,6 +183,46 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               void* stream);
 
 /*
+ * fa_decode_multi_workspace_size - bytes of device scratch fa_decode_multi
+ * needs for these sizes (partial outputs of sequences longer than 2048
+ * tokens); 0 for invalid or unsupported arguments.
+ */
+size_t fa_decode_multi_workspace_size(int nseq, int Sq, int Hq, int Hkv, int d, int block_size,
+                                      int max_blocks_per_seq);
+
+/*
+ * fa_decode_multi - Sq new query tokens per sequence against a paged cache
+ * (speculative-decoding verify step, chunked prefill).
+ *
+ * Passage: "Fast Inference and Training at Scale", section 6.5 Speculative
+ * Decoding (the target model evaluates all draft tokens in one forward pass),
+ * 6.1 KV Caching and 6.3 PagedAttention; "Week 13. GPUs and FlashAttention",
+ * Step 1 (a verify pass carries B (gamma + 1) tokens).
+ *
+ *   q            [nseq, Sq, Hq, d] bf16: the new tokens' queries.
+ *   kcache/vcache, block_table, seqlens, num_blocks: as for fa_decode; the
+ *                cache already holds the new tokens' K and V as the last Sq
+ *                of the seqlens[s] tokens of sequence s.
+ *   o            [nseq, Sq, Hq, d] bf16 output; lse [nseq, Sq, Hq] fp32
+ *                natural-log log-sum-exp, or NULL.
+ *
+ * Token t of sequence s sits at position seqlens[s] - Sq + t and attends to
+ * the cached keys at positions <= its own (causal, bottom-right aligned); a
+ * token with a negative position sees nothing (o = 0, lse = -inf).  Supported:
+ * d = 128, block_size = 16, Hq / Hkv in {1, 2, 4, 8} with (Hq / Hkv) * Sq <= 32
+ * (the query heads of a K/V head times the new tokens form one 32-row
+ * matrix-core tile); otherwise FA_ERR_UNSUPPORTED.  Device values are made
+ * safe as in fa_decode (lengths clamped, out-of-range block ids contribute no
+ * key, unused page slots never reach the output).  Workspace: caller-owned,
+ * 256-byte aligned, >= fa_decode_multi_workspace_size(...) bytes.
+ * Runs on `stream`; allocates nothing.  Returns FA_OK or a negative fa_status.
+ */
+int fa_decode_multi(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, float* lse, int nseq, int Sq, int Hq, int Hkv, int d,
+                    int block_size, int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * fa_quantize_fp8_bytes - bytes of the E4M3 codes fa_quantize_fp8 writes
  * for a [B, H, S, d] input in `layout` (FA_FP8_VBLOCKS pads S up to a
  * multiple of 64); 0 for invalid or unsupported arguments (d != 128).
@@ -257,8 +297,9 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
  * Measurement hook, not part of any attention computation.  start_event and
  * stop_event are hipEvent_t handles (created by the caller with timing
  * enabled; the library does not own them), both non-NULL, or both NULL to
- * clear.  The next fa_fwd, fa_bwd or fa_decode call made on the same host
- * thread launches its kernels with these events attached
+ * clear.  The next compute call (fa_fwd, fa_bwd, fa_decode, fa_decode_multi,
+ * fa_quantize_fp8 or fa_fwd_fp8) made on the same host thread launches its
+ * kernels with these events attached
  * (hipExtLaunchKernel): start_event records when the call's first kernel
  * begins executing and stop_event when its last kernel ends, so the elapsed
  * time between them is the call's GPU time without the stream markers that a

@@ -28,7 +28,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_workspace_size", "fa_fwd",
+    assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
+                           "fa_decode_multi_workspace_size", "fa_decode_workspace_size", "fa_fwd",
                            "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string",
                            "fa_time_next_call"]
 
@@ -167,3 +168,28 @@ def test_quantize_fp8_bytes(lib):
     assert f(2, 16, 2048, 128, 0) == 2 * 16 * 2048 * 128
     assert f(1, 2, 100, 128, 1) == 2 * 2 * 64 * 128      # V blocks pad 100 keys to 128
     assert f(1, 2, 100, 64, 0) == 0 and f(1, 2, 100, 128, 5) == 0 and f(0, 1, 1, 128, 0) == 0
+
+
+def _mq(lib, q=16, kc=32, vc=48, bt=64, sl=80, o=96, lse=0, nseq=2, Sq=4, Hq=8, Hkv=2, d=128, bs=16, mb=8,
+        nb=10, scale=0.1, ws=256, wsb=1 << 24):
+    P = ctypes.c_void_p
+    return lib.fa_decode_multi(P(q), P(kc), P(vc), P(bt), P(sl), P(o), P(lse) if lse else None, nseq, Sq, Hq, Hkv,
+                               d, bs, mb, nb, scale, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(sl=0), -1), (dict(Sq=0), -1), (dict(nb=0), -1), (dict(Hq=6, Hkv=4), -1),
+    (dict(scale=0.0), -1), (dict(q=24), -1), (dict(bt=66), -1), (dict(lse=98), -1),
+    (dict(d=64), -2), (dict(bs=32), -2), (dict(Sq=9), -2), (dict(Hq=32, Hkv=2), -2),
+    (dict(ws=0), -3), (dict(wsb=16), -3), (dict(ws=264), -3),
+])
+def test_decode_multi_rejects_before_launch(lib, kw, status):
+    assert _mq(lib, **kw) == status
+
+
+def test_decode_multi_workspace_size(lib):
+    f = lib.fa_decode_multi_workspace_size
+    # 128-page chunks; per (sequence, K/V head, chunk) 32 rows of 128 floats + 32 lse
+    assert f(64, 8, 32, 8, 128, 16, 512) == 64 * 8 * 4 * 32 * 129 * 4
+    assert f(1, 1, 1, 1, 128, 16, 1) == 256 * ((32 * 129 * 4 + 255) // 256)
+    assert f(1, 1, 1, 1, 64, 16, 1) == 0 and f(1, 1, 1, 1, 128, 8, 1) == 0

@@ -1,0 +1,135 @@
+"""GPU parity of multi-query paged attention (fa_decode_multi) against the
+fp64 oracle (oracle.paged_multi_query): Sq new tokens per sequence, each
+seeing the cache up to its own position.  Same bf16 tolerances as the other
+bf16 paths: max |dO| <= 2e-2, rel-RMS <= 5e-3, lse within 1e-3 with -inf
+exactly where the oracle has -inf."""
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from exact_tiled_attention_14_amd import inputs as I  # noqa: E402
+
+DEV = "cuda:0"
+MAX_ABS, REL_RMS, LSE_TOL = 2e-2, 5e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_tiled_attention_14_amd import binding
+    binding.load()
+    return binding
+
+
+def _bf(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def run(Bm, d, table=None):
+    bt = d.block_table if table is None else table
+    o, lse = Bm.fa_decode_multi(_bf(d.bits("q")), _bf(d.kcache_bits), _bf(d.vcache_bits),
+                                torch.from_numpy(bt).to(DEV), torch.from_numpy(d.seqlens).to(DEV), d.scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check(o, lse, O, L, label):
+    assert np.isfinite(o).all(), f"{label}: non-finite output"
+    err = np.abs(o - O)
+    ma = float(err.max())
+    rr = float(np.sqrt((err ** 2).sum() / max((O ** 2).sum(), 1e-300)))
+    print(f"{label}: max_abs={ma:.3e} rel_rms={rr:.3e}", flush=True)
+    assert ma <= MAX_ABS and rr <= REL_RMS, label
+    ninf = np.isneginf(L)
+    assert (np.isneginf(lse) == ninf).all(), f"{label}: -inf pattern"
+    if (~ninf).any():
+        assert float(np.abs(lse[~ninf] - L[~ninf]).max()) <= LSE_TOL, label
+
+
+@pytest.mark.parametrize("Hq,Hkv,Sq", [(32, 8, 8), (8, 8, 32), (8, 1, 4), (16, 8, 16), (32, 8, 5), (8, 2, 1)])
+def test_head_groups_and_token_counts(B, Hq, Hkv, Sq):
+    d = I.make_decode(5, Hq, Hkv, 128, len_lo=1, len_hi=700, seed=Hq + Hkv + Sq, sq=Sq)
+    o, lse = run(B, d)
+    O, L = oracle.paged_multi_query(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check(o, lse, O, L, f"Hq{Hq} Hkv{Hkv} Sq{Sq}")
+
+
+def test_ragged_lengths_nan_tails_and_short_sequences(B):
+    lens = np.array([1, 3, 8, 15, 16, 17, 33, 1000, 4095], dtype=np.int32)    # 1 and 3 < Sq: rows see nothing
+    d = I.make_decode(len(lens), 32, 8, 128, len_lo=1, len_hi=4096, seed=77, poison_tail=True, seqlens=lens, sq=8)
+    o, lse = run(B, d)
+    O, L = oracle.paged_multi_query(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check(o, lse, O, L, "ragged + NaN tails")
+
+
+@pytest.mark.parametrize("lens", [[2048], [2049, 4100], [8192, 2047, 6000]], ids=["one-chunk", "two-three", "four"])
+def test_long_sequences_split_in_chunks(B, lens):
+    lens = np.array(lens, dtype=np.int32)
+    d = I.make_decode(len(lens), 32, 8, 128, len_lo=1, len_hi=8192, seed=int(lens.sum()) % 997, seqlens=lens, sq=8)
+    o, lse = run(B, d)
+    O, L = oracle.paged_multi_query(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check(o, lse, O, L, f"chunks {lens.tolist()}")
+
+
+def test_empty_sequence_and_bad_block_ids(B):
+    lens = np.array([0, 40, 40], dtype=np.int32)
+    d = I.make_decode(3, 8, 2, 128, len_lo=1, len_hi=64, seed=5, seqlens=lens, sq=4)
+    table = d.block_table.copy()
+    table[2, 1] = 10 ** 6                      # tokens 16..31 of sequence 2: no key
+    o, lse = run(B, d, table)
+    O, L = oracle.paged_multi_query(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check(o[:2], lse[:2], O[:2], L[:2], "empty + valid")
+    assert (o[0] == 0).all() and np.isneginf(lse[0]).all()
+    # sequence 2 with its second page removed, by the oracle on the same keys
+    keep = np.r_[0:16, 32:40]
+    Kc, Vc = d.kcache, d.vcache
+    K = np.concatenate([Kc[d.block_table[2, p]] for p in range(3)], axis=1)[:, keep]   # [Hkv, 24, d]
+    V = np.concatenate([Vc[d.block_table[2, p]] for p in range(3)], axis=1)[:, keep]
+    q = d.q[2].transpose(1, 0, 2)[None]                    # [1, Hq, Sq, d]
+    pos = np.arange(40)[keep]
+    for t in range(4):
+        vis = pos <= 40 - 4 + t
+        Ot, Lt = oracle.sdpa(q[:, :, t:t + 1], K[None][:, :, vis], V[None][:, :, vis], False, d.scale)
+        check(o[2, t][None], lse[2, t][None], Ot[0, :, 0][None], Lt[0, :, 0][None], f"bad block id, token {t}")
+
+
+def test_verify_workload_sampled(B):
+    """The 64-sequence, 8-token verify workload in the benchmark's launch
+    configuration; 10 sequences (shortest and longest included) checked."""
+    d = I.workload("paged_verify_64seq_q8_h32kv8_d128")
+    o, lse = run(B, d)
+    rng = np.random.default_rng(606)
+    seqs = sorted(set(rng.choice(64, 8, replace=False).tolist()) | {int(np.argmin(d.seqlens)), int(np.argmax(d.seqlens))})
+    sub = d.subset(seqs)
+    O, L = oracle.paged_multi_query(sub.q, sub.kcache, sub.vcache, sub.block_table, sub.seqlens, sub.scale)
+    check(o[seqs], lse[seqs], O, L, "verify workload")
+
+
+def test_one_token_matches_decode(B):
+    d = I.make_decode(6, 32, 8, 128, len_lo=100, len_hi=3000, seed=31, sq=1)
+    o, lse = run(B, d)
+    o1, l1 = B.fa_decode(_bf(I.bf16_bits(d.q[:, 0])), _bf(d.kcache_bits), _bf(d.vcache_bits),
+                         torch.from_numpy(d.block_table).to(DEV), torch.from_numpy(d.seqlens).to(DEV), d.scale)
+    torch.cuda.synchronize()
+    assert np.abs(o[:, 0] - o1.float().cpu().numpy()).max() <= 2 * MAX_ABS / 4
+    assert np.abs(lse[:, 0] - l1.cpu().numpy()).max() <= LSE_TOL
+
+
+def test_binding_errors(B):
+    d = I.make_decode(2, 8, 2, 128, len_lo=10, len_hi=20, seed=1, sq=5)     # 4 heads x 5 tokens = 20 rows: fine
+    q = _bf(d.bits("q"))
+    kc, vc = _bf(d.kcache_bits), _bf(d.vcache_bits)
+    bt, sl = torch.from_numpy(d.block_table).to(DEV), torch.from_numpy(d.seqlens).to(DEV)
+    big = torch.zeros((2, 9, 8, 128), dtype=torch.bfloat16, device=DEV)     # 4 x 9 = 36 rows > 32
+    with pytest.raises(B.FAError) as e:
+        B.fa_decode_multi(big, kc, vc, bt, sl)
+    assert e.value.status == B.FA_ERR_UNSUPPORTED
+    with pytest.raises(B.FAError) as e:
+        B.fa_decode_multi(q, kc, vc, bt, sl, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == B.FA_ERR_WORKSPACE
