@@ -52,6 +52,8 @@ EXTRA = ["causal_gqa_h32kv8_s8192_d128_outliers", "causal_gqa_h32kv8_s32768_d128
 PROFILE_PREFILL = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_b2_h16_s2048_d128.md")
 PROFILE_DECODE = os.path.join(ROOT, "profiles", "decode_paged_64seq_h32kv8_d128.md")
 PROFILE_FP8 = os.path.join(ROOT, "profiles", "fwd_fp8_causal_mha_b2_h16_s2048_d128.md")
+PROFILE_VERIFY = os.path.join(ROOT, "profiles", "decode_multi_paged_64seq_q8_h32kv8_d128.md")
+VERIFY = "paged_verify_64seq_q8_h32kv8_d128"
 CPU_MIN_SECONDS = 10.0
 
 
@@ -95,6 +97,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
+    ap.add_argument("--no-verify", action="store_true", help="skip the multi-query (verify) decode timing")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads per oracle call when timing the CPU baseline")
     args = ap.parse_args()
 
@@ -350,6 +353,54 @@ def main():
         }
         log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q/k/v "
             f"{st['quant_q']['mean']*1e3:.1f}/{st['quant_k']['mean']*1e3:.1f}/{st['quant_v']['mean']*1e3:.1f} us")
+
+    # ---- multi-query paged attention (verify step, 8 new tokens per sequence) ----
+    if not args.no_verify:
+        log("verify: inputs")
+        cv = inputs.workload(VERIFY)
+        vshp = cv.shape
+        v_q = to_dev(cv.bits("q"))
+        v_kc, v_vc = to_dev(cv.kcache_bits), to_dev(cv.vcache_bits)
+        v_bt = torch.from_numpy(cv.block_table).to(dev)
+        v_sl = torch.from_numpy(cv.seqlens).to(dev)
+        v_o = torch.empty_like(v_q)
+        v_l = torch.empty((vshp["nseq"], vshp["Sq"], vshp["Hq"]), dtype=torch.float32, device=dev)
+        v_ws = torch.empty(binding.fa_decode_multi_workspace_size(vshp["nseq"], vshp["Sq"], vshp["Hq"], vshp["Hkv"],
+                                                                  vshp["d"], vshp["block_size"], vshp["max_blocks"]),
+                           dtype=torch.uint8, device=dev)
+
+        def run_verify():
+            binding.fa_decode_multi(v_q, v_kc, v_vc, v_bt, v_sl, cv.scale, out=v_o, lse=v_l, workspace=v_ws)
+
+        for _ in range(2):
+            run_verify()
+        reps = max(5, min(K, 20))
+        evs = kernel_events(reps)
+        torch.cuda.synchronize()
+        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
+        host0 = time.perf_counter()
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(i & 0xFF)
+            binding.fa_time_next_call(a, b)
+            run_verify()
+        host_s = time.perf_counter() - host0
+        torch.cuda.synchronize()
+        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
+        vbytes = metrics.decode_kv_bytes(cv.seqlens, vshp["Hkv"], vshp["d"])
+        gbs_v = vbytes / (st["mean"] * 1e-3) / 1e9
+        result["verify"] = {
+            "workload": VERIFY, "kernels": "mq_partial_kernel<4> + mq_combine_kernel<4>", "bound": "hbm",
+            "achieved": round(gbs_v, 1), "peak": peak_gb, "unit": "GB/s", "frac": round(gbs_v / peak_gb, 4),
+            "traffic": profiling.current_traffic(PROFILE_VERIFY),
+            "algorithmic_kv_bytes_per_launch": vbytes, "kv_tokens": cv.kv_tokens,
+            "flops_per_launch": metrics.decode_flops(cv.seqlens, vshp["Hq"], vshp["d"]) * vshp["Sq"],
+            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
+            "note": "caches flushed (512 MiB write) before each launch, outside its events",
+            "host_lead": lead_report(lead, host_s),
+        }
+        log(f"verify: {st['mean']*1e3:.1f} us -> {gbs_v:.0f} GB/s")
+        del v_q, v_kc, v_vc, v_o, v_ws
+        torch.cuda.empty_cache()
 
     # ---- larger prefill workloads, timed on their own ----
     if not args.no_extra:

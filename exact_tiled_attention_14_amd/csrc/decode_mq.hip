@@ -14,9 +14,9 @@
 //   * Rows: the G = Hq/Hkv query heads of a K/V head times the Sq tokens form
 //     R = G Sq <= 32 rows, one 32-row matrix-core tile (row r = token r / G,
 //     head r % G); a page is read once for all of them.
-//   * Work: one workgroup per (K/V-head chunk of 128 pages, sequence, K/V
-//     head), chunk-major so the first chunks of all sequences go first; each
-//     of its 4 waves takes 32 pages.  A step is 2 pages (32 keys): K goes
+//   * Work: one workgroup per (chunk of 128 pages, sequence, K/V head),
+//     chunk-major so the first chunks of all sequences go first; the chunk's
+//     pages are split evenly over its 4 waves.  A step is 2 pages (32 keys): K goes
 //     straight from HBM into the registers that form the A operand of
 //     S^T = K Q^T (lane = key row, 16-byte loads), the next step's K loads are
 //     issued before this step's products; V goes by global-to-LDS loads into
@@ -102,8 +102,11 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
     if (chunk >= max(nch, 1)) return;                     // whole workgroup: no barrier reached
 
     const int32_t* trow = table + (int64_t)s * max_blocks;
-    const int p0 = chunk * kChunkPages + wave * kPagesPerWave;
-    const int p1 = min(p0 + kPagesPerWave, npages);
+    // the chunk's pages, split evenly over the 4 waves (a last, partial chunk too)
+    const int ch0 = chunk * kChunkPages, ch1 = min(ch0 + kChunkPages, npages);
+    const int per = (ch1 - ch0 + kWavesM - 1) / kWavesM;
+    const int p0 = min(ch0 + wave * per, ch1);
+    const int p1 = min(p0 + per, ch1);
     const int n_steps = p1 > p0 ? (p1 - p0 + 1) / 2 : 0;
 
     // this lane's query row: token t, head kvh * G + j
@@ -126,10 +129,13 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
     // lane l -> row 4c + l / 16, physical chunk l % 16 (swizzle 4 (row % 4))
     const int v_lane_el = (lane >> 4) * kD + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
 
+    // The wave's page ids (at most 32), one per lane, loaded once; a step reads
+    // its two ids from this register (uniform lane reads, no branch around
+    // them) instead of waiting on table loads behind its own prefetch.
+    const int tb_lane = (p0 + lane < p1) ? trow[p0 + lane] : -1;
     auto blk_of = [&](int p) -> int {                     // block id of page p, -1 if unusable
-        if (p >= p1) return -1;
-        const int b = trow[p];
-        return (b >= 0 && b < num_blocks) ? b : -1;
+        const int b = __builtin_amdgcn_readlane(tb_lane, min(max(p - p0, 0), 63));
+        return (p < p1 && b >= 0 && b < num_blocks) ? b : -1;
     };
     auto issue_v = [&](int step, uint8_t* stage) {
         const int pa = p0 + 2 * step;
@@ -138,18 +144,21 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
         for (int c = 0; c < 8; ++c) {
             const int b = c < 4 ? b0 : b1;
             const uint16_t* g = VC + page_row(b, Hkv, kvh, 4 * (c & 3)) + v_lane_el;
+            // cache policy 2: non-temporal, the pages are streamed once
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                             (__attribute__((address_space(3))) void*)(stage + c * 1024), 16, 0, 0);
+                                             (__attribute__((address_space(3))) void*)(stage + c * 1024), 16, 0, 2);
         }
     };
     // K operand of S^T = K Q^T: lane l -> key l % 32 of the step (page
     // (l % 32) / 16, slot l % 16), head-dim elements 16 i + 8 h .. +7
     auto load_k = [&](int step, bf16x8 (&kr)[kD / 16]) {
-        const int pa = p0 + 2 * step + (l32 >> 4);
-        const int b = max(blk_of(pa), 0);
+        const int pa = p0 + 2 * step;
+        const int b0 = max(blk_of(pa), 0), b1 = max(blk_of(pa + 1), 0);
+        const int b = l32 < 16 ? b0 : b1;
         const uint16_t* kp = KC + page_row(b, Hkv, kvh, l32 & 15) + 8 * hh;
 #pragma unroll
-        for (int i = 0; i < kD / 16; ++i) kr[i] = *reinterpret_cast<const bf16x8*>(kp + 16 * i);
+        for (int i = 0; i < kD / 16; ++i)
+            kr[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 16 * i)));
     };
 
     f32x16 oacc[4];

@@ -37,6 +37,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_KERNEL_HINT = "copyBuffer|elementwise|copy|fill"   # what the plain copy (and its source fill) show up as
 PREFILL = "causal_mha_b2_h16_s2048_d128"
 DECODE = "paged_decode_64seq_h32kv8_d128"
+VERIFY = "paged_verify_64seq_q8_h32kv8_d128"
 
 
 def source_sha256(path: str) -> str:
@@ -92,6 +93,19 @@ def _run(args) -> None:
         launches.append(("fp8_quantize_q", lambda: binding.fa_quantize_fp8(fq, 128, rot=rot)))
         launches.append(("fp8_forward", lambda: binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale, out=fo,
                                                                    lse=fl)))
+    if args.workload in ("verify", "all"):
+        cv = inputs.workload(VERIFY)
+        vs = cv.shape
+        vq, vkc, vvc = to_dev(cv.bits("q")), to_dev(cv.kcache_bits), to_dev(cv.vcache_bits)
+        vbt = torch.from_numpy(cv.block_table).to(dev)
+        vsl = torch.from_numpy(cv.seqlens).to(dev)
+        vo = torch.empty_like(vq)
+        vl = torch.empty((vs["nseq"], vs["Sq"], vs["Hq"]), dtype=torch.float32, device=dev)
+        vws = torch.empty(binding.fa_decode_multi_workspace_size(vs["nseq"], vs["Sq"], vs["Hq"], vs["Hkv"], vs["d"],
+                                                                 vs["block_size"], vs["max_blocks"]),
+                          dtype=torch.uint8, device=dev)
+        launches.append(("verify", lambda: binding.fa_decode_multi(vq, vkc, vvc, vbt, vsl, cv.scale, out=vo, lse=vl,
+                                                                   workspace=vws)))
     if args.workload in ("decode", "all"):
         d = inputs.workload(DECODE)
         s = d.shape
@@ -243,7 +257,7 @@ def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "all"], default="all")
+    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "verify", "all"], default="all")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--copy-mib", type=int, default=1024)
     s = sub.add_parser("summarize")

@@ -68,7 +68,8 @@ def test_ragged_lengths_nan_tails_and_short_sequences(B):
     check(o, lse, O, L, "ragged + NaN tails")
 
 
-@pytest.mark.parametrize("lens", [[2048], [2049, 4100], [8192, 2047, 6000]], ids=["one-chunk", "two-three", "four"])
+@pytest.mark.parametrize("lens", [[2048], [2049, 4100], [8192, 2047, 6000], [70, 130, 2090, 40]],
+                         ids=["one-chunk", "two-three", "four", "partial-chunks"])
 def test_long_sequences_split_in_chunks(B, lens):
     lens = np.array(lens, dtype=np.int32)
     d = I.make_decode(len(lens), 32, 8, 128, len_lo=1, len_hi=8192, seed=int(lens.sum()) % 997, seqlens=lens, sq=8)
