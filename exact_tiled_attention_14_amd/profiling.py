@@ -95,14 +95,14 @@ def _run(args) -> None:
                                                                    lse=fl)))
     if args.workload in ("verify", "all"):
         cv = inputs.workload(VERIFY)
-        vs = cv.shape
+        vsh = cv.shape
         vq, vkc, vvc = to_dev(cv.bits("q")), to_dev(cv.kcache_bits), to_dev(cv.vcache_bits)
         vbt = torch.from_numpy(cv.block_table).to(dev)
         vsl = torch.from_numpy(cv.seqlens).to(dev)
         vo = torch.empty_like(vq)
-        vl = torch.empty((vs["nseq"], vs["Sq"], vs["Hq"]), dtype=torch.float32, device=dev)
-        vws = torch.empty(binding.fa_decode_multi_workspace_size(vs["nseq"], vs["Sq"], vs["Hq"], vs["Hkv"], vs["d"],
-                                                                 vs["block_size"], vs["max_blocks"]),
+        vl = torch.empty((vsh["nseq"], vsh["Sq"], vsh["Hq"]), dtype=torch.float32, device=dev)
+        vws = torch.empty(binding.fa_decode_multi_workspace_size(vsh["nseq"], vsh["Sq"], vsh["Hq"], vsh["Hkv"], vsh["d"],
+                                                                 vsh["block_size"], vsh["max_blocks"]),
                           dtype=torch.uint8, device=dev)
         launches.append(("verify", lambda: binding.fa_decode_multi(vq, vkc, vvc, vbt, vsl, cv.scale, out=vo, lse=vl,
                                                                    workspace=vws)))
