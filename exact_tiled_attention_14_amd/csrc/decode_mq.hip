@@ -16,13 +16,14 @@
 //     head r % G); a page is read once for all of them.
 //   * Work: one workgroup per (chunk of 128 pages, sequence, K/V head),
 //     chunk-major so the first chunks of all sequences go first; the chunk's
-//     pages are split evenly over its 4 waves.  A step is 2 pages (32 keys): K goes
-//     straight from HBM into the registers that form the A operand of
-//     S^T = K Q^T (lane = key row, 16-byte loads), the next step's K loads are
-//     issued before this step's products; V goes by global-to-LDS loads into
-//     the wave's own LDS stages (double buffered) and is read back transposed
-//     (ds_read_b64_tr_b16) as the A operand of O^T += V^T P^T.  Waves share
-//     no data and meet only at the final merge.
+//     pages are split evenly over its 4 waves.  A step is 2 pages (32 keys):
+//     its K and V arrive in registers by coalesced non-temporal loads (1 KiB
+//     of contiguous memory per instruction), are written to the wave's own
+//     LDS tile, and are read back as matrix-core operands: K rows for
+//     S^T = K Q^T, V transposed (ds_read_b64_tr_b16) for O^T += V^T P^T.  The
+//     next step's loads are issued right after this step's tile is written,
+//     so they stream while this step computes.  Waves share no data and meet
+//     only at the final merge.
 //   * Online softmax per lane (one row) with the deferred rescale of the
 //     prefill kernel; keys past the sequence or the wave's pages, above a
 //     row's causal limit, or in pages whose block id is out of range are
@@ -70,7 +71,6 @@ __device__ __forceinline__ bf16x8 vt_op(const uint8_t* st, int ks, int db, int l
     return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Slot (in the K/V cache, in elements) of row `row` of page `blk` for head kvh.
 __device__ __forceinline__ int64_t page_row(int blk, int Hkv, int kvh, int row) {
@@ -124,10 +124,12 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
         }
     }
 
-    uint8_t* const vst = lds + wave * 2 * kStepBytes;     // this wave's two V stages
-    // global-to-LDS lane offset for V: load c fills rows 4c .. 4c+3 of a stage,
-    // lane l -> row 4c + l / 16, physical chunk l % 16 (swizzle 4 (row % 4))
-    const int v_lane_el = (lane >> 4) * kD + 8 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
+    // This wave's LDS tile for one step: K rows 0..31 (8 KiB), then V rows
+    // 0..31 (8 KiB), row-major 256-byte rows.  K chunks are XOR-swizzled by
+    // row % 16 and V chunks by 4 (row % 4), so the K operand reads (32 rows,
+    // one chunk) and the transposing V reads hit distinct banks.
+    uint8_t* const ktile = lds + wave * 2 * kStepBytes;
+    uint8_t* const vtile = ktile + kStepBytes;
 
     // The wave's page ids (at most 32), one per lane, loaded once; a step reads
     // its two ids from this register (uniform lane reads, no branch around
@@ -137,28 +139,21 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
         const int b = __builtin_amdgcn_readlane(tb_lane, min(max(p - p0, 0), 63));
         return (p < p1 && b >= 0 && b < num_blocks) ? b : -1;
     };
-    auto issue_v = [&](int step, uint8_t* stage) {
+    // One step's K and V straight into registers with coalesced 16-byte
+    // non-temporal loads: load c (0..7) takes rows 4 (c % 4) .. +3 of page
+    // c / 4, lane l row 4 (c % 4) + l / 16, 16-byte chunk l % 16 (1 KiB of
+    // contiguous memory per instruction).  A lane-per-key layout would touch
+    // 32 rows per instruction and streamed a third slower.
+    u32x4 kr[8], vr[8];
+    auto load_step = [&](int step) {
         const int pa = p0 + 2 * step;
         const int b0 = max(blk_of(pa), 0), b1 = max(blk_of(pa + 1), 0);
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            const int b = c < 4 ? b0 : b1;
-            const uint16_t* g = VC + page_row(b, Hkv, kvh, 4 * (c & 3)) + v_lane_el;
-            // cache policy 2: non-temporal, the pages are streamed once
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                             (__attribute__((address_space(3))) void*)(stage + c * 1024), 16, 0, 2);
+            const int64_t off = page_row(c < 4 ? b0 : b1, Hkv, kvh, 4 * (c & 3) + (lane >> 4)) + 8 * (lane & 15);
+            kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(KC + off));
+            vr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(VC + off));
         }
-    };
-    // K operand of S^T = K Q^T: lane l -> key l % 32 of the step (page
-    // (l % 32) / 16, slot l % 16), head-dim elements 16 i + 8 h .. +7
-    auto load_k = [&](int step, bf16x8 (&kr)[kD / 16]) {
-        const int pa = p0 + 2 * step;
-        const int b0 = max(blk_of(pa), 0), b1 = max(blk_of(pa + 1), 0);
-        const int b = l32 < 16 ? b0 : b1;
-        const uint16_t* kp = KC + page_row(b, Hkv, kvh, l32 & 15) + 8 * hh;
-#pragma unroll
-        for (int i = 0; i < kD / 16; ++i)
-            kr[i] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 16 * i)));
     };
 
     f32x16 oacc[4];
@@ -166,35 +161,31 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
     for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
     float m_run = kNegInf, l_run = 0.f;
 
-    bf16x8 ka[kD / 16], kb[kD / 16];
-    if (n_steps > 0) {
-        issue_v(0, vst);
-        load_k(0, ka);
-    }
-    auto step = [&](int it, bf16x8 (&kc)[kD / 16], bf16x8 (&kn)[kD / 16]) __attribute__((always_inline)) {
-        wait_vm_all();                                    // K(it) in registers, V(it) in LDS
-        if (it + 1 < n_steps) {
-            issue_v(it + 1, vst + ((it + 1) & 1) * kStepBytes);
-            load_k(it + 1, kn);
-        }
-        f32x16 sacc = f32x16{};
-#pragma unroll
-        for (int i = 0; i < kD / 16; ++i) sacc = mfma32(kc[i], qf[i], sacc);
-        // mask: keys of the step are pages pa, pa + 1 of this wave
+    if (n_steps > 0) load_step(0);
+    const int sw_k = l32 & 15;                            // K swizzle of this lane's operand row
+    auto step = [&](int it) __attribute__((always_inline)) {
         const int pa = p0 + 2 * it;
         const bool ok0 = blk_of(pa) >= 0, ok1 = blk_of(pa + 1) >= 0;
         const int end = min(len, p1 * kPage);            // first position this wave must not use
-        uint8_t* const st = vst + (it & 1) * kStepBytes;
-        if (pa * kPage + 32 > end || !ok0 || !ok1) {
-            // V rows of unusable keys may hold anything (NaN in unused slots):
-            // zero them, as p = 0 alone does not cancel a NaN in the product
+        // registers -> this wave's tile (the previous step's reads of it are
+        // done: a wave's LDS operations complete in order); V rows of unusable
+        // keys are written as zeros, as p = 0 alone does not cancel a NaN
 #pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const int r = 4 * c + (lane >> 4);
-                const bool bad = (r < 16 ? !ok0 : !ok1) || pa * kPage + r >= end;
-                if (bad) *reinterpret_cast<u32x4*>(st + r * 256 + 16 * (lane & 15)) = u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int c = 0; c < 8; ++c) {
+            const int r = 4 * c + (lane >> 4), ch = lane & 15;
+            const bool bad = (r < 16 ? !ok0 : !ok1) || pa * kPage + r >= end;
+            *reinterpret_cast<u32x4*>(ktile + r * 256 + 16 * (ch ^ (r & 15))) = kr[c];
+            *reinterpret_cast<u32x4*>(vtile + r * 256 + 16 * (ch ^ (4 * (r & 3)))) = bad ? u32x4{0u, 0u, 0u, 0u} : vr[c];
         }
+        if (it + 1 < n_steps) load_step(it + 1);          // in flight while this step computes
+        f32x16 sacc = f32x16{};
+        const uint8_t* krow = ktile + l32 * 256;
+#pragma unroll
+        for (int i = 0; i < kD / 16; ++i) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * i + hh) ^ sw_k));
+            sacc = mfma32(ka, qf[i], sacc);
+        }
+        // mask: keys of the step are pages pa, pa + 1 of this wave
         float mx = kNegInf;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -231,18 +222,14 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
         for (int ks = 0; ks < 2; ++ks) {
             const bf16x8 pb = __builtin_bit_cast(bf16x8, pw[ks]);
 #pragma unroll
-            for (int db = 0; db < 4; ++db) oacc[db] = mfma32(vt_op(st, ks, db, lane), pb, oacc[db]);
+            for (int db = 0; db < 4; ++db) oacc[db] = mfma32(vt_op(vtile, ks, db, lane), pb, oacc[db]);
         }
     };
-    for (int it = 0; it < n_steps; it += 2) {
-        step(it, ka, kb);
-        if (it + 1 < n_steps) step(it + 1, kb, ka);
-    }
-    wait_vm_all();
+    for (int it = 0; it < n_steps; ++it) step(it);
 
     // ---- merge the 4 waves: unnormalised o into this wave's own LDS stages ----
     const float l_tot = half_swap_sum(l_run);
-    float* ow = reinterpret_cast<float*>(vst);            // [32 rows][128] fp32 = 16 KiB
+    float* ow = reinterpret_cast<float*>(ktile);          // [32 rows][128] fp32 = the wave's 16 KiB tile
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
