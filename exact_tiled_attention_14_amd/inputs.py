@@ -314,6 +314,49 @@ def make_decode(nseq: int, Hq: int, Hkv: int, d: int, *, len_lo: int, len_hi: in
                       scale=float(scale if scale is not None else 1.0 / math.sqrt(d)), seed=seed)
 
 
+@dataclass
+class MLACase:
+    """One latent-cache decode step: a query token per sequence, a paged
+    cache of d_c-dimensional latents, and per-head up-projections."""
+    q: np.ndarray            # [nseq, H, d_h] float32 (bf16-exact)
+    w_uk: np.ndarray         # [H, d_c, d_h] float32 (bf16-exact): K = c W_uk[h]
+    w_uv_t: np.ndarray       # [H, d_h, d_c] float32 (bf16-exact): V = c W_uv_t[h]^T
+    cache: DecodeCase        # latent pages: kcache_bits [num_blocks, 1, block_size, d_c]
+    scale: float
+
+    @property
+    def ccache(self) -> np.ndarray:
+        return self.cache.kcache[:, 0]
+
+    @property
+    def ccache_bits(self) -> np.ndarray:
+        return np.ascontiguousarray(self.cache.kcache_bits[:, 0])
+
+    @property
+    def shape(self):
+        nseq, H, dh = self.q.shape
+        cs = self.cache.shape
+        return dict(nseq=nseq, H=H, d_h=dh, d_c=self.w_uk.shape[1], block_size=cs["block_size"],
+                    num_blocks=cs["num_blocks"], max_blocks=cs["max_blocks"])
+
+
+def make_mla_decode(nseq: int, H: int, d_h: int, d_c: int, *, len_lo: int, len_hi: int, seed: int = 0,
+                    seqlens: np.ndarray | None = None, poison_tail: bool = False) -> MLACase:
+    """Seeded latent-cache decode inputs: the paged latent cache as in
+    :func:`make_decode` (one "head" of width d_c), q ~ N(0,1), and
+    up-projections ~ N(0, 1/d_c) so that reconstructed keys and values have
+    unit variance; everything rounded to bf16."""
+    cache = make_decode(nseq, 1, 1, d_c, len_lo=len_lo, len_hi=len_hi, seed=seed, seqlens=seqlens,
+                        poison_tail=poison_tail)
+    rq, rk, rv = _streams(seed + 0x4D4C41, 3)
+    q = _normal(rq, (nseq, H, d_h))
+    wk = _normal(rk, (H, d_c, d_h)) * np.float32(1.0 / math.sqrt(d_c))
+    wv = _normal(rv, (H, d_h, d_c)) * np.float32(1.0 / math.sqrt(d_c))
+    for t in (q, wk, wv):
+        _round_bf16_inplace(t)
+    return MLACase(q=q, w_uk=wk, w_uv_t=wv, cache=cache, scale=1.0 / math.sqrt(d_h))
+
+
 # --- the five named workloads ---------------------------------------------
 
 WORKLOADS = {
@@ -335,6 +378,10 @@ WORKLOADS = {
     # fill one 32-row matrix-core tile
     "paged_verify_64seq_q8_h32kv8_d128": dict(kind="decode", seed=6, nseq=64, Hq=32, Hkv=8, d=128,
                                               len_lo=1024, len_hi=8192, block_size=16, sq=8),
+    # latent-cache decode: 64 sequences, 16 heads of 128 reading one
+    # 512-wide latent per token (keys and values rebuilt by up-projection)
+    "mla_decode_64seq_h16_dc512": dict(kind="mla", seed=7, nseq=64, H=16, d_h=128, d_c=512,
+                                       len_lo=1024, len_hi=8192),
 }
 
 
@@ -345,4 +392,6 @@ def workload(name: str, **overrides):
     kind = spec.pop("kind")
     if kind == "prefill":
         return make_prefill(**spec)
+    if kind == "mla":
+        return make_mla_decode(**spec)
     return make_decode(**spec)

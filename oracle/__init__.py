@@ -44,6 +44,7 @@ from .attention import (  # noqa: F401
     gather_pages,
     paged_decode,
     paged_multi_query,
+    mla_decode,
     split_partials,
     merge_partials,
     sdpa_backward,

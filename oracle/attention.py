@@ -35,6 +35,7 @@ __all__ = [
     "gather_pages",
     "paged_decode",
     "paged_multi_query",
+    "mla_decode",
     "split_partials",
     "merge_partials",
     "sdpa_backward",
@@ -304,6 +305,43 @@ def paged_multi_query(q, kcache, vcache, block_table, seqlens, scale: float):
         oo, ll = sdpa(q[s].transpose(1, 0, 2)[None], K, V, True, scale)      # [1, Hq, Sq, d]
         o[s] = oo[0].transpose(1, 0, 2)
         lse[s] = ll[0].T
+    return o, lse
+
+
+def mla_decode(q, w_uk, w_uv_t, ccache, block_table, seqlens, scale: float):
+    """Decode over a latent cache (multi-head latent attention).
+
+    "Fast Inference and Training at Scale", section 6.4 MLA: the cache keeps
+    only the compressed latent c (d_c values per token); each time a cached
+    token is attended to, its keys and values are reconstructed with learned
+    up-projections, K = c W_K and V = c W_V, then attention proceeds as usual
+    (one new query token per sequence, section 6.1; the paged cache of
+    section 6.3).  Written out as the pages state it: per head h the full
+    K_h = C W_K[h] and V_h = C W_V[h] are materialised.
+
+    q: [nseq, H, d_h]; w_uk: [H, d_c, d_h] (W_K per head); w_uv_t: [H, d_h,
+    d_c] (W_V per head, transposed); ccache: [num_blocks, block_size, d_c];
+    block_table [nseq, max_blocks]; seqlens [nseq].
+    Returns (o [nseq, H, d_h], lse [nseq, H]).
+    """
+    q = _as64(q)
+    nseq, H, dh = q.shape
+    wk, wv = _as64(w_uk), _as64(w_uv_t)
+    bs = ccache.shape[1]
+    cc = np.asarray(ccache)[:, None]                     # one latent "head"
+    o = np.zeros((nseq, H, dh))
+    lse = np.full((nseq, H), -np.inf)
+    for s in range(nseq):
+        n = int(seqlens[s])
+        if n <= 0:
+            continue
+        C = _as64(gather_pages(cc, block_table[s], n, 0, bs))       # [n, d_c]
+        for h in range(H):
+            K = C @ wk[h]                                           # [n, d_h]
+            V = C @ wv[h].T
+            vis = np.ones((1, n), dtype=bool)
+            oo, ll, _ = _attend(q[s, h][None], K, V, vis, scale)
+            o[s, h], lse[s, h] = oo[0], ll[0]
     return o, lse
 
 

@@ -435,6 +435,92 @@ def test_multi_query_planted_mistakes_are_caught(monkeypatch):
         assert caught, "no multi-query pin caught the planted mistake"
 
 
+# --- 8c. latent-cache (MLA) decode -----------------------------------------
+
+def _mla_case(rng, lens, H=3, dh=4, dc=6, bs=16):
+    kc, _, table = _paged(lens, 1, dc, bs, rng)
+    cc = kc[:, 0]                                             # [nb, bs, d_c]
+    q = rng.standard_normal((len(lens), H, dh))
+    wk = rng.standard_normal((H, dc, dh)) / np.sqrt(dc)
+    wv = rng.standard_normal((H, dh, dc)) / np.sqrt(dc)
+    return q, wk, wv, cc, table
+
+
+def test_mla_with_selecting_projections_is_mqa_decode():
+    """W_K = W_V = [I; 0] pick the first d_h latent values as key and value:
+    MLA is then single-K/V-head decode over those values."""
+    rng = np.random.default_rng(16)
+    lens = [37, 16, 50]
+    q, wk, wv, cc, table = _mla_case(rng, lens)
+    H, dh, dc = 3, 4, 6
+    sel = np.zeros((dc, dh))
+    sel[:dh] = np.eye(dh)
+    wk[:] = sel
+    wv[:] = sel.T
+    o, lse = oracle.mla_decode(q, wk, wv, cc, table, np.array(lens), 0.7)
+    c4 = cc[..., :dh][:, None]                                # [nb, 1, bs, d_h]
+    o2, l2 = oracle.paged_decode(q, c4, c4, table, np.array(lens), 0.7)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l2, rtol=0, atol=1e-12)
+
+
+def test_mla_absorbed_form_is_the_same_attention():
+    """Scores q . (c W_K) = (W_K q) . c and sum_j p_j c_j W_V = (sum_j p_j c_j) W_V:
+    attention over the latent values with the absorbed query, then the
+    up-projection, gives the same output (the form the kernels compute)."""
+    rng = np.random.default_rng(17)
+    lens = [40, 23]
+    q, wk, wv, cc, table = _mla_case(rng, lens)
+    o, lse = oracle.mla_decode(q, wk, wv, cc, table, np.array(lens), 0.5)
+    for s, n in enumerate(lens):
+        C = cc[table[s, :-(-n // 16)]].reshape(-1, cc.shape[-1])[:n]
+        for h in range(q.shape[1]):
+            qa = wk[h] @ q[s, h]                              # [d_c]
+            sc = 0.5 * (C @ qa)
+            m = sc.max()
+            p = np.exp(sc - m)
+            lat = (p @ C) / p.sum()
+            np.testing.assert_allclose(lat @ wv[h].T, o[s, h], atol=1e-12)
+            np.testing.assert_allclose(m + np.log(p.sum()), lse[s, h], atol=1e-12)
+
+
+def test_mla_heads_use_their_own_projections():
+    rng = np.random.default_rng(18)
+    lens = [30]
+    q, wk, wv, cc, table = _mla_case(rng, lens)
+    o, lse = oracle.mla_decode(q, wk, wv, cc, table, np.array(lens), 0.5)
+    perm = [2, 0, 1]
+    o2, l2 = oracle.mla_decode(q[:, perm], wk[perm], wv[perm], cc, table, np.array(lens), 0.5)
+    np.testing.assert_allclose(o2, o[:, perm], atol=1e-12)
+    np.testing.assert_allclose(l2, lse[:, perm], atol=1e-12)
+    # scaling W_V scales the output only; scaling W_K against q changes nothing
+    o3, l3 = oracle.mla_decode(q / 2, wk * 2, wv * 3, cc, table, np.array(lens), 0.5)
+    np.testing.assert_allclose(o3, 3 * o, atol=1e-12)
+    np.testing.assert_allclose(l3, lse, atol=1e-12)
+
+
+def test_mla_planted_mistakes_are_caught(monkeypatch):
+    """Keys from W_V, or values from the untransposed W_V layout, fail a pin."""
+    orig = oa.mla_decode
+
+    def swapped(q, w_uk, w_uv_t, *a, **k):
+        return orig(q, np.swapaxes(w_uv_t, 1, 2), np.swapaxes(w_uk, 1, 2), *a, **k)
+
+    def no_transpose(q, w_uk, w_uv_t, ccache, *a, **k):
+        return orig(q, w_uk, np.swapaxes(w_uk, 1, 2), ccache, *a, **k)
+
+    for mutant in (swapped, no_transpose):
+        monkeypatch.setattr(oracle, "mla_decode", mutant)
+        caught = 0
+        for fn in (test_mla_with_selecting_projections_is_mqa_decode, test_mla_absorbed_form_is_the_same_attention):
+            try:
+                fn()
+            except (AssertionError, ValueError):
+                caught += 1
+        monkeypatch.setattr(oracle, "mla_decode", orig)
+        assert caught, "no MLA pin caught the planted mistake"
+
+
 # --- 9. the pins catch planted mistakes -----------------------------------
 
 def _run_pins(golden_dir):
