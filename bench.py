@@ -54,6 +54,8 @@ PROFILE_DECODE = os.path.join(ROOT, "profiles", "decode_paged_64seq_h32kv8_d128.
 PROFILE_FP8 = os.path.join(ROOT, "profiles", "fwd_fp8_causal_mha_b2_h16_s2048_d128.md")
 PROFILE_VERIFY = os.path.join(ROOT, "profiles", "decode_multi_paged_64seq_q8_h32kv8_d128.md")
 VERIFY = "paged_verify_64seq_q8_h32kv8_d128"
+PROFILE_MLA = os.path.join(ROOT, "profiles", "mla_decode_64seq_h16_dc512.md")
+MLA = "mla_decode_64seq_h16_dc512"
 CPU_MIN_SECONDS = 10.0
 
 
@@ -98,6 +100,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--no-verify", action="store_true", help="skip the multi-query (verify) decode timing")
+    ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode timing")
     ap.add_argument("--cpu-heads", type=int, default=4, help="heads per oracle call when timing the CPU baseline")
     args = ap.parse_args()
 
@@ -400,6 +403,60 @@ def main():
         }
         log(f"verify: {st['mean']*1e3:.1f} us -> {gbs_v:.0f} GB/s")
         del v_q, v_kc, v_vc, v_o, v_ws
+        torch.cuda.empty_cache()
+
+    # ---- latent-cache (MLA) decode: 16 heads over one 512-wide latent per token ----
+    if not args.no_mla:
+        log("mla: inputs")
+        cm = inputs.workload(MLA)
+        msh = cm.shape
+        m_q, m_wk, m_wv = to_dev(inputs.bf16_bits(cm.q)), to_dev(inputs.bf16_bits(cm.w_uk)), \
+            to_dev(inputs.bf16_bits(cm.w_uv_t))
+        m_cc = to_dev(cm.ccache_bits)
+        m_bt = torch.from_numpy(cm.cache.block_table).to(dev)
+        m_sl = torch.from_numpy(cm.cache.seqlens).to(dev)
+        m_o = torch.empty_like(m_q)
+        m_l = torch.empty((msh["nseq"], msh["H"]), dtype=torch.float32, device=dev)
+        m_ws = torch.empty(binding.fa_mla_decode_workspace_size(msh["nseq"], msh["H"], msh["d_h"], msh["d_c"],
+                                                                msh["block_size"], msh["max_blocks"]),
+                           dtype=torch.uint8, device=dev)
+
+        def run_mla():
+            binding.fa_mla_decode(m_q, m_wk, m_wv, m_cc, m_bt, m_sl, cm.scale, out=m_o, lse=m_l, workspace=m_ws)
+
+        for _ in range(2):
+            run_mla()
+        reps = max(5, min(K, 20))
+        evs = kernel_events(reps)
+        torch.cuda.synchronize()
+        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
+        host0 = time.perf_counter()
+        for i, (a, b) in enumerate(evs):
+            flush.fill_(i & 0xFF)
+            binding.fa_time_next_call(a, b)
+            run_mla()
+        host_s = time.perf_counter() - host0
+        torch.cuda.synchronize()
+        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
+        lat_bytes = metrics.mla_latent_bytes(cm.cache.seqlens, msh["d_c"])
+        gbs_m = lat_bytes / (st["mean"] * 1e-3) / 1e9
+        result["mla"] = {
+            "workload": MLA, "bound": "hbm",
+            "kernels": "mla_absorb_kernel + mla_partial_kernel + mla_combine_kernel + mla_upproj_kernel",
+            "achieved": round(gbs_m, 1), "peak": peak_gb, "unit": "GB/s", "frac": round(gbs_m / peak_gb, 4),
+            "traffic": profiling.current_traffic(PROFILE_MLA),
+            "algorithmic_latent_bytes_per_launch": lat_bytes,
+            "min_bytes_per_launch": metrics.mla_total_bytes(cm.cache.seqlens, msh["H"], msh["d_h"], msh["d_c"]),
+            "kv_tokens": cm.cache.kv_tokens,
+            "flops_per_launch": metrics.mla_flops(cm.cache.seqlens, msh["H"], msh["d_h"], msh["d_c"]),
+            "materialized_kv_bytes_equivalent": metrics.decode_kv_bytes(cm.cache.seqlens, msh["H"], msh["d_h"]),
+            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
+            "note": "achieved = latent bytes over the whole call (4 kernels); caches flushed (512 MiB write) "
+                    "before each call, outside its events",
+            "host_lead": lead_report(lead, host_s),
+        }
+        log(f"mla: {st['mean']*1e3:.1f} us -> {gbs_m:.0f} GB/s of latents")
+        del m_q, m_wk, m_wv, m_cc, m_o, m_ws, cm
         torch.cuda.empty_cache()
 
     # ---- larger prefill workloads, timed on their own ----

@@ -61,6 +61,10 @@ def load() -> ctypes.CDLL:
     lib.fa_decode_multi_workspace_size.restype = sz
     lib.fa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_decode_multi.restype = i
+    lib.fa_mla_decode_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.fa_mla_decode_workspace_size.restype = sz
+    lib.fa_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_mla_decode.restype = i
     lib.fa_time_next_call.argtypes = [vp, vp]
     lib.fa_time_next_call.restype = i
     lib.fa_status_string.argtypes = [i]
@@ -422,4 +426,55 @@ def fa_decode_multi(q, kcache, vcache, block_table, seqlens, scale: float | None
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     if st != FA_OK:
         raise FAError("fa_decode_multi", st)
+    return out, lse
+
+
+def fa_mla_decode_workspace_size(nseq: int, H: int, d_h: int, d_c: int, block_size: int,
+                                 max_blocks_per_seq: int) -> int:
+    return int(load().fa_mla_decode_workspace_size(nseq, H, d_h, d_c, block_size, max_blocks_per_seq))
+
+
+def fa_mla_decode(q, w_uk, w_uv_t, ccache, block_table, seqlens, scale: float | None = None, out=None, lse=None,
+                  workspace=None):
+    """One new token per sequence against a paged latent cache (MLA).
+
+    q [nseq,H,d_h], w_uk [H,d_c,d_h], w_uv_t [H,d_h,d_c], ccache
+    [num_blocks,block_size,d_c], all bf16; block_table, seqlens as for
+    fa_decode.  Returns ``(o [nseq,H,d_h] bf16, lse [nseq,H] fp32)``.
+    """
+    lib = load()
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(w_uk, "w_uk", torch.bfloat16, 3, dev)
+    _check(w_uv_t, "w_uv_t", torch.bfloat16, 3, dev)
+    _check(ccache, "ccache", torch.bfloat16, 3, dev)
+    _check(block_table, "block_table", torch.int32, 2, dev)
+    _check(seqlens, "seqlens", torch.int32, 1, dev)
+    nseq, H, dh = q.shape
+    num_blocks, bs, dc = ccache.shape
+    if tuple(w_uk.shape) != (H, dc, dh) or tuple(w_uv_t.shape) != (H, dh, dc):
+        raise ValueError("projection shapes must be w_uk [H,d_c,d_h] and w_uv_t [H,d_h,d_c]")
+    if block_table.shape[0] != nseq or seqlens.shape[0] != nseq:
+        raise ValueError("block_table / seqlens must have nseq rows")
+    max_blocks = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(dh)
+    need = fa_mla_decode_workspace_size(nseq, H, dh, dc, bs, max_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif workspace.device != dev:
+        raise ValueError("workspace must be on q's device")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+    if lse is None:
+        lse = torch.empty((nseq, H), dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, 2, dev)
+    st = lib.fa_mla_decode(_ptr(q), _ptr(w_uk), _ptr(w_uv_t), _ptr(ccache), _ptr(block_table), _ptr(seqlens),
+                           _ptr(out), _ptr(lse), nseq, H, dh, dc, bs, max_blocks, num_blocks, float(scale),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
+    if st != FA_OK:
+        raise FAError("fa_mla_decode", st)
     return out, lse

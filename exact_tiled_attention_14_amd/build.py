@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "quant_fp8.hip", "fwd_fp8.hip", "decode_mq.hip"]
+SOURCES = ["fa_api.hip", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd_bf16.hip", "quant_fp8.hip", "fwd_fp8.hip", "decode_mq.hip", "mla.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 instructions are disabled for all device code: the compiler may

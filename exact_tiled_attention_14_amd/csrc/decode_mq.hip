@@ -43,6 +43,7 @@ constexpr int kWavesM = 4;
 constexpr int kThreadsM = 64 * kWavesM;
 constexpr int kPagesPerWave = 32;
 constexpr int kChunkPages = kPagesPerWave * kWavesM;     // 128 pages per workgroup
+static_assert(kPagesPerWave <= 64, "a wave's page ids fit one register across its lanes");
 constexpr int kStepBytes = 2 * kPage * kD * 2;           // V of one 32-key step: 8 KiB
 constexpr float kTauM = 8.f;
 

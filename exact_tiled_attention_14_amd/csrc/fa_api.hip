@@ -230,4 +230,39 @@ int fa_decode_multi(const void* q, const void* kcache, const void* vcache, const
                                                                                                   : FA_ERR_HIP;
 }
 
+size_t fa_mla_decode_workspace_size(int nseq, int H, int d_h, int d_c, int block_size, int max_blocks_per_seq) {
+    if (nseq < 1 || H < 1 || max_blocks_per_seq < 1) return 0;
+    if (d_h != 128 || d_c != 512 || block_size != 16 || H > 128) return 0;
+    return fa::mla_workspace_bytes(nseq, H, max_blocks_per_seq);
+}
+
+int fa_mla_decode(const void* q, const void* w_uk, const void* w_uv_t, const void* ccache,
+                  const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int nseq, int H,
+                  int d_h, int d_c, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    TimingScope timing_scope;
+    if (!q || !w_uk || !w_uv_t || !ccache || !block_table || !seqlens || !o) return FA_ERR_INVALID_ARG;
+    if (nseq < 1 || H < 1 || d_h < 1 || d_c < 1 || block_size < 1 || max_blocks_per_seq < 1 || num_blocks < 1)
+        return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(w_uk) || !aligned16(w_uv_t) || !aligned16(ccache) || !aligned16(o))
+        return FA_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(seqlens) & 3u))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (!fits(nseq, H, d_h, 1) || !fits(H, d_c, d_h, 1) || !fits(num_blocks, block_size, d_c, 1) ||
+        (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+        return FA_ERR_INVALID_ARG;
+    if (d_h != 128 || d_c != 512 || block_size != 16 || H > 128) return FA_ERR_UNSUPPORTED;
+    const int64_t nchunk = (max_blocks_per_seq + 31) / 32;
+    if (nchunk * nseq > INT32_MAX || nseq > 65535 * 32) return FA_ERR_UNSUPPORTED;
+    const size_t need = fa_mla_decode_workspace_size(nseq, H, d_h, d_c, block_size, max_blocks_per_seq);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
+    fa::MlaArgs a{q, w_uk, w_uv_t, ccache, block_table, seqlens, o, lse, nseq, H, max_blocks_per_seq, num_blocks,
+                  scale};
+    return fa::launch_mla_decode(a, workspace, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
+                                                                                                 : FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -85,6 +85,24 @@ struct DecodeMqArgs {
 size_t decode_mq_workspace_bytes(int nseq, int Hkv, int max_blocks);
 hipError_t launch_decode_mq(const DecodeMqArgs& a, void* workspace, hipStream_t stream);
 
+// Latent-cache decode: H query heads of 128 over a paged cache of 512-wide
+// latents, with per-head up-projections.
+struct MlaArgs {
+    const void* q;         // [nseq, H, 128]
+    const void* w_uk;      // [H, 512, 128]
+    const void* w_uv_t;    // [H, 128, 512]
+    const void* ccache;    // [num_blocks, 16, 512]
+    const int32_t* block_table;
+    const int32_t* seqlens;
+    void* o;               // [nseq, H, 128]
+    float* lse;            // [nseq, H] or nullptr
+    int nseq, H, max_blocks, num_blocks;
+    float scale;
+};
+
+size_t mla_workspace_bytes(int nseq, int H, int max_blocks);
+hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t stream);
+
 // FP8 block quantization of a [BH, S, 128] bf16 tensor.
 struct QuantArgs {
     const void* x;

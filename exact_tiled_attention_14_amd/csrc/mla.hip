@@ -1,0 +1,454 @@
+// Latent-cache (MLA) decode: one new query token per sequence attending to a
+// paged cache of compressed latents, gfx950.
+//
+// "Fast Inference and Training at Scale", section 6.4: the cache keeps only
+// the latent c (d_c = 512 values per token) and the keys and values of head h
+// are rebuilt from it, K_h = C W_K[h], V_h = C W_V[h].  Materialising them
+// would cost H d_h (2 of them) values per cached token; the kernels use the
+// same products in the other order (exact in real arithmetic):
+//
+//   score_hj = q_h . (c_j W_K[h]) = (W_K[h] q_h) . c_j
+//   o_h      = sum_j p_hj c_j W_V[h] = (sum_j p_hj c_j) W_V[h]
+//
+// so the latent itself serves as the single shared key and value (one K/V
+// head, as in section 6.2 with G = 1), and only the query and the output are
+// projected:
+//
+//   1. mla_absorb_kernel: q~ = W_K[h] q_h (fp32, d_c per head) for all
+//      sequences, on the matrix cores.
+//   2. mla_partial_kernel: attention of 16 absorbed queries (one head group)
+//      over the sequence's latents, per 32-page chunk of a sequence.  The
+//      four waves of a workgroup split the 512 latent dimensions into
+//      128-wide slices: each wave loads its slice of the chunk's latents
+//      (coalesced, two 32-token steps ahead, into registers, then its own
+//      LDS tile), computes its slice's part of the scores, and the four parts
+//      are summed through LDS, so every wave holds the full scores of the 16
+//      heads; each wave then accumulates its slice of sum_j p_hj c_j.  Online
+//      softmax as in the prefill kernel.  16 x 16 x 32 matrix-core products
+//      (16 tokens x 16 heads), so 16 heads fill the tile with no padding.
+//   3. mla_combine_kernel: merges the chunks of each sequence (log-sum-exp
+//      weights) into the normalised latent output (fp32).
+//   4. mla_upproj_kernel: o_h = (sum_j p_hj c_j) W_V[h] on the matrix cores.
+//
+// q~ and the latent output are intermediate results, not inputs: rounding
+// them to bf16 would add about 2^-9 relative error to every score and output
+// on top of what the plain path has.  Each is kept in fp32 and enters the
+// matrix cores as the sum of two bf16 terms (hi = bf16(x), lo = bf16(x - hi),
+// two products into one fp32 accumulator), which keeps it to about 2^-17.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+constexpr int kDC = 512;                // latent width
+constexpr int kDH = 128;                // head dim
+constexpr int kPageM = 16;
+constexpr int kChunkM = 32;             // pages per workgroup of the partial kernel
+constexpr int kHG = 16;                 // heads per workgroup of the partial kernel
+static_assert(kChunkM <= 64, "a chunk's page ids fit one register across a wave's lanes");
+constexpr int kThreadsL = 256;
+constexpr float kTauL = 8.f;
+
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// LDS tile rows are 256 bytes (128 bf16 of one token's latent slice); chunk c
+// of row r sits at c ^ swz(r).  Conflict-free for the operand reads of the
+// scores (16 consecutive rows, one chunk each), for the transposing reads of
+// the weighted sum (8 consecutive rows, one aligned chunk pair each) and for
+// the row writes (one row, 16 chunks).
+__device__ __forceinline__ int swz(int r) { return (2 * (r & 7)) ^ ((r >> 3) & 1); }
+
+__device__ __forceinline__ s16x4 lds_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const __attribute__((address_space(3))) uint8_t*)p);
+}
+
+// 16x16x32 bf16 matrix-core product, fp32 accumulation: lane l holds row
+// l % 16 of A and column l % 16 of B, contraction elements 8 (l / 16) .. +7;
+// the accumulator holds D[4 (l / 16) + r][l % 16] in register r.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed operand of the weighted sum for latent block blk (dims
+// 16 blk .. +15 of the slice): lane l receives dim 16 blk + l % 16 of the
+// tokens 4 g + e and 16 + 4 g + e (g = l / 16, e = 0..3), the order in which
+// a lane holds p.  Each 16-lane group reads a 4-row x 16-column block per
+// instruction and receives it transposed.
+__device__ __forceinline__ bf16x8 tr_op(const uint8_t* tile, int blk, int lane) {
+    const int s = lane & 15, g = lane >> 4;
+    const int col = 16 * blk + 4 * (s & 3);
+    const int r0 = 4 * g + (s >> 2), r1 = r0 + 16;
+    const int x = col >> 3, half = (col >> 2) & 1;
+    const s16x4 a = lds_tr16(tile + r0 * 256 + 16 * (x ^ swz(r0)) + 8 * half);
+    const s16x4 b = lds_tr16(tile + r1 * 256 + 16 * (x ^ swz(r1)) + 8 * half);
+    const s16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight fp32 values as hi + lo bf16 operands.
+__device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+    const u32x4 h = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                     pack_bf16x2(b[2], b[3])};
+    const u32x4 l = {pack_bf16x2(a[0] - bf16lo_to_f32(h[0]), a[1] - bf16hi_to_f32(h[0])),
+                     pack_bf16x2(a[2] - bf16lo_to_f32(h[1]), a[3] - bf16hi_to_f32(h[1])),
+                     pack_bf16x2(b[0] - bf16lo_to_f32(h[2]), b[1] - bf16hi_to_f32(h[2])),
+                     pack_bf16x2(b[2] - bf16lo_to_f32(h[3]), b[3] - bf16hi_to_f32(h[3]))};
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// ---- 1. absorbed queries: q~[s, h, :] = W_K[h] q[s, h] ----
+// Workgroup (h, 128 latent rows, 32 sequences); wave w computes 32 of the
+// rows: D[i][j] = sum_k W_K[h][i][k] q[s_j][h][k] (A = rows of W_K[h], B =
+// query rows), all loads issued before the 8 products.
+__global__ __launch_bounds__(kThreadsL) void mla_absorb_kernel(const uint16_t* __restrict__ Qin,
+                                                               const uint16_t* __restrict__ WK,
+                                                               float* __restrict__ Qa, int nseq, int H) {
+    const int h = blockIdx.x, s0 = blockIdx.z * 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int s = s0 + l32;
+    const int i_base = 128 * blockIdx.y + 32 * wave;
+    const uint16_t* qp = Qin + ((int64_t)min(s, nseq - 1) * H + h) * kDH + 8 * hh;
+    const uint16_t* wp = WK + ((int64_t)h * kDC + i_base + l32) * kDH + 8 * hh;
+    bf16x8 qb[kDH / 16], wa[kDH / 16];
+#pragma unroll
+    for (int k = 0; k < kDH / 16; ++k) {
+        qb[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+        wa[k] = *reinterpret_cast<const bf16x8*>(wp + 16 * k);
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k = 0; k < kDH / 16; ++k) acc = mfma32(wa[k], qb[k], acc);
+    if (s >= nseq) return;
+    float* out = Qa + ((int64_t)s * H + h) * kDC + i_base;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<f32x4*>(out + 8 * a + 4 * hh) = f32x4{acc[4 * a], acc[4 * a + 1], acc[4 * a + 2], acc[4 * a + 3]};
+}
+
+// ---- 2. attention over the latents, one chunk of a sequence, 16 heads ----
+__global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
+    const float* __restrict__ Qa, const uint16_t* __restrict__ CC, const int32_t* __restrict__ table,
+    const int32_t* __restrict__ seqlens, float* __restrict__ Olat, float* __restrict__ LSE,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, int nseq, int H, int Hp, int max_blocks, int num_blocks,
+    int nchunk, float scale_log2) {
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[4][32 * 256];   // each wave's latent slice, 32 tokens
+    __shared__ __attribute__((aligned(16))) float xs[2][4][2][64 * 4];      // per-wave partial scores, by step parity
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
+
+    const int chunk = blockIdx.x / nseq, s = blockIdx.x % nseq;   // chunk-major
+    const int head = kHG * blockIdx.y + l16;                      // this lane's head (>= H: padding)
+    const int len = min(max(seqlens[s], 0), max_blocks * kPageM);
+    const int npages = (len + kPageM - 1) / kPageM;
+    const int nch = (npages + kChunkM - 1) / kChunkM;
+    if (chunk >= max(nch, 1)) return;                     // whole workgroup: no barrier reached
+    const int p0 = chunk * kChunkM, p1 = min(p0 + kChunkM, npages);
+    const int n_steps = (p1 - p0 + 1) / 2;                // 0 for an empty sequence
+    const int32_t* trow = table + (int64_t)s * max_blocks;
+    const int tb_lane = (p0 + lane < p1) ? trow[p0 + lane] : -1;   // the chunk's page ids, one per lane
+    auto blk_of = [&](int p) -> int {
+        const int b = __builtin_amdgcn_readlane(tb_lane, min(max(p - p0, 0), 63));
+        return (p < p1 && b >= 0 && b < num_blocks) ? b : -1;
+    };
+
+    // this lane's 32 slice entries of its head's absorbed query (loaded here,
+    // split into hi + lo bf16 once the first latent loads are issued): the
+    // B operand of S^T = C Q~^T, contraction group g of 32 ks + ..
+    const bool row_ok = head < H;
+    f32x4 qraw[8];
+    {
+        const float* qp = Qa + ((int64_t)s * H + min(head, H - 1)) * kDC + 128 * wave + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            qraw[2 * ks] = *reinterpret_cast<const f32x4*>(qp + 32 * ks);
+            qraw[2 * ks + 1] = *reinterpret_cast<const f32x4*>(qp + 32 * ks + 4);
+        }
+    }
+    bf16x8 qh[4], ql[4];
+
+    uint8_t* const tile = tiles[wave];
+    // coalesced loads of this wave's slice of a step's 32 tokens: load c takes
+    // rows 4 (c % 4) + l / 16 of page c / 4, 16-byte chunk l % 16 of the
+    // slice.  Steps past the chunk read page 0 (never used).
+    auto load_step = [&](int step, u32x4 (&cr)[8]) {
+        const int pa = p0 + 2 * step;
+        const int b0 = max(blk_of(pa), 0), b1 = max(blk_of(pa + 1), 0);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int64_t row = (int64_t)(c < 4 ? b0 : b1) * kPageM + 4 * (c & 3) + (lane >> 4);
+            cr[c] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(CC + row * kDC + 128 * wave + 8 * (lane & 15)));
+        }
+    };
+
+    f32x4 oacc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) oacc[i] = f32x4{};
+    float m_run = kNegInf, l_run = 0.f;
+
+    auto step = [&](int it, u32x4 (&cr)[8]) __attribute__((always_inline)) {
+        const int pa = p0 + 2 * it;
+        const bool ok0 = blk_of(pa) >= 0, ok1 = blk_of(pa + 1) >= 0;
+        // registers -> tile; rows of unusable tokens are zero (the tile also
+        // serves as the value operand, where p = 0 would not cancel a NaN)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int r = 4 * c + (lane >> 4), ch = lane & 15;
+            const bool bad = (r < 16 ? !ok0 : !ok1) || pa * kPageM + r >= len;
+            *reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (ch ^ swz(r))) = bad ? u32x4{0u, 0u, 0u, 0u} : cr[c];
+        }
+        load_step(it + 2, cr);                            // in flight for two steps
+        // this wave's slice of the scores: S^T (16 tokens x 16 heads) per token block
+        f32x4 sp[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            sp[tb] = f32x4{};
+            const int r = 16 * tb + l16;
+            const uint8_t* crow = tile + r * 256;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const bf16x8 ca = *reinterpret_cast<const bf16x8*>(crow + 16 * ((4 * ks + g) ^ swz(r)));
+                sp[tb] = mfma16(ca, qh[ks], sp[tb]);
+                sp[tb] = mfma16(ca, ql[ks], sp[tb]);
+            }
+        }
+        // sum the four slices through LDS (double buffered by step parity)
+        float* xw = xs[it & 1][wave][0] + lane * 4;
+        *reinterpret_cast<f32x4*>(xw) = sp[0];
+        *reinterpret_cast<f32x4*>(xw + 64 * 4) = sp[1];
+        __syncthreads();
+        f32x4 sa[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) sa[tb] += *reinterpret_cast<const f32x4*>(xs[it & 1][w][tb] + lane * 4);
+        // mask; token of (tb, e) is 16 tb + 4 g + e
+        float mx = kNegInf;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int kk = 16 * tb + 4 * g + e;
+                const bool ok = row_ok && (tb == 0 ? ok0 : ok1) && pa * kPageM + kk < len;
+                sa[tb][e] = ok ? sa[tb][e] : kNegInf;
+                mx = fmaxf(mx, sa[tb][e]);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kTauL)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = exp2f_hw(m_run - (m_new == kNegInf ? 0.f : m_new));
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) oacc[i] *= alpha;
+        }
+        const float m_use = m_run == kNegInf ? 0.f : m_run;
+        u32x4 pw;
+        float rs = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const float a = exp2f_hw(fmaf(sa[tb][0], scale_log2, -m_use));
+            const float b = exp2f_hw(fmaf(sa[tb][1], scale_log2, -m_use));
+            const float c = exp2f_hw(fmaf(sa[tb][2], scale_log2, -m_use));
+            const float d = exp2f_hw(fmaf(sa[tb][3], scale_log2, -m_use));
+            rs += (a + b) + (c + d);
+            pw[2 * tb] = pack_bf16x2(a, b);
+            pw[2 * tb + 1] = pack_bf16x2(c, d);
+        }
+        l_run += rs;
+        // this wave's slice of sum_j p_hj c_j: O^T (latent x heads) += C^T P^T
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) oacc[blk] = mfma16(tr_op(tile, blk, lane), pb, oacc[blk]);
+    };
+
+    u32x4 crA[8], crB[8];
+    load_step(0, crA);
+    // keep the issue order (step 0 first): the loop waits only for the older
+    // of the two steps in flight, which the wait counts can express only if
+    // both paths into the loop issue the loads in the same order
+    __builtin_amdgcn_sched_barrier(0);
+    load_step(1, crB);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        split_bf16x8(row_ok ? qraw[2 * ks] : f32x4{}, row_ok ? qraw[2 * ks + 1] : f32x4{}, qh[ks], ql[ks]);
+    for (int it = 0; it < n_steps; it += 2) {
+        step(it, crA);
+        step(it + 1, crB);                                 // past the chunk: every token masked
+    }
+
+    // every wave holds the same (m, l) per head; output this wave's slice
+    float l_tot = l_run + __shfl_xor(l_run, 16);
+    l_tot += __shfl_xor(l_tot, 32);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+    if (!row_ok) return;
+    float* op;
+    if (nch <= 1) {
+        op = Olat + ((int64_t)s * H + head) * kDC + 128 * wave;
+        if (LSE != nullptr && wave == 0 && g == 0) LSE[(int64_t)s * H + head] = lse;
+    } else {
+        const int64_t slot = (int64_t)s * nchunk + chunk;
+        op = ws_o + (slot * Hp + head) * kDC + 128 * wave;
+        if (wave == 0 && g == 0) ws_lse[slot * Hp + head] = lse;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) *reinterpret_cast<f32x4*>(op + 16 * blk + 4 * g) = oacc[blk] * inv;
+}
+
+// ---- 3. merge the chunks of a sequence ----
+// Workgroup (sequence, head); thread t owns latent entries 4t .. 4t + 3 and
+// reads them from every chunk (one 2 KiB row per chunk, coalesced).
+constexpr int kThreadsC = kDC / 4;
+__global__ __launch_bounds__(kThreadsC) void mla_combine_kernel(const float* __restrict__ ws_o,
+                                                                const float* __restrict__ ws_lse,
+                                                                const int32_t* __restrict__ seqlens,
+                                                                float* __restrict__ Olat, float* __restrict__ LSE,
+                                                                int H, int Hp, int max_blocks, int nchunk) {
+    const int s = blockIdx.x, row = blockIdx.y;
+    const int len = min(max(seqlens[s], 0), max_blocks * kPageM);
+    const int nch = ((len + kPageM - 1) / kPageM + kChunkM - 1) / kChunkM;
+    if (nch <= 1) return;
+    const int t = threadIdx.x;
+    const int64_t slot0 = (int64_t)s * nchunk;
+    float M = kNegInf;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, ws_lse[(slot0 + c) * Hp + row]);
+    float L = 0.f;
+    f32x4 acc = f32x4{};
+#pragma unroll 4
+    for (int c = 0; c < nch; ++c) {
+        const float lc = ws_lse[(slot0 + c) * Hp + row];
+        const float w = M == kNegInf ? 0.f : exp2f_hw((lc - M) * kLog2e);
+        L += w;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + ((slot0 + c) * Hp + row) * kDC + 4 * t);
+        acc[0] = fmaf(w, v[0], acc[0]);
+        acc[1] = fmaf(w, v[1], acc[1]);
+        acc[2] = fmaf(w, v[2], acc[2]);
+        acc[3] = fmaf(w, v[3], acc[3]);
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<f32x4*>(Olat + ((int64_t)s * H + row) * kDC + 4 * t) =
+        f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    if (LSE != nullptr && t == 0) LSE[(int64_t)s * H + row] = L > 0.f ? M + log2f_hw(L) * kLn2 : kNegInf;
+}
+
+// ---- 4. up-projection: o[s, h, j] = sum_i W_V^T[h][j][i] olat[s, h, i] ----
+// Workgroup (h, 32 output dims, 32 sequences); wave w sums latent entries
+// 128 w .. 128 w + 127 (D[j][t] over its part of i, hi + lo products), and
+// the four partial tiles are added through LDS.
+__global__ __launch_bounds__(kThreadsL) void mla_upproj_kernel(const float* __restrict__ Olat,
+                                                               const uint16_t* __restrict__ WVT,
+                                                               uint16_t* __restrict__ O, int nseq, int H) {
+    __shared__ __attribute__((aligned(16))) float red[3][64 * 16];
+    const int h = blockIdx.x, j0 = 32 * blockIdx.y, s0 = blockIdx.z * 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int s = s0 + l32;
+    const float* lp = Olat + ((int64_t)min(s, nseq - 1) * H + h) * kDC + 128 * wave + 8 * hh;
+    const uint16_t* wp = WVT + ((int64_t)h * kDH + j0 + l32) * kDC + 128 * wave + 8 * hh;
+    f32x4 la[8], lb[8];
+    bf16x8 wa[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        la[k] = *reinterpret_cast<const f32x4*>(lp + 16 * k);
+        lb[k] = *reinterpret_cast<const f32x4*>(lp + 16 * k + 4);
+        wa[k] = *reinterpret_cast<const bf16x8*>(wp + 16 * k);
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        bf16x8 hi, lo;
+        split_bf16x8(la[k], lb[k], hi, lo);
+        acc = mfma32(wa[k], hi, acc);
+        acc = mfma32(wa[k], lo, acc);
+    }
+    if (wave > 0) {
+        float* r = red[wave - 1] + lane * 16;
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) *reinterpret_cast<f32x4*>(r + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
+    }
+    __syncthreads();
+    if (wave > 0 || s >= nseq) return;
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+        const float* r = red[w] + lane * 16;
+#pragma unroll
+        for (int q = 0; q < 16; q += 4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(r + q);
+            acc[q] += v[0];
+            acc[q + 1] += v[1];
+            acc[q + 2] += v[2];
+            acc[q + 3] += v[3];
+        }
+    }
+    uint16_t* out = O + ((int64_t)s * H + h) * kDH + j0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int j = 8 * a + 4 * hh;
+        *reinterpret_cast<u32x2*>(out + j) =
+            u32x2{pack_bf16x2(acc[4 * a], acc[4 * a + 1]), pack_bf16x2(acc[4 * a + 2], acc[4 * a + 3])};
+    }
+}
+
+struct MlaLayout {
+    size_t qa, olat, wo, wl, total;
+};
+
+int head_groups(int H) { return (H + kHG - 1) / kHG; }
+
+MlaLayout mla_layout(int nseq, int H, int max_blocks) {
+    const size_t nchunk = (size_t)(max_blocks + kChunkM - 1) / kChunkM;
+    const size_t Hp = (size_t)kHG * head_groups(H);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    MlaLayout L{};
+    L.qa = 0;
+    L.olat = up(L.qa + (size_t)nseq * H * kDC * 4);
+    L.wo = up(L.olat + (size_t)nseq * H * kDC * 4);
+    L.wl = up(L.wo + (size_t)nseq * nchunk * Hp * kDC * 4);
+    L.total = up(L.wl + (size_t)nseq * nchunk * Hp * 4);
+    return L;
+}
+
+}  // namespace
+
+size_t mla_workspace_bytes(int nseq, int H, int max_blocks) { return mla_layout(nseq, H, max_blocks).total; }
+
+hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t stream) {
+    const MlaLayout L = mla_layout(a.nseq, a.H, a.max_blocks);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    float* qa = reinterpret_cast<float*>(ws + L.qa);
+    float* olat = reinterpret_cast<float*>(ws + L.olat);
+    float* wo = reinterpret_cast<float*>(ws + L.wo);
+    float* wl = reinterpret_cast<float*>(ws + L.wl);
+    const int nchunk = (a.max_blocks + kChunkM - 1) / kChunkM;
+    const unsigned sblocks = (unsigned)((a.nseq + 31) / 32);
+    launch_kernel<false>(mla_absorb_kernel, dim3((unsigned)a.H, kDC / 128, sblocks), dim3(kThreadsL), 0, stream,
+                         (const uint16_t*)a.q, (const uint16_t*)a.w_uk, qa, a.nseq, a.H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int hg = head_groups(a.H);
+    launch_kernel<false>(mla_partial_kernel, dim3((unsigned)((int64_t)nchunk * a.nseq), (unsigned)hg), dim3(kThreadsL),
+                         0, stream, (const float*)qa, (const uint16_t*)a.ccache, a.block_table, a.seqlens, olat, a.lse,
+                         wo, wl, a.nseq, a.H, kHG * hg, a.max_blocks, a.num_blocks, nchunk, a.scale * kLog2e);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_kernel<false>(mla_combine_kernel, dim3((unsigned)a.nseq, (unsigned)a.H), dim3(kThreadsC), 0, stream, wo, wl,
+                         a.seqlens, olat, a.lse, a.H, kHG * hg, a.max_blocks, nchunk);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    launch_kernel(mla_upproj_kernel, dim3((unsigned)a.H, kDH / 32, sblocks), dim3(kThreadsL), 0, stream,
+                  (const float*)olat, (const uint16_t*)a.w_uv_t, (uint16_t*)a.o, a.nseq, a.H);
+    return hipGetLastError();
+}
+
+}  // namespace fa

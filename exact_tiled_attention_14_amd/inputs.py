@@ -339,6 +339,12 @@ class MLACase:
         return dict(nseq=nseq, H=H, d_h=dh, d_c=self.w_uk.shape[1], block_size=cs["block_size"],
                     num_blocks=cs["num_blocks"], max_blocks=cs["max_blocks"])
 
+    def subset(self, seqs) -> "MLACase":
+        """The listed sequences alone, their latent pages copied out and renumbered."""
+        seqs = [int(s) for s in seqs]
+        return MLACase(q=self.q[seqs].copy(), w_uk=self.w_uk, w_uv_t=self.w_uv_t, cache=self.cache.subset(seqs),
+                       scale=self.scale)
+
 
 def make_mla_decode(nseq: int, H: int, d_h: int, d_c: int, *, len_lo: int, len_hi: int, seed: int = 0,
                     seqlens: np.ndarray | None = None, poison_tail: bool = False) -> MLACase:

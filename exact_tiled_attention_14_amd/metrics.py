@@ -71,6 +71,28 @@ def decode_flops(seqlens, Hq: int, d: int) -> int:
     return int(np.asarray(seqlens, dtype=np.int64).sum()) * Hq * 4 * d
 
 
+def mla_latent_bytes(seqlens, d_c: int, elem_bytes: int = 2) -> int:
+    """Latent-cache bytes of the tokens attended to: one d_c-wide latent per
+    token, read once (it serves as the key and the value of every head)."""
+    return int(np.asarray(seqlens, dtype=np.int64).sum()) * d_c * elem_bytes
+
+
+def mla_total_bytes(seqlens, H: int, d_h: int, d_c: int, elem_bytes: int = 2) -> int:
+    """Minimum HBM bytes of one latent-cache decode step: the latents, both
+    up-projections once, the queries and the outputs (with lse)."""
+    n = len(seqlens)
+    return (mla_latent_bytes(seqlens, d_c, elem_bytes) + 2 * H * d_c * d_h * elem_bytes
+            + 2 * n * H * d_h * elem_bytes + n * H * 4)
+
+
+def mla_flops(seqlens, H: int, d_h: int, d_c: int) -> int:
+    """Algorithmic FLOPs of latent-cache decode in the absorbed form: per head
+    the query and output projections (2 d_c d_h each per sequence) and, per
+    attended token, the score and the weighted latent sum (2 d_c each)."""
+    n = len(seqlens)
+    return int(np.asarray(seqlens, dtype=np.int64).sum()) * H * 4 * d_c + n * H * 4 * d_c * d_h
+
+
 def decode_intensity(Hq: int, Hkv: int, elem_bytes: int = 2) -> float:
     """FLOP per KV byte of single-token decode: 4 d (Hq/Hkv) over 2 d elem_bytes."""
     return 4.0 * (Hq / Hkv) / (2.0 * elem_bytes)

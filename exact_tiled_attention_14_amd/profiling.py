@@ -38,6 +38,7 @@ COPY_KERNEL_HINT = "copyBuffer|elementwise|copy|fill"   # what the plain copy (a
 PREFILL = "causal_mha_b2_h16_s2048_d128"
 DECODE = "paged_decode_64seq_h32kv8_d128"
 VERIFY = "paged_verify_64seq_q8_h32kv8_d128"
+MLA = "mla_decode_64seq_h16_dc512"
 
 
 def source_sha256(path: str) -> str:
@@ -106,6 +107,20 @@ def _run(args) -> None:
                           dtype=torch.uint8, device=dev)
         launches.append(("verify", lambda: binding.fa_decode_multi(vq, vkc, vvc, vbt, vsl, cv.scale, out=vo, lse=vl,
                                                                    workspace=vws)))
+    if args.workload in ("mla", "all"):
+        cm = inputs.workload(MLA)
+        msh = cm.shape
+        mq, mwk, mwv = (to_dev(inputs.bf16_bits(x)) for x in (cm.q, cm.w_uk, cm.w_uv_t))
+        mcc = to_dev(cm.ccache_bits)
+        mbt = torch.from_numpy(cm.cache.block_table).to(dev)
+        msl = torch.from_numpy(cm.cache.seqlens).to(dev)
+        mo = torch.empty_like(mq)
+        ml = torch.empty((msh["nseq"], msh["H"]), dtype=torch.float32, device=dev)
+        mws = torch.empty(binding.fa_mla_decode_workspace_size(msh["nseq"], msh["H"], msh["d_h"], msh["d_c"],
+                                                               msh["block_size"], msh["max_blocks"]),
+                          dtype=torch.uint8, device=dev)
+        launches.append(("mla", lambda: binding.fa_mla_decode(mq, mwk, mwv, mcc, mbt, msl, cm.scale, out=mo, lse=ml,
+                                                              workspace=mws)))
     if args.workload in ("decode", "all"):
         d = inputs.workload(DECODE)
         s = d.shape
@@ -257,7 +272,7 @@ def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "verify", "all"], default="all")
+    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "verify", "mla", "all"], default="all")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--copy-mib", type=int, default=1024)
     s = sub.add_parser("summarize")

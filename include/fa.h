@@ -32,8 +32,17 @@
  *   - Arguments are validated on the host before anything is launched; a
  *     non-zero status means nothing was enqueued (except FA_ERR_HIP, which
  *     reports a launch failure).  No C++ exception crosses this boundary.
- *   - The library keeps no global mutable state; calls are re-entrant and
- *     calls on different streams may overlap.
+ *   - The library's only state is the per-thread timing setting of
+ *     fa_time_next_call, used by the next compute call on that thread;
+ *     otherwise calls are re-entrant and calls on different streams may
+ *     overlap.
+ *
+ * Entry points: fa_fwd (prefill, bf16 or fp32), fa_bwd (its gradients),
+ * fa_decode (one new token per sequence, paged cache), fa_decode_multi (Sq new
+ * tokens per sequence, paged cache), fa_mla_decode (one new token per
+ * sequence, paged latent cache), fa_quantize_fp8 and fa_fwd_fp8 (FP8
+ * forward with block scales), fa_time_next_call (measurement), plus the
+ * *_workspace_size / *_bytes size queries and fa_status_string.
  */
 #ifndef EXACT_TILED_ATTENTION_FA_H
 #define EXACT_TILED_ATTENTION_FA_H
@@ -221,6 +230,47 @@ int fa_decode_multi(const void* q, const void* kcache, const void* vcache, const
                     const int32_t* seqlens, void* o, float* lse, int nseq, int Sq, int Hq, int Hkv, int d,
                     int block_size, int max_blocks_per_seq, int num_blocks, float scale, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * fa_mla_decode_workspace_size - bytes of device scratch fa_mla_decode needs
+ * for these sizes (absorbed queries, the latent output and per-chunk partial
+ * results); 0 for invalid or unsupported arguments.
+ */
+size_t fa_mla_decode_workspace_size(int nseq, int H, int d_h, int d_c, int block_size, int max_blocks_per_seq);
+
+/*
+ * fa_mla_decode - one new query token per sequence against a paged cache of
+ * compressed latents (multi-head latent attention).
+ *
+ * Passage: "Fast Inference and Training at Scale", section 6.4 MLA (the cache
+ * holds only the latent c of each token; keys and values are rebuilt from it
+ * by learned up-projections), with 6.1 KV Caching and 6.3 PagedAttention.
+ *
+ *   q        [nseq, H, d_h] bf16: the new tokens' queries.
+ *   w_uk     [H, d_c, d_h] bf16: head h's keys are K_h = C w_uk[h].
+ *   w_uv_t   [H, d_h, d_c] bf16: head h's values are V_h = C w_uv_t[h]^T.
+ *   ccache   [num_blocks, block_size, d_c] bf16 latent pages.
+ *   block_table, seqlens, num_blocks: as for fa_decode (one cache "head").
+ *   o        [nseq, H, d_h] bf16 output; lse [nseq, H] fp32 natural-log
+ *            log-sum-exp of the scaled scores, or NULL.
+ *
+ * o[s, h] = softmax(scale q_h K_h^T) V_h over the seqlens[s] cached tokens;
+ * an empty sequence gives o = 0, lse = -inf.  The keys and values are never
+ * formed: the query is projected into the latent space (w_uk[h] q_h, kept
+ * in fp32), attention runs over the latents, and the latent result (fp32) is
+ * projected by w_uv_t[h]; products run on the matrix cores with fp32 sums,
+ * the two fp32 intermediates entering them as hi + lo bf16 pairs.
+ * Supported: d_h = 128, d_c = 512, block_size = 16, 1 <= H <= 128; otherwise
+ * FA_ERR_UNSUPPORTED.  Device values are made safe as in fa_decode.
+ * All tensors dense, 16-byte aligned (block_table, seqlens, lse 4-byte).
+ * Workspace: caller-owned, 256-byte aligned, >= fa_mla_decode_workspace_size
+ * bytes.  Runs on `stream`; allocates nothing.  Returns FA_OK or a negative
+ * fa_status.
+ */
+int fa_mla_decode(const void* q, const void* w_uk, const void* w_uv_t, const void* ccache,
+                  const int32_t* block_table, const int32_t* seqlens, void* o, float* lse, int nseq, int H,
+                  int d_h, int d_c, int block_size, int max_blocks_per_seq, int num_blocks, float scale,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * fa_quantize_fp8_bytes - bytes of the E4M3 codes fa_quantize_fp8 writes

@@ -30,8 +30,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
                            "fa_decode_multi_workspace_size", "fa_decode_workspace_size", "fa_fwd",
-                           "fa_fwd_fp8", "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string",
-                           "fa_time_next_call"]
+                           "fa_fwd_fp8", "fa_mla_decode", "fa_mla_decode_workspace_size", "fa_quantize_fp8",
+                           "fa_quantize_fp8_bytes", "fa_status_string", "fa_time_next_call"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -193,3 +193,33 @@ def test_decode_multi_workspace_size(lib):
     assert f(64, 8, 32, 8, 128, 16, 512) == 64 * 8 * 4 * 32 * 129 * 4
     assert f(1, 1, 1, 1, 128, 16, 1) == 256 * ((32 * 129 * 4 + 255) // 256)
     assert f(1, 1, 1, 1, 64, 16, 1) == 0 and f(1, 1, 1, 1, 128, 8, 1) == 0
+
+
+def _mla(lib, q=16, wk=32, wv=48, cc=64, bt=80, sl=96, o=112, lse=None, nseq=2, H=16, dh=128, dc=512, bs=16, mb=20,
+         nb=40, scale=0.1, ws=256, wsb=1 << 24):
+    P = ctypes.c_void_p
+    return lib.fa_mla_decode(P(q), P(wk), P(wv), P(cc), P(bt), P(sl), P(o), P(lse) if lse else None, nseq, H, dh,
+                             dc, bs, mb, nb, scale, P(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(wk=0), -1), (dict(wv=0), -1), (dict(cc=0), -1), (dict(bt=0), -1), (dict(o=0), -1),
+    (dict(H=0), -1), (dict(nb=0), -1), (dict(mb=0), -1), (dict(scale=float("nan")), -1), (dict(scale=-1.0), -1),
+    (dict(wv=40), -1), (dict(sl=98), -1), (dict(lse=114), -1),
+    (dict(dh=64), -2), (dict(dc=256), -2), (dict(bs=32), -2), (dict(H=129), -2),
+    (dict(ws=0), -3), (dict(wsb=16), -3), (dict(ws=272), -3),
+])
+def test_mla_decode_rejects_before_launch(lib, kw, status):
+    assert _mla(lib, **kw) == status
+
+
+def test_mla_decode_workspace_size(lib):
+    f = lib.fa_mla_decode_workspace_size
+    # absorbed queries and latent output (fp32, 512 per head), then per
+    # (sequence, 32-page chunk) one row of 512 floats and one lse per head,
+    # heads padded to a multiple of 16
+    assert f(64, 16, 128, 512, 16, 512) == 2 * 64 * 16 * 2048 + 64 * 16 * 16 * 2048 + 64 * 16 * 16 * 4
+    assert f(1, 1, 128, 512, 16, 1) == 2048 + 2048 + 16 * 2048 + 256
+    assert f(3, 40, 128, 512, 16, 65) == 2 * 3 * 40 * 2048 + 3 * 3 * 48 * 2048 + 256 * -(-3 * 3 * 48 * 4 // 256)
+    assert f(1, 129, 128, 512, 16, 1) == 0 and f(1, 1, 64, 512, 16, 1) == 0 and f(1, 1, 128, 512, 8, 1) == 0
+    assert f(0, 16, 128, 512, 16, 1) == 0
