@@ -254,8 +254,9 @@ int fa_mla_decode(const void* q, const void* w_uk, const void* w_uv_t, const voi
         (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return FA_ERR_INVALID_ARG;
     if (d_h != 128 || d_c != 512 || block_size != 16 || H > 128) return FA_ERR_UNSUPPORTED;
-    const int64_t nchunk = (max_blocks_per_seq + 31) / 32;
-    if (nchunk * nseq > INT32_MAX || nseq > 65535 * 32) return FA_ERR_UNSUPPORTED;
+    // work items of the partial kernel (grid x) and sequence blocks of the
+    // projections (grid z) stay within the launch limits
+    if ((int64_t)nseq * max_blocks_per_seq > INT32_MAX / 2 || nseq > 65535 * 32) return FA_ERR_UNSUPPORTED;
     const size_t need = fa_mla_decode_workspace_size(nseq, H, d_h, d_c, block_size, max_blocks_per_seq);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;

@@ -15,19 +15,28 @@
 // projected:
 //
 //   1. mla_absorb_kernel: q~ = W_K[h] q_h (fp32, d_c per head) for all
-//      sequences, on the matrix cores.
+//      sequences, on the matrix cores; one extra workgroup of the same launch
+//      splits the work of step 2 (below).
 //   2. mla_partial_kernel: attention of 16 absorbed queries (one head group)
-//      over the sequence's latents, per 32-page chunk of a sequence.  The
-//      four waves of a workgroup split the 512 latent dimensions into
-//      128-wide slices: each wave loads its slice of the chunk's latents
-//      (coalesced, two 32-token steps ahead, into registers, then its own
-//      LDS tile), computes its slice's part of the scores, and the four parts
-//      are summed through LDS, so every wave holds the full scores of the 16
-//      heads; each wave then accumulates its slice of sum_j p_hj c_j.  Online
-//      softmax as in the prefill kernel.  16 x 16 x 32 matrix-core products
+//      over a range of at most 64 pages of one sequence.  Per
+//      32-token step each wave loads 8 whole latent rows (1 KiB per load
+//      instruction, two steps ahead, into registers) and writes them to a
+//      workgroup tile in LDS kept as four 128-wide slices.  Wave w then
+//      computes slice w's part of the scores, the four parts are summed
+//      through LDS, so every wave holds the full scores of the 16 heads, and
+//      wave w accumulates slice w of sum_j p_hj c_j.  Online softmax as in
+//      the prefill kernel.  16 x 16 x 32 matrix-core products
 //      (16 tokens x 16 heads), so 16 heads fill the tile with no padding.
-//   3. mla_combine_kernel: merges the chunks of each sequence (log-sum-exp
+//   3. mla_combine_kernel: merges the parts of each sequence (log-sum-exp
 //      weights) into the normalised latent output (fp32).
+//
+// Work split: sequence lengths differ widely and live on the device, so the
+// scheduling workgroup sums the pages P of all sequences and cuts each
+// sequence into ceil(pages / t) near-equal parts, t = ceil(P / slots) pages
+// rounded up to even and capped at 64 (slots: workgroups of step 2 that stay
+// resident, less one per sequence for the rounding).  Every part then takes
+// about the same time and the whole grid runs in one wave; a sequence of one
+// part writes its final latent output directly.
 //   4. mla_upproj_kernel: o_h = (sum_j p_hj c_j) W_V[h] on the matrix cores.
 //
 // q~ and the latent output are intermediate results, not inputs: rounding
@@ -35,6 +44,9 @@
 // on top of what the plain path has.  Each is kept in fp32 and enters the
 // matrix cores as the sum of two bf16 terms (hi = bf16(x), lo = bf16(x - hi),
 // two products into one fp32 accumulator), which keeps it to about 2^-17.
+#include <algorithm>
+#include <atomic>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -44,9 +56,10 @@ namespace {
 constexpr int kDC = 512;                // latent width
 constexpr int kDH = 128;                // head dim
 constexpr int kPageM = 16;
-constexpr int kChunkM = 32;             // pages per workgroup of the partial kernel
+constexpr int kMaxPart = 64;            // pages per workgroup of the partial kernel, at most
 constexpr int kHG = 16;                 // heads per workgroup of the partial kernel
-static_assert(kChunkM <= 64, "a chunk's page ids fit one register across a wave's lanes");
+constexpr int kMaxSlots = 1024;         // resident partial workgroups assumed when sizing the workspace
+static_assert(kMaxPart <= 64, "a part's page ids fit one register across a wave's lanes");
 constexpr int kThreadsL = 256;
 constexpr float kTauL = 8.f;
 
@@ -101,13 +114,68 @@ __device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x
     lo = __builtin_bit_cast(bf16x8, l);
 }
 
+// ---- work split (one workgroup) ----
+// work[i] = (sequence, first page, end page, 0) for i < W, sequence -1 after;
+// part[s] = (first work index, number of parts) of sequence s.
+__device__ void mla_schedule(const int32_t* __restrict__ seqlens, int nseq, int max_blocks, int target, int wcap,
+                             int4* __restrict__ work, int2* __restrict__ part) {
+    __shared__ int64_t red[kThreadsL];
+    __shared__ int scan[kThreadsL];
+    const int tid = threadIdx.x;
+    auto pages_of = [&](int s) { return (min(max(seqlens[s], 0), max_blocks * kPageM) + kPageM - 1) / kPageM; };
+    int64_t local = 0;
+    for (int s = tid; s < nseq; s += kThreadsL) local += pages_of(s);
+    red[tid] = local;
+    __syncthreads();
+    for (int w = kThreadsL / 2; w > 0; w >>= 1) {
+        if (tid < w) red[tid] += red[tid + w];
+        __syncthreads();
+    }
+    const int64_t P = red[0];
+    int64_t t = (P + target - 1) / target;
+    t = min<int64_t>(kMaxPart, max<int64_t>(2, (t + 1) & ~(int64_t)1));
+    int base = 0;
+    for (int c0 = 0; c0 < nseq; c0 += kThreadsL) {
+        const int s = c0 + tid;
+        const int pg = s < nseq ? pages_of(s) : 0;
+        const int n = s < nseq ? max(1, (int)((pg + t - 1) / t)) : 0;
+        __syncthreads();                                  // the previous round's reads of scan[] are done
+        scan[tid] = n;
+        __syncthreads();
+        for (int w = 1; w < kThreadsL; w <<= 1) {         // inclusive scan
+            const int v = tid >= w ? scan[tid - w] : 0;
+            __syncthreads();
+            scan[tid] += v;
+            __syncthreads();
+        }
+        const int first = base + scan[tid] - n;
+        if (s < nseq) {
+            part[s] = int2{first, n};
+            const int steps = (pg + 1) / 2;               // parts cut at even pages (whole 32-token steps)
+            for (int k = 0; k < n; ++k) {
+                const int a0 = (int)((int64_t)k * steps / n), a1 = (int)((int64_t)(k + 1) * steps / n);
+                work[first + k] = int4{s, 2 * a0, min(2 * a1, pg), 0};
+            }
+        }
+        base += scan[kThreadsL - 1];
+    }
+    for (int i = base + tid; i < wcap; i += kThreadsL) work[i] = int4{-1, 0, 0, 0};
+}
+
 // ---- 1. absorbed queries: q~[s, h, :] = W_K[h] q[s, h] ----
 // Workgroup (h, 128 latent rows, 32 sequences); wave w computes 32 of the
 // rows: D[i][j] = sum_k W_K[h][i][k] q[s_j][h][k] (A = rows of W_K[h], B =
 // query rows), all loads issued before the 8 products.
 __global__ __launch_bounds__(kThreadsL) void mla_absorb_kernel(const uint16_t* __restrict__ Qin,
                                                                const uint16_t* __restrict__ WK,
-                                                               float* __restrict__ Qa, int nseq, int H) {
+                                                               float* __restrict__ Qa, int nseq, int H,
+                                                               const int32_t* __restrict__ seqlens, int max_blocks,
+                                                               int target, int wcap, int4* __restrict__ work,
+                                                               int2* __restrict__ part) {
+    if ((int)blockIdx.x == H) {                           // the scheduling workgroup
+        if (blockIdx.y == 0 && blockIdx.z == 0) mla_schedule(seqlens, nseq, max_blocks, target, wcap, work, part);
+        return;
+    }
     const int h = blockIdx.x, s0 = blockIdx.z * 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
@@ -134,23 +202,25 @@ __global__ __launch_bounds__(kThreadsL) void mla_absorb_kernel(const uint16_t* _
 // ---- 2. attention over the latents, one chunk of a sequence, 16 heads ----
 __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
     const float* __restrict__ Qa, const uint16_t* __restrict__ CC, const int32_t* __restrict__ table,
-    const int32_t* __restrict__ seqlens, float* __restrict__ Olat, float* __restrict__ LSE,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, int nseq, int H, int Hp, int max_blocks, int num_blocks,
-    int nchunk, float scale_log2) {
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[4][32 * 256];   // each wave's latent slice, 32 tokens
-    __shared__ __attribute__((aligned(16))) float xs[2][4][2][64 * 4];      // per-wave partial scores, by step parity
+    const int32_t* __restrict__ seqlens, const int4* __restrict__ work, const int2* __restrict__ part,
+    float* __restrict__ Olat, float* __restrict__ LSE, float* __restrict__ ws_o, float* __restrict__ ws_lse, int H,
+    int Hp, int max_blocks, int num_blocks, float scale_log2) {
+    // latent tile of a step, double buffered: [buffer][slice][32 tokens][256 B]
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][4][32 * 256];
+    __shared__ __attribute__((aligned(16))) float xs[4][2][64 * 4];      // per-wave partial scores
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, g = lane >> 4;
 
-    const int chunk = blockIdx.x / nseq, s = blockIdx.x % nseq;   // chunk-major
-    const int head = kHG * blockIdx.y + l16;                      // this lane's head (>= H: padding)
+    const int wi = blockIdx.x;
+    const int4 item = work[wi];                           // (sequence, first page, end page)
+    const int s = item.x;
+    if (s < 0) return;                                    // whole workgroup: no barrier reached
+    const int head = kHG * blockIdx.y + l16;              // this lane's head (>= H: padding)
     const int len = min(max(seqlens[s], 0), max_blocks * kPageM);
-    const int npages = (len + kPageM - 1) / kPageM;
-    const int nch = (npages + kChunkM - 1) / kChunkM;
-    if (chunk >= max(nch, 1)) return;                     // whole workgroup: no barrier reached
-    const int p0 = chunk * kChunkM, p1 = min(p0 + kChunkM, npages);
+    const int p0 = item.y, p1 = item.z;                   // p1 - p0 <= 64, p0 even
+    const int nparts = part[s].y;
     const int n_steps = (p1 - p0 + 1) / 2;                // 0 for an empty sequence
     const int32_t* trow = table + (int64_t)s * max_blocks;
     const int tb_lane = (p0 + lane < p1) ? trow[p0 + lane] : -1;   // the chunk's page ids, one per lane
@@ -174,19 +244,16 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
     }
     bf16x8 qh[4], ql[4];
 
-    uint8_t* const tile = tiles[wave];
-    // coalesced loads of this wave's slice of a step's 32 tokens: load c takes
-    // rows 4 (c % 4) + l / 16 of page c / 4, 16-byte chunk l % 16 of the
-    // slice.  Steps past the chunk read page 0 (never used).
+    // coalesced loads of a step's latent rows: wave w takes tokens 8 w .. +7
+    // (page pa + w / 2), one whole 1 KiB row per instruction, lane l bytes
+    // 16 l .. +15.  Steps past the chunk read page 0 (never used).
+    const int my_page = wave >> 1, my_row0 = 8 * (wave & 1);
     auto load_step = [&](int step, u32x4 (&cr)[8]) {
-        const int pa = p0 + 2 * step;
-        const int b0 = max(blk_of(pa), 0), b1 = max(blk_of(pa + 1), 0);
+        const int b = max(blk_of(p0 + 2 * step + my_page), 0);
+        const uint16_t* src = CC + ((int64_t)b * kPageM + my_row0) * kDC + 8 * lane;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int64_t row = (int64_t)(c < 4 ? b0 : b1) * kPageM + 4 * (c & 3) + (lane >> 4);
-            cr[c] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(CC + row * kDC + 128 * wave + 8 * (lane & 15)));
-        }
+        for (int j = 0; j < 8; ++j)
+            cr[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + j * kDC));
     };
 
     f32x4 oacc[8];
@@ -197,15 +264,22 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
     auto step = [&](int it, u32x4 (&cr)[8]) __attribute__((always_inline)) {
         const int pa = p0 + 2 * it;
         const bool ok0 = blk_of(pa) >= 0, ok1 = blk_of(pa + 1) >= 0;
-        // registers -> tile; rows of unusable tokens are zero (the tile also
-        // serves as the value operand, where p = 0 would not cancel a NaN)
+        // registers -> tile (this lane's 16 bytes belong to slice l / 16);
+        // rows of unusable tokens are zero (the tile also serves as the value
+        // operand, where p = 0 would not cancel a NaN).  The other buffer may
+        // still be read by waves finishing the previous step.
+        uint8_t* const tbuf = tiles[it & 1][0];
+        const bool okw = my_page == 0 ? ok0 : ok1;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            const int r = 4 * c + (lane >> 4), ch = lane & 15;
-            const bool bad = (r < 16 ? !ok0 : !ok1) || pa * kPageM + r >= len;
-            *reinterpret_cast<u32x4*>(tile + r * 256 + 16 * (ch ^ swz(r))) = bad ? u32x4{0u, 0u, 0u, 0u} : cr[c];
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * wave + j, ch = lane & 15;
+            const bool bad = !okw || pa * kPageM + r >= len;
+            *reinterpret_cast<u32x4*>(tbuf + (lane >> 4) * (32 * 256) + r * 256 + 16 * (ch ^ swz(r))) =
+                bad ? u32x4{0u, 0u, 0u, 0u} : cr[j];
         }
         load_step(it + 2, cr);                            // in flight for two steps
+        __syncthreads();                                  // the step's tile is complete
+        const uint8_t* const tile = tiles[it & 1][wave];
         // this wave's slice of the scores: S^T (16 tokens x 16 heads) per token block
         f32x4 sp[2];
 #pragma unroll
@@ -220,8 +294,9 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
                 sp[tb] = mfma16(ca, ql[ks], sp[tb]);
             }
         }
-        // sum the four slices through LDS (double buffered by step parity)
-        float* xw = xs[it & 1][wave][0] + lane * 4;
+        // sum the four slices through LDS (every wave has finished reading
+        // the previous step's sums: it passed the barrier above)
+        float* xw = xs[wave][0] + lane * 4;
         *reinterpret_cast<f32x4*>(xw) = sp[0];
         *reinterpret_cast<f32x4*>(xw + 64 * 4) = sp[1];
         __syncthreads();
@@ -229,7 +304,7 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
 #pragma unroll
         for (int w = 0; w < 4; ++w)
 #pragma unroll
-            for (int tb = 0; tb < 2; ++tb) sa[tb] += *reinterpret_cast<const f32x4*>(xs[it & 1][w][tb] + lane * 4);
+            for (int tb = 0; tb < 2; ++tb) sa[tb] += *reinterpret_cast<const f32x4*>(xs[w][tb] + lane * 4);
         // mask; token of (tb, e) is 16 tb + 4 g + e
         float mx = kNegInf;
 #pragma unroll
@@ -294,33 +369,32 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
     const float lse = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
     if (!row_ok) return;
     float* op;
-    if (nch <= 1) {
+    if (nparts <= 1) {
         op = Olat + ((int64_t)s * H + head) * kDC + 128 * wave;
         if (LSE != nullptr && wave == 0 && g == 0) LSE[(int64_t)s * H + head] = lse;
     } else {
-        const int64_t slot = (int64_t)s * nchunk + chunk;
-        op = ws_o + (slot * Hp + head) * kDC + 128 * wave;
-        if (wave == 0 && g == 0) ws_lse[slot * Hp + head] = lse;
+        op = ws_o + ((int64_t)wi * Hp + head) * kDC + 128 * wave;
+        if (wave == 0 && g == 0) ws_lse[(int64_t)wi * Hp + head] = lse;
     }
 #pragma unroll
     for (int blk = 0; blk < 8; ++blk) *reinterpret_cast<f32x4*>(op + 16 * blk + 4 * g) = oacc[blk] * inv;
 }
 
-// ---- 3. merge the chunks of a sequence ----
+// ---- 3. merge the parts of a sequence ----
 // Workgroup (sequence, head); thread t owns latent entries 4t .. 4t + 3 and
-// reads them from every chunk (one 2 KiB row per chunk, coalesced).
+// reads them from every part (one 2 KiB row per part, coalesced).
 constexpr int kThreadsC = kDC / 4;
 __global__ __launch_bounds__(kThreadsC) void mla_combine_kernel(const float* __restrict__ ws_o,
                                                                 const float* __restrict__ ws_lse,
-                                                                const int32_t* __restrict__ seqlens,
+                                                                const int2* __restrict__ part,
                                                                 float* __restrict__ Olat, float* __restrict__ LSE,
-                                                                int H, int Hp, int max_blocks, int nchunk) {
+                                                                int H, int Hp) {
     const int s = blockIdx.x, row = blockIdx.y;
-    const int len = min(max(seqlens[s], 0), max_blocks * kPageM);
-    const int nch = ((len + kPageM - 1) / kPageM + kChunkM - 1) / kChunkM;
+    const int2 pt = part[s];
+    const int nch = pt.y;
     if (nch <= 1) return;
     const int t = threadIdx.x;
-    const int64_t slot0 = (int64_t)s * nchunk;
+    const int64_t slot0 = pt.x;
     float M = kNegInf;
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ws_lse[(slot0 + c) * Hp + row]);
     float L = 0.f;
@@ -401,22 +475,46 @@ __global__ __launch_bounds__(kThreadsL) void mla_upproj_kernel(const float* __re
 }
 
 struct MlaLayout {
-    size_t qa, olat, wo, wl, total;
+    size_t qa, olat, work, part, wo, wl, total;
+    int64_t wcap;
 };
 
 int head_groups(int H) { return (H + kHG - 1) / kHG; }
 
+// Work items the partial kernel may be given: at most target + nseq (parts
+// of t >= P / target pages, one rounding per sequence) or, when t is capped,
+// P / 64 + nseq with P <= nseq * max_blocks.
+int64_t work_capacity(int nseq, int max_blocks, int64_t target) {
+    return std::max<int64_t>(target, ((int64_t)nseq * max_blocks + kMaxPart - 1) / kMaxPart) + nseq;
+}
+
 MlaLayout mla_layout(int nseq, int H, int max_blocks) {
-    const size_t nchunk = (size_t)(max_blocks + kChunkM - 1) / kChunkM;
     const size_t Hp = (size_t)kHG * head_groups(H);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     MlaLayout L{};
+    L.wcap = work_capacity(nseq, max_blocks, kMaxSlots);
     L.qa = 0;
     L.olat = up(L.qa + (size_t)nseq * H * kDC * 4);
-    L.wo = up(L.olat + (size_t)nseq * H * kDC * 4);
-    L.wl = up(L.wo + (size_t)nseq * nchunk * Hp * kDC * 4);
-    L.total = up(L.wl + (size_t)nseq * nchunk * Hp * 4);
+    L.work = up(L.olat + (size_t)nseq * H * kDC * 4);
+    L.part = up(L.work + (size_t)L.wcap * sizeof(int4));
+    L.wo = up(L.part + (size_t)nseq * sizeof(int2));
+    L.wl = up(L.wo + (size_t)L.wcap * Hp * kDC * 4);
+    L.total = up(L.wl + (size_t)L.wcap * Hp * 4);
     return L;
+}
+
+int device_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
@@ -428,22 +526,30 @@ hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t stre
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     float* qa = reinterpret_cast<float*>(ws + L.qa);
     float* olat = reinterpret_cast<float*>(ws + L.olat);
+    int4* work = reinterpret_cast<int4*>(ws + L.work);
+    int2* part = reinterpret_cast<int2*>(ws + L.part);
     float* wo = reinterpret_cast<float*>(ws + L.wo);
     float* wl = reinterpret_cast<float*>(ws + L.wl);
-    const int nchunk = (a.max_blocks + kChunkM - 1) / kChunkM;
+    const int hg = head_groups(a.H);
+    // two partial workgroups stay resident per CU; one part per slot, less
+    // one per sequence for the rounding of the parts
+    const int64_t slots = std::min<int64_t>(kMaxSlots, 2 * (int64_t)device_cus() / hg);
+    const int64_t target = std::max<int64_t>(1, slots - a.nseq);
+    const int64_t wcap = work_capacity(a.nseq, a.max_blocks, target);   // <= L.wcap: target <= kMaxSlots
     const unsigned sblocks = (unsigned)((a.nseq + 31) / 32);
-    launch_kernel<false>(mla_absorb_kernel, dim3((unsigned)a.H, kDC / 128, sblocks), dim3(kThreadsL), 0, stream,
-                         (const uint16_t*)a.q, (const uint16_t*)a.w_uk, qa, a.nseq, a.H);
+    launch_kernel<false>(mla_absorb_kernel, dim3((unsigned)a.H + 1, kDC / 128, sblocks), dim3(kThreadsL), 0, stream,
+                         (const uint16_t*)a.q, (const uint16_t*)a.w_uk, qa, a.nseq, a.H, a.seqlens, a.max_blocks,
+                         (int)target, (int)wcap, work, part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int hg = head_groups(a.H);
-    launch_kernel<false>(mla_partial_kernel, dim3((unsigned)((int64_t)nchunk * a.nseq), (unsigned)hg), dim3(kThreadsL),
-                         0, stream, (const float*)qa, (const uint16_t*)a.ccache, a.block_table, a.seqlens, olat, a.lse,
-                         wo, wl, a.nseq, a.H, kHG * hg, a.max_blocks, a.num_blocks, nchunk, a.scale * kLog2e);
+    launch_kernel<false>(mla_partial_kernel, dim3((unsigned)wcap, (unsigned)hg), dim3(kThreadsL), 0, stream,
+                         (const float*)qa, (const uint16_t*)a.ccache, a.block_table, a.seqlens, (const int4*)work,
+                         (const int2*)part, olat, a.lse, wo, wl, a.H, kHG * hg, a.max_blocks, a.num_blocks,
+                         a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_kernel<false>(mla_combine_kernel, dim3((unsigned)a.nseq, (unsigned)a.H), dim3(kThreadsC), 0, stream, wo, wl,
-                         a.seqlens, olat, a.lse, a.H, kHG * hg, a.max_blocks, nchunk);
+                         (const int2*)part, olat, a.lse, a.H, kHG * hg);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     launch_kernel(mla_upproj_kernel, dim3((unsigned)a.H, kDH / 32, sblocks), dim3(kThreadsL), 0, stream,

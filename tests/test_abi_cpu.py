@@ -215,11 +215,18 @@ def test_mla_decode_rejects_before_launch(lib, kw, status):
 
 def test_mla_decode_workspace_size(lib):
     f = lib.fa_mla_decode_workspace_size
-    # absorbed queries and latent output (fp32, 512 per head), then per
-    # (sequence, 32-page chunk) one row of 512 floats and one lse per head,
-    # heads padded to a multiple of 16
-    assert f(64, 16, 128, 512, 16, 512) == 2 * 64 * 16 * 2048 + 64 * 16 * 16 * 2048 + 64 * 16 * 16 * 4
-    assert f(1, 1, 128, 512, 16, 1) == 2048 + 2048 + 16 * 2048 + 256
-    assert f(3, 40, 128, 512, 16, 65) == 2 * 3 * 40 * 2048 + 3 * 3 * 48 * 2048 + 256 * -(-3 * 3 * 48 * 4 // 256)
+    # absorbed queries and latent output (fp32, 512 per head), the work list
+    # (16 B per item) and per-sequence part table (8 B), then per work item
+    # one row of 512 floats and one lse per head, heads padded to a multiple
+    # of 16.  Work items: at most max(1024, nseq * max_blocks / 64) + nseq.
+    up = lambda x: -(-x // 256) * 256
+    def size(nseq, H, mb):
+        wcap = max(1024, -(-nseq * mb // 64)) + nseq
+        hp = 16 * -(-H // 16)
+        return (up(nseq * H * 2048) * 2 + up(wcap * 16) + up(nseq * 8) + up(wcap * hp * 2048) + up(wcap * hp * 4))
+    assert f(64, 16, 128, 512, 16, 512) == size(64, 16, 512)
+    assert f(1, 1, 128, 512, 16, 1) == size(1, 1, 1)
+    assert f(3, 40, 128, 512, 16, 65) == size(3, 40, 65)
+    assert f(4096, 16, 128, 512, 16, 2048) == size(4096, 16, 2048)      # capped parts: nseq * max_blocks / 64
     assert f(1, 129, 128, 512, 16, 1) == 0 and f(1, 1, 64, 512, 16, 1) == 0 and f(1, 1, 128, 512, 8, 1) == 0
     assert f(0, 16, 128, 512, 16, 1) == 0

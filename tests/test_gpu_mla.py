@@ -86,6 +86,23 @@ def test_long_sequences_split_in_chunks(B, lens):
     check(o, lse, O, L, f"chunks {lens.tolist()}")
 
 
+def test_one_long_sequence_split_over_the_chip(B):
+    """40,000 tokens of one sequence: the work split cuts it into hundreds of
+    parts that the combine kernel merges."""
+    c = I.make_mla_decode(1, 16, 128, 512, len_lo=1, len_hi=40000, seed=5, seqlens=np.array([40000], np.int32))
+    o, lse = run(B, c)
+    O, L = ref(c)
+    check(o, lse, O, L, "one long sequence")
+
+
+def test_more_sequences_than_resident_workgroups(B):
+    """700 short sequences: one part each, more work items than stay resident."""
+    c = I.make_mla_decode(700, 16, 128, 512, len_lo=0, len_hi=90, seed=6)
+    o, lse = run(B, c)
+    O, L = ref(c)
+    check(o, lse, O, L, "700 sequences")
+
+
 def test_empty_sequence_and_bad_block_ids(B):
     lens = np.array([0, 40, 600], dtype=np.int32)
     c = I.make_mla_decode(3, 16, 128, 512, len_lo=1, len_hi=600, seed=9, seqlens=lens)
