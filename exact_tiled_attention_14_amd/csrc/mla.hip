@@ -119,36 +119,43 @@ __device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x
 // part[s] = (first work index, number of parts) of sequence s.
 __device__ void mla_schedule(const int32_t* __restrict__ seqlens, int nseq, int max_blocks, int target, int wcap,
                              int4* __restrict__ work, int2* __restrict__ part) {
-    __shared__ int64_t red[kThreadsL];
-    __shared__ int scan[kThreadsL];
-    const int tid = threadIdx.x;
+    constexpr int kW = kThreadsL / 64;
+    __shared__ int64_t wsum[kW];
+    __shared__ int wscan[2][kW];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     auto pages_of = [&](int s) { return (min(max(seqlens[s], 0), max_blocks * kPageM) + kPageM - 1) / kPageM; };
     int64_t local = 0;
     for (int s = tid; s < nseq; s += kThreadsL) local += pages_of(s);
-    red[tid] = local;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) local += __shfl_xor(local, o);
+    if (lane == 0) wsum[wave] = local;
     __syncthreads();
-    for (int w = kThreadsL / 2; w > 0; w >>= 1) {
-        if (tid < w) red[tid] += red[tid + w];
-        __syncthreads();
-    }
-    const int64_t P = red[0];
+    int64_t P = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) P += wsum[w];
     int64_t t = (P + target - 1) / target;
     t = min<int64_t>(kMaxPart, max<int64_t>(2, (t + 1) & ~(int64_t)1));
     int base = 0;
-    for (int c0 = 0; c0 < nseq; c0 += kThreadsL) {
+    for (int c0 = 0, round = 0; c0 < nseq; c0 += kThreadsL, round ^= 1) {
         const int s = c0 + tid;
         const int pg = s < nseq ? pages_of(s) : 0;
         const int n = s < nseq ? max(1, (int)((pg + t - 1) / t)) : 0;
-        __syncthreads();                                  // the previous round's reads of scan[] are done
-        scan[tid] = n;
-        __syncthreads();
-        for (int w = 1; w < kThreadsL; w <<= 1) {         // inclusive scan
-            const int v = tid >= w ? scan[tid - w] : 0;
-            __syncthreads();
-            scan[tid] += v;
-            __syncthreads();
+        int incl = n;                                     // inclusive scan within the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(incl, o);
+            if (lane >= o) incl += v;
         }
-        const int first = base + scan[tid] - n;
+        if (lane == 63) wscan[round][wave] = incl;        // alternate buffers: no barrier before the write
+        __syncthreads();
+        int before = base, total = 0;
+#pragma unroll
+        for (int w = 0; w < kW; ++w) {
+            const int v = wscan[round][w];
+            before += w < wave ? v : 0;
+            total += v;
+        }
+        const int first = before + incl - n;
         if (s < nseq) {
             part[s] = int2{first, n};
             const int steps = (pg + 1) / 2;               // parts cut at even pages (whole 32-token steps)
@@ -157,7 +164,7 @@ __device__ void mla_schedule(const int32_t* __restrict__ seqlens, int nseq, int 
                 work[first + k] = int4{s, 2 * a0, min(2 * a1, pg), 0};
             }
         }
-        base += scan[kThreadsL - 1];
+        base += total;
     }
     for (int i = base + tid; i < wcap; i += kThreadsL) work[i] = int4{-1, 0, 0, 0};
 }
