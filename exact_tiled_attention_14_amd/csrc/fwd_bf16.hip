@@ -137,8 +137,9 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const uint8_t* p) {
 
 // Scores of one 64-key block for this wave's 32 rows: S^T = K Q^T, the two
 // 32-key halves as interleaved MFMA chains, LDS operand reads one step ahead.
-// After MFMA step s the callback `between(s)` is emitted, so independent
-// vector work can be interleaved with the matrix-core work.
+// After each product k (k = 0 .. 2 NS - 1) the callback `between(k)` is
+// emitted, so independent vector work fills the matrix core's busy time
+// instead of waiting behind a second product.
 template <int D, typename F>
 __device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint8_t* kt, const bf16x8 (&qf)[D / 16],
                                             int l32, int hh, F&& between) {
@@ -151,20 +152,28 @@ __device__ __forceinline__ void score_block(f32x16 (&sacc)[2], const uint8_t* kt
     auto rd = [&](const uint8_t* r, int s) {
         return *reinterpret_cast<const bf16x8*>(r + 16 * ((2 * s + hh) ^ sw));
     };
-    bf16x8 ka[2][2];
+    // operands of step s in ring slot s % 3, read two steps ahead
+    bf16x8 ka[3][2];
     ka[0][0] = rd(kr0, 0);
     ka[0][1] = rd(kr1, 0);
+    if (NS > 1) {
+        ka[1][0] = rd(kr0, 1);
+        ka[1][1] = rd(kr1, 1);
+    }
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-        if (s + 1 < NS) {
-            ka[(s + 1) & 1][0] = rd(kr0, s + 1);
-            ka[(s + 1) & 1][1] = rd(kr1, s + 1);
+        if (s + 2 < NS) {
+            ka[(s + 2) % 3][0] = rd(kr0, s + 2);
+            ka[(s + 2) % 3][1] = rd(kr1, s + 2);
         }
         FA_FENCE();
-        sacc[0] = mfma32(ka[s & 1][0], qf[s], sacc[0]);
-        sacc[1] = mfma32(ka[s & 1][1], qf[s], sacc[1]);
+        sacc[0] = mfma32(ka[s % 3][0], qf[s], sacc[0]);
         FA_FENCE();
-        between(s);
+        between(2 * s);
+        FA_FENCE();
+        sacc[1] = mfma32(ka[s % 3][1], qf[s], sacc[1]);
+        FA_FENCE();
+        between(2 * s + 1);
         FA_FENCE();
     }
 }
@@ -337,63 +346,70 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (has_next2) dma_tile<D>(Kh, kbuf + (it & 1) * T::K_BYTES, k_lane_off, (it + 2) * kBN, Sk, wave);
         if (has_next) dma_tile<D>(Vh, vbuf + ((it + 1) & 1) * T::V_BYTES, v_lane_off, (it + 1) * kBN, Sk, wave);
 
-        // ---- phase X: scores of block it+1 on the matrix core, exponentials of block it ----
-        u32x4 pfw[4];
+        // ---- phase X: scores of block it+1 on the matrix core, exponentials of
+        // the first 32 keys of block it; phase Y: O^T += V_it^T P_it^T on the
+        // matrix core, exponentials of the other 32 keys (each one key step
+        // ahead of the product that takes them), then the maximum of block
+        // it+1.  One unit of vector work follows every product, so the matrix
+        // core and the vector unit overlap.
+        float pv[32];           // p of block it: value v is scur[v / 16][v % 16]
+        u32x4 pfw[4];           // P operand of key step ks: pfw[ks]
         float rs = 0.f;
-        auto exp_chunk = [&](int c) {    // 4 scores: block c/4, registers 4(c%4) .. +3
-            const int blk = c >> 2, r0 = 4 * (c & 3);
-            const float p0 = exp2f_hw(fmaf(scur[blk][r0 + 0], scale_log2, -m_use));
-            const float p1 = exp2f_hw(fmaf(scur[blk][r0 + 1], scale_log2, -m_use));
-            const float p2 = exp2f_hw(fmaf(scur[blk][r0 + 2], scale_log2, -m_use));
-            const float p3 = exp2f_hw(fmaf(scur[blk][r0 + 3], scale_log2, -m_use));
+        auto exp_unit = [&](int v) {
+            const int blk = v >> 4, r = v & 15;
+            pv[v] = exp2f_hw(fmaf(scur[blk][r], scale_log2, -m_use));
             // the running sum adds the fp32 values: rounding p to bf16 would
             // move a short row's lse by up to 2^-9
-            rs += (p0 + p1) + (p2 + p3);
-            const uint32_t w01 = pack_bf16x2(p0, p1), w23 = pack_bf16x2(p2, p3);
-            const int pk = 2 * blk + (r0 >> 3), pw = (r0 & 7) >> 1;
-            pfw[pk][pw] = w01;
-            pfw[pk][pw + 1] = w23;
+            rs += pv[v];
+            if (v & 1) pfw[2 * blk + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[v - 1], pv[v]);
         };
+        constexpr int XS = 2 * NS;          // products of phase X
         snxt[0] = f32x16{};
         snxt[1] = f32x16{};
         if (has_next) {
-            score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_BYTES, qf, l32, hh, [&](int s) {
+            score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_BYTES, qf, l32, hh, [&](int k) {
 #pragma unroll
-                for (int c = s * (8 / NS); c < (s + 1) * (8 / NS); ++c) exp_chunk(c);
+                for (int v = k * 16 / XS; v < (k + 1) * 16 / XS; ++v) exp_unit(v);
             });
         } else {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) exp_chunk(c);
+            for (int v = 0; v < 16; ++v) exp_unit(v);
         }
-        l_run += rs;
 
-        // ---- phase Y: O^T += V_it^T P_it^T on the matrix core, maximum of block it+1 ----
         if (has_next && needs_mask((it + 1) * kBN)) mask_block<CAUSAL>(snxt, (it + 1) * kBN, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
             const uint8_t* vt = vbuf + (it & 1) * T::V_BYTES;
-            bf16x8 va[2][NDB];
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) va[0][db] = vt_operand<D>(vt, 0, db, lane);
+            // V^T operands in product order j = ks NDB + db, read three products ahead
+            constexpr int NJ = 4 * NDB;
+            bf16x8 vr[4];
+            vr[0] = vt_operand<D>(vt, 0, 0, lane);
+            vr[1] = vt_operand<D>(vt, 1 / NDB, 1 % NDB, lane);
+            vr[2] = vt_operand<D>(vt, 2 / NDB, 2 % NDB, lane);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                if (ks + 1 < 4) {
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) va[(ks + 1) & 1][db] = vt_operand<D>(vt, ks + 1, db, lane);
-                }
-                FA_FENCE();
                 const bf16x8 pb = __builtin_bit_cast(bf16x8, pfw[ks]);
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) oacc[db] = mfma32(va[ks & 1][db], pb, oacc[db]);
-                FA_FENCE();
-                if (has_next) {
-                    const int blk = ks >> 1, r0 = 8 * (ks & 1);
+                for (int db = 0; db < NDB; ++db) {
+                    const int j = ks * NDB + db;
+                    if (j + 3 < NJ) vr[(j + 3) % 4] = vt_operand<D>(vt, (j + 3) / NDB, (j + 3) % NDB, lane);
+                    FA_FENCE();
+                    oacc[db] = mfma32(vr[j % 4], pb, oacc[db]);
+                    FA_FENCE();
+                    if (ks < 2) {
+                        // p of keys 32 + 16 ks .. +15 (P operand of key step ks + 2)
 #pragma unroll
-                    for (int r = r0; r < r0 + 8; ++r) mxn = fmaxf(mxn, snxt[blk][r]);
+                        for (int v = 16 + 8 * ks + db * 8 / NDB; v < 16 + 8 * ks + (db + 1) * 8 / NDB; ++v) exp_unit(v);
+                    } else if (has_next) {
+                        const int blk = ks - 2;
+#pragma unroll
+                        for (int r = db * 16 / NDB; r < (db + 1) * 16 / NDB; ++r) mxn = fmaxf(mxn, snxt[blk][r]);
+                    }
+                    FA_FENCE();
                 }
-                FA_FENCE();
             }
         }
+        l_run += rs;
         if (has_next) mx_cur = half_swap_max(mxn) * scale_log2;
 
         wait_dma();
