@@ -17,10 +17,12 @@ JSON's `host_lead` says whether it did).  The
 headline `value` is the algorithmic TFLOP/s of the causal prefill (4 d FLOP per
 visible query-key pair) over the prefill launch time; decode reports the
 algorithmic KV bytes (each attended token's K and V once) over the decode
-launch time.  Before each decode launch a 512 MiB buffer is written so that
+launch time.  Before each decode launch a 512 MiB buffer is read so that
 neither L2 nor the 256 MB Infinity Cache holds cache lines from the last step
 (outside the decode's own events); the prefill, which follows the previous
-step's decode, also starts from cold caches.  `traffic` is the HBM bytes per
+step's decode, also starts from cold caches.  The flush reads rather than
+writes: a write leaves the caches full of dirty lines whose write-back would
+be charged to the next timed kernel.  `traffic` is the HBM bytes per
 launch that the rocprofv3 counter passes summarised under profiles/ measured,
 reported only while the kernel source is the one they measured.  The fp64 CPU
 oracle is timed on the whole prefill workload, repeated until at least 10 s
@@ -148,7 +150,17 @@ def main():
     ws_bytes = binding.fa_decode_workspace_size(dshp["nseq"], dshp["Hq"], dshp["Hkv"], dshp["d"],
                                                 dshp["block_size"], dshp["max_blocks"])
     d_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Between timed calls the caches are flushed by READING a 512 MiB buffer:
+    # L2 and the 256 MB Infinity Cache then hold only clean lines of an
+    # unrelated buffer.  Writing the buffer instead would leave them full of
+    # dirty lines whose write-back the next kernel pays for (the prefill took
+    # 65-69 us after a 512 MiB fill against 57-60 us after a 512 MiB read and
+    # 55 us warm; the decode was the same after either).
+    flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def flush_caches():
+        flush_buf.sum()
+
     log("decode inputs ready")
 
     def run_f32():
@@ -167,7 +179,7 @@ def main():
     for _ in range(args.warmup):
         run_f32()
         run_prefill()
-        flush.fill_(1)
+        flush_caches()
         run_decode()
     torch.cuda.synchronize()
 
@@ -185,7 +197,7 @@ def main():
         run_f32()
         binding.fa_time_next_call(*e_p[i])
         run_prefill()
-        flush.fill_(i & 0xFF)
+        flush_caches()
         binding.fa_time_next_call(*e_d[i])
         run_decode()
     t_end.record(stream)
@@ -330,7 +342,7 @@ def main():
         lead = gpu_lead(stream, 2.0 + 0.5 * reps)
         host0 = time.perf_counter()
         for i in range(reps):
-            flush.fill_(i & 0xFF)        # cold caches, as in the step
+            flush_caches()        # cold caches, as in the step
             run_fp8(evs[i])
         host_s = time.perf_counter() - host0
         torch.cuda.synchronize()
@@ -383,7 +395,7 @@ def main():
         lead = gpu_lead(stream, 2.0 + 0.3 * reps)
         host0 = time.perf_counter()
         for i, (a, b) in enumerate(evs):
-            flush.fill_(i & 0xFF)
+            flush_caches()
             binding.fa_time_next_call(a, b)
             run_verify()
         host_s = time.perf_counter() - host0
@@ -398,7 +410,7 @@ def main():
             "algorithmic_kv_bytes_per_launch": vbytes, "kv_tokens": cv.kv_tokens,
             "flops_per_launch": metrics.decode_flops(cv.seqlens, vshp["Hq"], vshp["d"]) * vshp["Sq"],
             "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
-            "note": "caches flushed (512 MiB write) before each launch, outside its events",
+            "note": "caches flushed (512 MiB read) before each launch, outside its events",
             "host_lead": lead_report(lead, host_s),
         }
         log(f"verify: {st['mean']*1e3:.1f} us -> {gbs_v:.0f} GB/s")
@@ -432,7 +444,7 @@ def main():
         lead = gpu_lead(stream, 2.0 + 0.3 * reps)
         host0 = time.perf_counter()
         for i, (a, b) in enumerate(evs):
-            flush.fill_(i & 0xFF)
+            flush_caches()
             binding.fa_time_next_call(a, b)
             run_mla()
         host_s = time.perf_counter() - host0
@@ -451,7 +463,7 @@ def main():
             "flops_per_launch": metrics.mla_flops(cm.cache.seqlens, msh["H"], msh["d_h"], msh["d_c"]),
             "materialized_kv_bytes_equivalent": metrics.decode_kv_bytes(cm.cache.seqlens, msh["H"], msh["d_h"]),
             "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
-            "note": "achieved = latent bytes over the whole call (4 kernels); caches flushed (512 MiB write) "
+            "note": "achieved = latent bytes over the whole call (4 kernels); caches flushed (512 MiB read) "
                     "before each call, outside its events",
             "host_lead": lead_report(lead, host_s),
         }

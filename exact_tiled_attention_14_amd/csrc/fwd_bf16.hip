@@ -323,8 +323,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
     // One K/V block: `scur` holds this block's scores, `snxt` receives the next
     // block's.  The loop is unrolled by two so the buffers swap roles instead
-    // of being copied.
-    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2]) __attribute__((always_inline)) {
+    // of being copied.  The four LDS stages a step touches (K and V written by
+    // this step's global-to-LDS loads, K and V read as operands) are disjoint;
+    // passing them as restrict pointers tells the compiler so.  Without that
+    // it must assume the transposing V reads may see the loads just issued,
+    // and waits for all of them before the first P V product, which leaves
+    // only the score phase to hide their latency instead of the whole step.
+    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2], uint8_t* __restrict__ k_dma,
+                    uint8_t* __restrict__ v_dma, const uint8_t* __restrict__ k_rd,
+                    const uint8_t* __restrict__ v_rd) __attribute__((always_inline)) {
         const bool has_next = it + 1 < n_it;
         const bool has_next2 = it + 2 < n_it;
 
@@ -343,8 +350,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         // K_{it+2} into the K stage freed by block it, V_{it+1} into the V stage
         // freed by block it-1; both land while this block is computed.
-        if (has_next2) dma_tile<D>(Kh, kbuf + (it & 1) * T::K_BYTES, k_lane_off, (it + 2) * kBN, Sk, wave);
-        if (has_next) dma_tile<D>(Vh, vbuf + ((it + 1) & 1) * T::V_BYTES, v_lane_off, (it + 1) * kBN, Sk, wave);
+        if (has_next2) dma_tile<D>(Kh, k_dma, k_lane_off, (it + 2) * kBN, Sk, wave);
+        if (has_next) dma_tile<D>(Vh, v_dma, v_lane_off, (it + 1) * kBN, Sk, wave);
 
         // ---- phase X: scores of block it+1 on the matrix core, exponentials of
         // the first 32 keys of block it; phase Y: O^T += V_it^T P_it^T on the
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         snxt[0] = f32x16{};
         snxt[1] = f32x16{};
         if (has_next) {
-            score_block<D>(snxt, kbuf + ((it + 1) & 1) * T::K_BYTES, qf, l32, hh, [&](int k) {
+            score_block<D>(snxt, k_rd, qf, l32, hh, [&](int k) {
 #pragma unroll
                 for (int v = k * 16 / XS; v < (k + 1) * 16 / XS; ++v) exp_unit(v);
             });
@@ -379,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (has_next && needs_mask((it + 1) * kBN)) mask_block<CAUSAL>(snxt, (it + 1) * kBN, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
-            const uint8_t* vt = vbuf + (it & 1) * T::V_BYTES;
+            const uint8_t* vt = v_rd;
             // V^T operands in product order j = ks NDB + db, read three products ahead
             constexpr int NJ = 4 * NDB;
             bf16x8 vr[4];
@@ -417,8 +424,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     };
     f32x16 s1[2];
     for (int it = 0; it < n_it; it += 2) {
-        step(it, s0, s1);
-        if (it + 1 < n_it) step(it + 1, s1, s0);
+        // even block: K_{it+2} -> K stage 0, V_{it+1} -> V stage 1; reads K stage 1, V stage 0
+        step(it, s0, s1, kbuf, vbuf + T::V_BYTES, kbuf + T::K_BYTES, vbuf);
+        if (it + 1 < n_it) step(it + 1, s1, s0, kbuf + T::K_BYTES, vbuf, kbuf, vbuf + T::V_BYTES);
     }
 
     // ---- epilogue: one division per row, bf16 output, natural-log lse ----

@@ -230,6 +230,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
 
     const int k_lane_off = k8_lane_offset(wave, lane);
     const int v_lane_off = v8_lane_offset(wave, lane);
+    // Block scales used by a step are loaded one step earlier (the first ones
+    // here, ahead of the prologue's wait): a load issued in the step itself
+    // would sit behind that step's global-to-LDS loads in the memory counter,
+    // so waiting for it would wait for them too.
+    const int sk0 = KSh[0];
+    int sk_pref = KSh[min(1, n_kblk - 1)];   // K scale of block it + 1
+    int sv_pref = VSh[0];                    // V scale of block it
     if (n_it > 0) {
         dma_k8(Kh, kbuf, k_lane_off, 0, Sk, wave);
         dma_v8(Vh, vbuf, v_lane_off, wave);
@@ -241,7 +248,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     f32x16 s0[2] = {f32x16{}, f32x16{}};
     float mx_cur = kNegInf;
     if (n_it > 0) {
-        score(s0, kbuf, KSh[0], [](int) {});
+        score(s0, kbuf, sk0, [](int) {});
         if (needs_mask(0)) mask_block8<CAUSAL>(s0, 0, Sk, my_q, diag, hh);
         float mx = kNegInf;
 #pragma unroll
@@ -253,7 +260,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     __syncthreads();
 
     const int sw_v = swz_v8(l32);   // rows 32 db + l32 share it (period 32)
-    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2]) __attribute__((always_inline)) {
+    // The LDS stages a step writes (global-to-LDS loads of K_{it+2}, V_{it+1})
+    // and reads (K_{it+1}, V_it) are disjoint; as restrict pointers the
+    // compiler knows it, and does not wait for the loads just issued before
+    // the first operand read of the step.
+    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2], uint8_t* __restrict__ k_dma,
+                    uint8_t* __restrict__ v_dma, const uint8_t* __restrict__ k_rd,
+                    const uint8_t* __restrict__ v_rd) __attribute__((always_inline)) {
         const bool has_next = it + 1 < n_it;
         const bool has_next2 = it + 2 < n_it;
 
@@ -266,11 +279,13 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
             for (int i = 0; i < 4; ++i) oacc[i] *= alpha;
         }
         const float m_use = m_run == kNegInf ? 0.f : m_run;
-        const int sv = VSh[it];
-        const int sk_next = has_next ? (int)KSh[it + 1] : 127;
+        const int sv = sv_pref;
+        const int sk_next = has_next ? sk_pref : 127;
+        sk_pref = KSh[min(it + 2, n_kblk - 1)];
+        sv_pref = VSh[min(it + 1, n_kblk - 1)];
 
-        if (has_next2) dma_k8(Kh, kbuf + (it & 1) * kTile8, k_lane_off, (it + 2) * kBN8, Sk, wave);
-        if (has_next) dma_v8(Vh + (int64_t)(it + 1) * kTile8, vbuf + ((it + 1) & 1) * kTile8, v_lane_off, wave);
+        if (has_next2) dma_k8(Kh, k_dma, k_lane_off, (it + 2) * kBN8, Sk, wave);
+        if (has_next) dma_v8(Vh + (int64_t)(it + 1) * kTile8, v_dma, v_lane_off, wave);
 
         // ---- phase X: scores of block it+1, exponentials of block it ----
         int pw[8];
@@ -288,7 +303,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         snxt[0] = f32x16{};
         snxt[1] = f32x16{};
         if (has_next) {
-            score(snxt, kbuf + ((it + 1) & 1) * kTile8, sk_next, [&](int i) {
+            score(snxt, k_rd, sk_next, [&](int i) {
                 exp_chunk(2 * i);
                 exp_chunk(2 * i + 1);
             });
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         if (has_next && needs_mask((it + 1) * kBN8)) mask_block8<CAUSAL>(snxt, (it + 1) * kBN8, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
-            const uint8_t* vt = vbuf + (it & 1) * kTile8 + l32 * 64;
+            const uint8_t* vt = v_rd + l32 * 64;
             const i32x8 pb = {pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[6], pw[7]};
             i32x8 va[2];
             va[0] = read32(vt, 2 * hh, sw_v);
@@ -327,8 +342,8 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     };
     f32x16 s1[2];
     for (int it = 0; it < n_it; it += 2) {
-        step(it, s0, s1);
-        if (it + 1 < n_it) step(it + 1, s1, s0);
+        step(it, s0, s1, kbuf, vbuf + kTile8, kbuf + kTile8, vbuf);
+        if (it + 1 < n_it) step(it + 1, s1, s0, kbuf + kTile8, vbuf, kbuf, vbuf + kTile8);
     }
 
     const float l_tot = half_swap_sum(l_run);
