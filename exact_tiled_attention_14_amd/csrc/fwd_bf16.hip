@@ -430,22 +430,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
 
     // ---- epilogue: one division per row, bf16 output, natural-log lse ----
+    // Each wave's 32 x D output tile passes through its own slice of LDS (free
+    // after the loop's last barrier), so that every global store instruction
+    // writes whole consecutive rows (1 KiB) instead of 16-byte pieces of 32
+    // rows.  16-byte chunks are XOR-swizzled by row for conflict-free LDS
+    // writes and reads.
     const float l_tot = half_swap_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_q < Sq) {
-        uint16_t* op = O + q_off + (int64_t)my_q * D;
+    {
+        constexpr int CH = D / 8;                 // 16-byte chunks per row
+        constexpr int RPP = 64 / CH;              // rows per wave-wide 16-byte pass
+        uint8_t* const ot = lds + wave * 32 * T::ROWB;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int d0 = 32 * db + 8 * a + 4 * hh;
+                const int c = 4 * db + a;         // chunk of head-dim columns 32 db + 8 a .. +7
                 const u32x2 w = {pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv),
                                  pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + d0) = w;
+                *reinterpret_cast<u32x2*>(ot + l32 * T::ROWB + 16 * (c ^ (l32 & (CH - 1))) + 8 * hh) = w;
             }
-        if (LSE != nullptr && hh == 0)
-            LSE[((int64_t)b * Hq + hq) * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+        __syncthreads();
+        const int rr = lane / CH, cc = lane % CH;
+#pragma unroll
+        for (int i = 0; i < 32 / RPP; ++i) {
+            const int r = i * RPP + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * T::ROWB + 16 * (cc ^ (r & (CH - 1))));
+            if (qw + r < Sq) *reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc) = v;
+        }
     }
+    if (LSE != nullptr && hh == 0 && my_q < Sq)
+        LSE[((int64_t)b * Hq + hq) * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
 }
 
 int num_cus() {
