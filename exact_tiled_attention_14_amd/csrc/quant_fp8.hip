@@ -80,39 +80,66 @@ __global__ __launch_bounds__(kQThreads) void quant_rows_kernel(const uint16_t* _
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
 
-    // stage R (or the identity) once; 16-byte chunk c of row n sits at
-    // chunk c ^ (n % 16), so the operand reads (32 rows, one chunk) spread
-    // over all banks
-    for (int c = tid; c < kQD * kQD / 8; c += kQThreads) {
-        const int n = c / (kQD / 8), ch = c % (kQD / 8);
-        u32x4 v;
-        if (rot != nullptr) {
-            v = *reinterpret_cast<const u32x4*>(rot + n * kQD + 8 * ch);
-        } else {
+    const int rsub = wave % (R / 32);          // this wave's 32-row slice of the block
+    const int nb0 = (wave / (R / 32)) * NB;    // its first column block
+    // this lane's operands of block blk (its row of the slice), loaded one
+    // block ahead so that the loads of the next block overlap this one
+    bf16x8 xn[kQD / 16];
+    auto load_x = [&](int64_t blk) {
+        const int64_t bh = blk / nblk;
+        const int row = (int)(blk % nblk) * R + rsub * 32 + l32;
+        const uint16_t* xr = X + (bh * S + min(row, S - 1)) * kQD + 8 * hh;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int k0 = 8 * ch + 2 * i;
-                v[i] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
+        for (int s = 0; s < kQD / 16; ++s) xn[s] = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
+    };
+    if (blockIdx.x < total) load_x(blockIdx.x);
+
+    // stage R (or the identity) once, all loads in flight together; 16-byte
+    // chunk c of row n sits at chunk c ^ (n % 16), so the operand reads (32
+    // rows, one chunk) spread over all banks
+    constexpr int NST = kQD * kQD / 8 / kQThreads;
+    static_assert(NST * kQThreads * 8 == kQD * kQD, "staging split");
+    u32x4 rv[NST];
+    if (rot != nullptr) {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int c = tid + kQThreads * i;
+            rv[i] = *reinterpret_cast<const u32x4*>(rot + (c / (kQD / 8)) * kQD + 8 * (c % (kQD / 8)));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int c = tid + kQThreads * i;
+            const int n = c / (kQD / 8), ch = c % (kQD / 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int k0 = 8 * ch + 2 * k;
+                rv[i][k] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
             }
         }
-        *reinterpret_cast<u32x4*>(rt + n * kQD + 8 * (ch ^ (n & 15))) = v;
+    }
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+        const int c = tid + kQThreads * i;
+        const int n = c / (kQD / 8), ch = c % (kQD / 8);
+        *reinterpret_cast<u32x4*>(rt + n * kQD + 8 * (ch ^ (n & 15))) = rv[i];
     }
     __syncthreads();
 
-    const int rsub = wave % (R / 32);          // this wave's 32-row slice of the block
-    const int nb0 = (wave / (R / 32)) * NB;    // its first column block
     for (int64_t blk = blockIdx.x; blk < total; blk += gridDim.x) {
         const int64_t bh = blk / nblk;
         const int j = (int)(blk % nblk);
         const int row = j * R + rsub * 32 + l32;   // this lane's row of the slice
-        const uint16_t* xr = X + (bh * S + min(row, S - 1)) * kQD + 8 * hh;
+        bf16x8 xc[kQD / 16];
+#pragma unroll
+        for (int s = 0; s < kQD / 16; ++s) xc[s] = row < S ? xn[s] : bf16x8{};
+        if (blk + gridDim.x < total) load_x(blk + gridDim.x);
         f32x16 acc[NB];
 #pragma unroll
         for (int i = 0; i < NB; ++i) acc[i] = f32x16{};
 #pragma unroll
         for (int s = 0; s < kQD / 16; ++s) {
-            bf16x8 xb = *reinterpret_cast<const bf16x8*>(xr + 16 * s);
-            if (row >= S) xb = bf16x8{};
+            const bf16x8 xb = xc[s];
 #pragma unroll
             for (int i = 0; i < NB; ++i) {
                 const int n = 32 * (nb0 + i) + l32;
