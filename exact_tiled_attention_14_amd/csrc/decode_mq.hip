@@ -301,11 +301,14 @@ __global__ __launch_bounds__(kThreadsM) void mq_combine_kernel(const float* __re
     const int row = tid >> 3, c0 = 16 * (tid & 7);
     if (row >= G * Sq) return;
     const int64_t slot0 = ((int64_t)s * Hkv + kvh) * nchunk;
+    // (unrolled so that the reads of several chunks are in flight together)
     float M = kNegInf;
+#pragma unroll 4
     for (int c = 0; c < nch; ++c) M = fmaxf(M, ws_lse[(slot0 + c) * 32 + row]);
     float acc[16], L = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll 4
     for (int c = 0; c < nch; ++c) {
         const float lc = ws_lse[(slot0 + c) * 32 + row];
         const float w = M == kNegInf ? 0.f : exp2f_hw((lc - M) * kLog2e);

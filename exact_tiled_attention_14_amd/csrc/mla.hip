@@ -402,11 +402,20 @@ __global__ __launch_bounds__(kThreadsC) void mla_combine_kernel(const float* __r
     if (nch <= 1) return;
     const int t = threadIdx.x;
     const int64_t slot0 = pt.x;
+    // the parts' maximum lse: each thread reads every kThreadsC-th part, so all
+    // reads are in flight at once, then a reduction over the workgroup
+    __shared__ float s_red[kThreadsC / 64];
     float M = kNegInf;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, ws_lse[(slot0 + c) * Hp + row]);
+    for (int c = t; c < nch; c += kThreadsC) M = fmaxf(M, ws_lse[(slot0 + c) * Hp + row]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    if ((t & 63) == 0) s_red[t >> 6] = M;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kThreadsC / 64; ++w) M = fmaxf(M, s_red[w]);
     float L = 0.f;
     f32x4 acc = f32x4{};
-#pragma unroll 4
+#pragma unroll 8
     for (int c = 0; c < nch; ++c) {
         const float lc = ws_lse[(slot0 + c) * Hp + row];
         const float w = M == kNegInf ? 0.f : exp2f_hw((lc - M) * kLog2e);
