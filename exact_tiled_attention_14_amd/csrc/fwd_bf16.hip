@@ -214,30 +214,63 @@ __device__ __forceinline__ void mask_block(f32x16 (&sacc)[2], int kv0, int Sk, i
         }
 }
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
+// Barrier of the four waves of one wave group, through a counter in LDS:
+// each wave adds 1 on arrival and leaves once all four have arrived for this
+// round (the counter grows by 4 per round; `target` is the wave's running
+// round total).  The wait is bounded, so no wave can spin forever.
+__device__ __forceinline__ void group_barrier(uint8_t* ctr_p, int& target, int lane) {
+    int* const ctr = reinterpret_cast<int*>(ctr_p);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    target += kWaves;
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (c >= target) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+template <int D, bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk,
-    float scale_log2, int n_qblk, int xcd_groups, int mirror) {
+    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror) {
     using T = Tile<D>;
     constexpr int NS = D / 16;          // MFMA steps of one score block
     constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * T::K_BYTES + 2 * T::V_BYTES];
-    uint8_t* const kbuf = lds;                      // K stages 0, 1
-    uint8_t* const vbuf = lds + 2 * T::K_BYTES;     // V stages 0, 1
+    constexpr int GROUP_LDS = 2 * T::K_BYTES + 2 * T::V_BYTES;
+    // pair mode: two wave groups, each with its own K/V stages, plus their barrier counters
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[PAIR ? 2 * GROUP_LDS + 64 : GROUP_LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
+    const int grp = PAIR ? wave_id / kWaves : 0;                  // wave group (pair mode: 0 = A, 1 = B)
+    const int wave = PAIR ? wave_id % kWaves : wave_id;           // row slice and load slice in the group
+    uint8_t* const kbuf = lds + grp * GROUP_LDS;                  // K stages 0, 1
+    uint8_t* const vbuf = kbuf + 2 * T::K_BYTES;                  // V stages 0, 1
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int g = Hq / Hkv;
+    int bar_target = 0;
+    if constexpr (PAIR) {
+        if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
+        __syncthreads();
+    }
+    // barrier of the threads that share this workgroup's (or wave group's) K/V stages
+    auto gsync = [&]() __attribute__((always_inline)) {
+        if constexpr (PAIR) {
+            group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane);
+        } else {
+            __syncthreads();
+        }
+    };
 
-    // ---- which (batch, head, query block) this workgroup owns ----
-    int b, hq, kvh, qb;
+    // ---- which (batch, head) and rank this workgroup owns ----
+    int b, hq, kvh, rank;
     {
         const int w = blockIdx.x;
-        int rank;
         if (xcd_groups) {
             // 8 XCDs receive workgroups round-robin; keep each K/V head on one XCD.
             const int xcd = w & 7, j = w >> 3;
@@ -257,22 +290,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             kvh = hq / g;
         }
         // second half of a grid that is resident all at once: reverse order
-        if (mirror && rank >= (n_qblk + 1) / 2) rank = n_qblk - 1 - (rank - (n_qblk + 1) / 2);
-        qb = CAUSAL ? n_qblk - 1 - rank : rank;
+        if (mirror && rank >= (n_rank + 1) / 2) rank = n_rank - 1 - (rank - (n_rank + 1) / 2);
     }
 
     const int64_t q_off = ((int64_t)b * Hq + hq) * Sq * D;
-    const int64_t kv_off = ((int64_t)b * Hkv + kvh) * Sk * D;
+    const int diag = Sk - Sq;           // key j visible to row i iff j <= i + diag
+    f32x16 oacc[NDB];
+    float m_run, l_run;                 // reference maximum of scale*log2(e)*s; this lane's share of the row sum
+
+    // ---- epilogue of a query block: one division per row, bf16 output,
+    // natural-log lse ----
+    // Each wave's 32 x D output tile passes through its own slice of LDS (free
+    // after the loop's last barrier), so that every global store instruction
+    // writes whole consecutive rows (1 KiB) instead of 16-byte pieces of 32
+    // rows.  16-byte chunks are XOR-swizzled by row for conflict-free LDS
+    // writes and reads.
+    auto write_out = [&](const int qb) __attribute__((always_inline)) {
+        const int qw = qb * kBM + wave * 32;
+        int ln = lane;
+        if constexpr (PAIR) asm volatile("" : "+v"(ln));   // staging addresses formed here (see run_job)
+        const int l32 = ln & 31, hh = ln >> 5;
+        const int my_q = qw + l32;
+        const float l_tot = half_swap_sum(l_run);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        constexpr int CH = D / 8;                 // 16-byte chunks per row
+        constexpr int RPP = 64 / CH;              // rows per wave-wide 16-byte pass
+        uint8_t* const ot = kbuf + wave * 32 * T::ROWB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int c = 4 * db + a;         // chunk of head-dim columns 32 db + 8 a .. +7
+                const u32x2 w = {pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv),
+                                 pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
+                *reinterpret_cast<u32x2*>(ot + l32 * T::ROWB + 16 * (c ^ (l32 & (CH - 1))) + 8 * hh) = w;
+            }
+        gsync();
+        const int rr = ln / CH, cc = ln % CH;
+#pragma unroll
+        for (int r8 = 0; r8 < 32 / RPP; ++r8) {
+            const int r = r8 * RPP + rr;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * T::ROWB + 16 * (cc ^ (r & (CH - 1))));
+            if (qw + r < Sq) *reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc) = v;
+        }
+        if (LSE != nullptr && hh == 0 && my_q < Sq)
+            LSE[((int64_t)b * Hq + hq) * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+    };
+
+    // One job: query block qb against K/V blocks [kb0, kb1); with `final` the
+    // output of the block is written, else the state stays in oacc/m_run/l_run.
+    auto run_job = [&](const int qb, const int kb0, const int kb1, const bool final) __attribute__((always_inline)) {
+    // (empty asm statements: the per-lane addresses are formed inside each job,
+    // not kept live, and spilled, across the other job of a pair workgroup)
+    int64_t kv_off = ((int64_t)b * Hkv + kvh) * Sk * D;
+    int k_lane_off = dma_lane_offset<D, true>(wave, lane);
+    int v_lane_off = dma_lane_offset<D, false>(wave, lane);
+    if constexpr (PAIR) {
+        asm volatile("" : "+s"(kv_off));
+        asm volatile("" : "+v"(k_lane_off), "+v"(v_lane_off));
+    }
     const uint16_t* Kh = K + kv_off;
     const uint16_t* Vh = V + kv_off;
     const int q0 = qb * kBM;
     const int qw = q0 + wave * 32;      // first query row of this wave
     const int my_q = qw + l32;          // the query row this lane's scores belong to
-    const int diag = Sk - Sq;           // key j visible to row i iff j <= i + diag
-
-    int kv_end = Sk;
-    if (CAUSAL) kv_end = min(Sk, max(0, q0 + kBM + diag));
-    const int n_it = (kv_end + kBN - 1) / kBN;
+    const int n_it = kb1 - kb0;         // K/V blocks of this job
 
     // Q fragment, the B operand of S^T = K Q^T: 8 contiguous head-dim elements per step.
     bf16x8 qf[NS];
@@ -285,31 +367,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         }
     }
 
-    f32x16 oacc[NDB];
 #pragma unroll
     for (int i = 0; i < NDB; ++i) oacc[i] = f32x16{};
-    float m_run = kNegInf;   // reference maximum of scale*log2(e)*s for this row
-    float l_run = 0.f;       // running sum of this lane's share of the row
+    m_run = kNegInf;
+    l_run = 0.f;
 
     // a block needs the elementwise mask if it runs past Sk or crosses this wave's diagonal
     auto needs_mask = [&](int kv0) { return (kv0 + kBN > Sk) || (CAUSAL && kv0 + kBN - 1 > qw + diag); };
 
-    // ---- prologue: K_0, V_0, K_1 into LDS; scores of block 0 ----
-    const int k_lane_off = dma_lane_offset<D, true>(wave, lane);
-    const int v_lane_off = dma_lane_offset<D, false>(wave, lane);
+    // ---- prologue: K_kb0, V_kb0, K_kb0+1 into LDS; scores of block kb0 ----
     if (n_it > 0) {
-        dma_tile<D>(Kh, kbuf, k_lane_off, 0, Sk, wave);
-        dma_tile<D>(Vh, vbuf, v_lane_off, 0, Sk, wave);
+        dma_tile<D>(Kh, kbuf, k_lane_off, kb0 * kBN, Sk, wave);
+        dma_tile<D>(Vh, vbuf, v_lane_off, kb0 * kBN, Sk, wave);
     }
-    if (n_it > 1) dma_tile<D>(Kh, kbuf + T::K_BYTES, k_lane_off, kBN, Sk, wave);
+    if (n_it > 1) dma_tile<D>(Kh, kbuf + T::K_BYTES, k_lane_off, (kb0 + 1) * kBN, Sk, wave);
     wait_dma();
-    __syncthreads();
+    gsync();
 
     f32x16 s0[2] = {f32x16{}, f32x16{}};
     float mx_cur = kNegInf;
     if (n_it > 0) {
         score_block<D>(s0, kbuf, qf, l32, hh, [](int) {});
-        if (needs_mask(0)) mask_block<CAUSAL>(s0, 0, Sk, my_q, diag, hh);
+        if (needs_mask(kb0 * kBN)) mask_block<CAUSAL>(s0, kb0 * kBN, Sk, my_q, diag, hh);
         float mx = kNegInf;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -319,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
     }
     // K stage 0 is rewritten (with K_2) at the end of the first iteration:
     // every wave must have finished reading it above.
-    __syncthreads();
+    gsync();
 
     // One K/V block: `scur` holds this block's scores, `snxt` receives the next
     // block's.  The loop is unrolled by two so the buffers swap roles instead
@@ -334,6 +413,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
                     const uint8_t* __restrict__ v_rd) __attribute__((always_inline)) {
         const bool has_next = it + 1 < n_it;
         const bool has_next2 = it + 2 < n_it;
+        const int kb = kb0 + it;        // absolute K/V block of this step
 
         // ---- move the reference maximum only when a row outgrows it by 2^kTau ----
         // Otherwise p <= 2^kTau and the stale reference cancels in the final
@@ -350,8 +430,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
 
         // K_{it+2} into the K stage freed by block it, V_{it+1} into the V stage
         // freed by block it-1; both land while this block is computed.
-        if (has_next2) dma_tile<D>(Kh, k_dma, k_lane_off, (it + 2) * kBN, Sk, wave);
-        if (has_next) dma_tile<D>(Vh, v_dma, v_lane_off, (it + 1) * kBN, Sk, wave);
+        if (has_next2) dma_tile<D>(Kh, k_dma, k_lane_off, (kb + 2) * kBN, Sk, wave);
+        if (has_next) dma_tile<D>(Vh, v_dma, v_lane_off, (kb + 1) * kBN, Sk, wave);
 
         // ---- phase X: scores of block it+1 on the matrix core, exponentials of
         // the first 32 keys of block it; phase Y: O^T += V_it^T P_it^T on the
@@ -383,7 +463,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
             for (int v = 0; v < 16; ++v) exp_unit(v);
         }
 
-        if (has_next && needs_mask((it + 1) * kBN)) mask_block<CAUSAL>(snxt, (it + 1) * kBN, Sk, my_q, diag, hh);
+        if (has_next && needs_mask((kb + 1) * kBN)) mask_block<CAUSAL>(snxt, (kb + 1) * kBN, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
             const uint8_t* vt = v_rd;
@@ -420,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (has_next) mx_cur = half_swap_max(mxn) * scale_log2;
 
         wait_dma();
-        __syncthreads();
+        gsync();
     };
     f32x16 s1[2];
     for (int it = 0; it < n_it; it += 2) {
@@ -429,38 +509,66 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(
         if (it + 1 < n_it) step(it + 1, s1, s0, kbuf + T::K_BYTES, vbuf, kbuf, vbuf + T::V_BYTES);
     }
 
-    // ---- epilogue: one division per row, bf16 output, natural-log lse ----
-    // Each wave's 32 x D output tile passes through its own slice of LDS (free
-    // after the loop's last barrier), so that every global store instruction
-    // writes whole consecutive rows (1 KiB) instead of 16-byte pieces of 32
-    // rows.  16-byte chunks are XOR-swizzled by row for conflict-free LDS
-    // writes and reads.
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    {
-        constexpr int CH = D / 8;                 // 16-byte chunks per row
-        constexpr int RPP = 64 / CH;              // rows per wave-wide 16-byte pass
-        uint8_t* const ot = lds + wave * 32 * T::ROWB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int c = 4 * db + a;         // chunk of head-dim columns 32 db + 8 a .. +7
-                const u32x2 w = {pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv),
-                                 pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
-                *reinterpret_cast<u32x2*>(ot + l32 * T::ROWB + 16 * (c ^ (l32 & (CH - 1))) + 8 * hh) = w;
+    if (final) write_out(qb);
+    };   // run_job
+
+    if constexpr (PAIR) {
+        // Pair workgroup p of (b, hq): heavy block i = n-1-p and light block p
+        // (n query blocks; i == p for the middle block when n is odd).  Group A
+        // takes K/V blocks [0, split) of block i; group B the whole of block p,
+        // then [split, 2i + 2) of block i: n + 1 blocks each, and the two
+        // groups run unsynchronised on their own LDS stages.
+        const int p = rank, i = n_qblk - 1 - p;
+        const int split = i != p ? n_qblk + 1 : (n_qblk + 1) / 2;
+        if (grp == 0) {
+            run_job(i, 0, split, false);
+        } else {
+            if (i != p) {
+                run_job(p, 0, 2 * p + 2, true);
+                gsync();                 // its output staging is read before the next job's loads reuse the LDS
             }
-        __syncthreads();
-        const int rr = lane / CH, cc = lane % CH;
-#pragma unroll
-        for (int i = 0; i < 32 / RPP; ++i) {
-            const int r = i * RPP + rr;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * T::ROWB + 16 * (cc ^ (r & (CH - 1))));
-            if (qw + r < Sq) *reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc) = v;
+            run_job(i, split, 2 * i + 2, false);
         }
+        // ---- the halves of block i meet: the online-softmax update of two
+        // partial states, M = max(m_A, m_B), acc = acc_A 2^(m_A - M) + acc_B
+        // 2^(m_B - M), l likewise.  Group B's waves hold the same rows and
+        // columns, lane for lane, as group A's. ----
+        __syncthreads();                 // both groups done; every K/V stage is free
+        float* const st = reinterpret_cast<float*>(lds + GROUP_LDS) + wave * (64 * 16 * NDB);
+        float2* const sml = reinterpret_cast<float2*>(lds + GROUP_LDS / 4 * 3) + wave * 64;
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<f32x4*>(st + ((db * 4 + a) * 64 + lane) * 4) =
+                        f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]};
+            sml[lane] = make_float2(m_run, l_run);
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const float2 ml = sml[lane];
+            const float M = fmaxf(m_run, ml.x);
+            const float Mu = M == kNegInf ? 0.f : M;
+            const float wa = exp2f_hw(m_run - Mu), wb = exp2f_hw(ml.x - Mu);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 o = *reinterpret_cast<const f32x4*>(st + ((db * 4 + a) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oacc[db][4 * a + e] = oacc[db][4 * a + e] * wa + o[e] * wb;
+                }
+            l_run = l_run * wa + ml.y * wb;
+            m_run = M;
+            write_out(i);
+        }
+    } else {
+        const int qb = CAUSAL ? n_qblk - 1 - rank : rank;
+        int kv_end = Sk;
+        if (CAUSAL) kv_end = min(Sk, max(0, qb * kBM + kBM + diag));
+        run_job(qb, 0, (kv_end + kBN - 1) / kBN, true);
     }
-    if (LSE != nullptr && hh == 0 && my_q < Sq)
-        LSE[((int64_t)b * Hq + hq) * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
 }
 
 int num_cus() {
@@ -473,16 +581,29 @@ int num_cus() {
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int n_qblk = (a.Sq + kBM - 1) / kBM;
-    const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
     const int units = a.B * a.Hkv;
     const int xcd_groups = (units % 8 == 0) ? units / 8 : 0;
     const float scale_log2 = a.scale * kLog2e;
+    const int cus = num_cus();
+    // Pair grid: a causal square problem whose query blocks, paired heavy with
+    // light, fit one 8-wave workgroup per CU; every workgroup then walks the
+    // same number of K/V blocks.
+    const int n_pairs = (n_qblk + 1) / 2;
+    if (D == 128 && CAUSAL && a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 &&
+        (int64_t)a.B * a.Hq * n_pairs <= cus) {
+        const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+        launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
+                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                      a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0);
+        return hipGetLastError();
+    }
+    const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
     // Two workgroups fit on a CU; if the whole grid is resident at once, pair
     // heavy and light causal Q blocks on the same CU.
-    const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)num_cus()) ? 1 : 0;
-    launch_kernel((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
+    const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)cus) ? 1 : 0;
+    launch_kernel((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, xcd_groups, mirror);
+                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror);
     return hipGetLastError();
 }
 

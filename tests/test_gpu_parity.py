@@ -387,3 +387,39 @@ def test_binding_errors(B):
     with pytest.raises(B.FAError) as e:
         run_decode(B, d, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == B.FA_ERR_WORKSPACE
+
+
+# --- causal square problems that fit one 8-wave workgroup per CU: the pair
+# grid (heavy block n-1-p and light block p share a workgroup, the heavy one
+# split between its two wave groups and merged at the end) ----------------
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 1024), (1, 3, 1, 384), (2, 4, 2, 256), (1, 2, 1, 1152),
+                                   (1, 1, 1, 2048), (1, 16, 8, 1024), (1, 5, 5, 640)],
+                         ids=lambda s: "B{}Hq{}Hkv{}S{}".format(*s))
+def test_pair_grid_matches_oracle(B, shape):
+    b, hq, hkv, s = shape
+    n = s // 128
+    assert b * hq * ((n + 1) // 2) <= 256       # the pair grid applies (one workgroup per CU)
+    c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=11 * s + hq)
+    o, lse = run_fwd(B, c)
+    O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
+    check_o(o, O, "bf16", f"pair grid {shape}")
+    check_lse(lse, L, f"pair grid {shape}")
+
+
+def test_pair_grid_closed_forms(B):
+    # V = 1 gives O = 1; Q = 0 gives the cumulative mean of V and lse = ln(#visible)
+    c = I.make_prefill(1, 2, 2, 1024, 1024, 128, causal=True, seed=9)
+    q, k = _bf(c.bits("q")), _bf(c.bits("k"))
+    ones = torch.ones_like(q)
+    o, _ = B.fa_fwd(q, k, ones, True, c.scale)
+    torch.cuda.synchronize()
+    assert float((o.float() - 1).abs().max()) <= 2 ** -8
+    v = _bf(c.bits("v"))
+    o, lse = B.fa_fwd(torch.zeros_like(q), k, v, True, c.scale)
+    torch.cuda.synchronize()
+    vv = _np(v)
+    cum = np.cumsum(vv, axis=2) / np.arange(1, 1025)[None, None, :, None]
+    check_o(_np(o), cum, "bf16", "pair grid q=0")
+    check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(np.arange(1, 1025.0)), (1, 2, 1024)),
+              "pair grid q=0 lse")
