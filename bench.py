@@ -241,7 +241,7 @@ def main():
             "step_also_runs": [FP32, DECODE],
         },
         "roofline": {
-            "kernel": "fwd_bf16_kernel<128,causal>",
+            "kernel": "fwd_bf16_kernel<128,causal,pair>",
             "bound": "mfma",
             "achieved": round(tflops_p, 2),
             "peak": peak_tf,
