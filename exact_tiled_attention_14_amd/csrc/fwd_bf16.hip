@@ -588,14 +588,15 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     // Pair grid: a causal square problem whose query blocks, paired heavy with
     // light, fit one 8-wave workgroup per CU; every workgroup then walks the
     // same number of K/V blocks.
-    const int n_pairs = (n_qblk + 1) / 2;
-    if (D == 128 && CAUSAL && a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 &&
-        (int64_t)a.B * a.Hq * n_pairs <= cus) {
-        const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
-        launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
-                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                      a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0);
-        return hipGetLastError();
+    if constexpr (D == 128 && CAUSAL) {
+        const int n_pairs = (n_qblk + 1) / 2;
+        if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
+            const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+            launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
+                          (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0);
+            return hipGetLastError();
+        }
     }
     const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
     // Two workgroups fit on a CU; if the whole grid is resident at once, pair
