@@ -487,7 +487,9 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
                         // p of keys 32 + 16 ks .. +15 (P operand of key step ks + 2)
 #pragma unroll
                         for (int v = 16 + 8 * ks + db * 8 / NDB; v < 16 + 8 * ks + (db + 1) * 8 / NDB; ++v) exp_unit(v);
-                    } else if (has_next) {
+                    } else {
+                        // (without a next block snxt holds zeros and mxn is not used:
+                        // no branch inside the product sequence)
                         const int blk = ks - 2;
 #pragma unroll
                         for (int r = db * 16 / NDB; r < (db + 1) * 16 / NDB; ++r) mxn = fmaxf(mxn, snxt[blk][r]);
