@@ -82,6 +82,79 @@ def lead_report(lead, host_s):
             "host_ahead": bool(host_s * 1e3 < spin_ms)}
 
 
+class GfxClock:
+    """Samples the shader (GFX) clock and the socket power with amdsmi while
+    the GPU works through a queued loop.  Fractions of peak are quoted against
+    the 2.4 GHz peak clock; under sustained matrix-core load the clock and power
+    limits say how far the chip actually ran from it.  Every method returns
+    None / [] when amdsmi is not usable on the machine."""
+
+    def __init__(self):
+        self.h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            hs = amdsmi.amdsmi_get_processor_handles()
+            if hs:
+                self.h, self.smi = hs[0], amdsmi
+        except Exception:
+            self.h = None
+
+    @staticmethod
+    def _num(x):
+        if isinstance(x, (list, tuple)):
+            v = [float(e) for e in x if isinstance(e, (int, float))]
+            return sorted(v)[len(v) // 2] if v else None
+        return float(x) if isinstance(x, (int, float)) else None
+
+    def read(self):
+        """{name: value} of this instant (MHz, W), values that the driver does not report left out."""
+        if self.h is None:
+            return {}
+        out = {}
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
+            for key, name in (("current_gfxclks", "current_gfxclk_mhz"), ("current_gfxclk", "current_gfxclk_mhz"),
+                              ("average_gfxclk_frequency", "average_gfxclk_mhz"),
+                              ("average_socket_power", "socket_power_w")):
+                v = self._num(m.get(key))
+                if v is not None and name not in out:
+                    out[name] = v
+        except Exception:
+            pass
+        if "current_gfxclk_mhz" not in out:
+            try:
+                out["current_gfxclk_mhz"] = float(
+                    self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)["clk"])
+            except Exception:
+                pass
+        return out
+
+    def sample_until(self, done, start=None, period_s=0.0005, max_s=10.0):
+        """Samples from the completion of the torch event `start` (if given)
+        until the completion of `done`."""
+        out, t0 = [], time.perf_counter()
+        while start is not None and not start.query() and time.perf_counter() - t0 < max_s:
+            time.sleep(period_s)
+        while self.h is not None and not done.query() and time.perf_counter() - t0 < max_s:
+            v = self.read()
+            if v:
+                out.append(v)
+            time.sleep(period_s)
+        return out
+
+
+def clock_report(samples):
+    """Medians (and the sample count) of each quantity; None without samples."""
+    if not samples:
+        return None
+    rep = {"samples": len(samples)}
+    for name in sorted({k for s in samples for k in s}):
+        x = sorted(s[name] for s in samples if name in s)
+        rep[name] = x[len(x) // 2]
+    return rep
+
+
 def kernel_events(n):
     """n (start, stop) pairs of timing events for fa_time_next_call."""
     from exact_tiled_attention_14_amd import binding
@@ -472,6 +545,22 @@ def main():
         torch.cuda.empty_cache()
 
     # ---- larger prefill workloads, timed on their own ----
+    clock = GfxClock()
+    # ---- shader clock under the headline prefill, repeated back to back ----
+    if clock.h is not None:
+        for _ in range(3):
+            run_prefill()
+        torch.cuda.synchronize()
+        lead = gpu_lead(stream, 40.0)           # the host enqueues every prefill before the GPU starts them
+        for _ in range(400):
+            run_prefill()
+        done = torch.cuda.Event()
+        done.record(stream)
+        samples = clock.sample_until(done, start=lead[1])
+        torch.cuda.synchronize()
+        # (the first quarter of the samples is dropped: the clock settles under the new load)
+        result["roofline"]["gfx_clock_under_load"] = clock_report(samples[len(samples) // 4:])
+
     if not args.no_extra:
         extra = {}
         for name in EXTRA:
@@ -495,13 +584,17 @@ def main():
                 binding.fa_time_next_call(a, b)
                 binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
             host_s = time.perf_counter() - host0
+            done = torch.cuda.Event()
+            done.record(stream)
+            samples = clock.sample_until(done, start=lead[1])
             torch.cuda.synchronize()
             st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
             fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
             tf = fl / (st["mean"] * 1e-3) / 1e12
             extra[name] = {"us": round(st["mean"] * 1e3, 1), "TFLOP/s": round(tf, 1),
                            "frac_bf16_peak": round(tf / peak_tf, 4), "reps": reps, "causal": spec["causal"],
-                           "host_lead": lead_report(lead, host_s)}
+                           "host_lead": lead_report(lead, host_s),
+                           "gfx_clock_under_load": clock_report(samples[len(samples) // 4:])}
             log(f"{name}: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
             del q, k, v, o, lse
             torch.cuda.empty_cache()
