@@ -168,7 +168,7 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
@@ -575,7 +575,8 @@ def main():
             scale = 1.0 / math.sqrt(s["d"])
             for _ in range(2):
                 binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
-            reps = max(3, min(K, 10))
+            # at least 50 timed launches of the 8k workload, 20 of the 32k one (with the default --steps)
+            reps = max(3, min(K, 20 if s["Sq"] > 8192 else 50))
             evs = kernel_events(reps)
             torch.cuda.synchronize()
             lead = gpu_lead(stream, 2.0 + 0.3 * reps)
