@@ -54,6 +54,10 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
+// Scheduling fence: LDS operand reads issued ahead of a group of products stay
+// ahead of it, so their latency is covered by the products in between.
+#define BWD_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 // Copy rows r0 .. r0+ROWS-1 of a [S, 128] bf16 matrix into an LDS tile with
 // the global-to-LDS load; rows past S repeat row S-1.  Load sl fills the
 // 1 KiB slice sl (4 rows); lane l lands at byte 16 l of it and fetches the
@@ -350,11 +354,26 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         const float* d_s = s_d[stage];
 
         // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
+        // (one wave per SIMD: the operands of head-dim step s + 1 are read while step s computes)
         f32x16 st = f32x16{}, pt = f32x16{};
+        bf16x8 qa[2], ka[2], ga[2], va[2];
+        qa[0] = row_operand(qt, l32, 0, hh);
+        ka[0] = row_operand(kv_lds[0], krow, 0, hh);
+        ga[0] = row_operand(gt, l32, 0, hh);
+        va[0] = row_operand(kv_lds[1], krow, 0, hh);
 #pragma unroll
         for (int s = 0; s < kD / 16; ++s) {
-            st = mfma32(row_operand(qt, l32, s, hh), row_operand(kv_lds[0], krow, s, hh), st);
-            pt = mfma32(row_operand(gt, l32, s, hh), row_operand(kv_lds[1], krow, s, hh), pt);
+            const int c = s & 1;
+            if (s + 1 < kD / 16) {
+                qa[c ^ 1] = row_operand(qt, l32, s + 1, hh);
+                ka[c ^ 1] = row_operand(kv_lds[0], krow, s + 1, hh);
+                ga[c ^ 1] = row_operand(gt, l32, s + 1, hh);
+                va[c ^ 1] = row_operand(kv_lds[1], krow, s + 1, hh);
+            }
+            BWD_FENCE();
+            st = mfma32(qa[c], ka[c], st);
+            pt = mfma32(ga[c], va[c], pt);
+            BWD_FENCE();
         }
         float p[16], ds[16];
 #pragma unroll
