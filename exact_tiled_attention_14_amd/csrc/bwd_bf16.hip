@@ -354,7 +354,14 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         const float* d_s = s_d[stage];
 
         // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
-        // (one wave per SIMD: the operands of head-dim step s + 1 are read while step s computes)
+        // (one wave per SIMD: the operands of head-dim step s + 1 are read while
+        // step s computes, and the rows' lse offsets and D before the products)
+        float lo_r[16], dd_r[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            lo_r[r] = lo_s[acc_row(r, hh)];
+            dd_r[r] = d_s[acc_row(r, hh)];
+        }
         f32x16 st = f32x16{}, pt = f32x16{};
         bf16x8 qa[2], ka[2], ga[2], va[2];
         qa[0] = row_operand(qt, l32, 0, hh);
@@ -380,10 +387,9 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         for (int r = 0; r < 16; ++r) {
             const int qi = acc_row(r, hh), q = q0 + qi;
             const bool ok = q < Sq && my_k < Sk && (!CAUSAL || my_k <= q + diag);
-            const float lo = lo_s[qi], dd = d_s[qi];
-            const float e = exp2f_hw(fmaf(st[r], scale_log2, -lo));
+            const float e = exp2f_hw(fmaf(st[r], scale_log2, -lo_r[r]));
             p[r] = ok ? e : 0.f;
-            ds[r] = p[r] * (pt[r] - dd);
+            ds[r] = p[r] * (pt[r] - dd_r[r]);
         }
         u32x4 pw[2], dsw[2];
         pack_operand(pw, p);
