@@ -217,14 +217,26 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
         const uint8_t* vt = kt + kKVBlk * kROWB;
 
         // S^T = K Q^T and dP^T = V dO^T for keys kv0 .. kv0+63 (two 32-key blocks)
+        // (products in the order (s, block, S or dP); each one's LDS operand is
+        // read one product ahead)
         f32x16 st[2] = {f32x16{}, f32x16{}}, pt[2] = {f32x16{}, f32x16{}};
+        constexpr int NP = kD / 16 * 4;
+        auto opnd = [&](int j) {
+            const int s = j >> 2, blk = (j >> 1) & 1;
+            return row_operand((j & 1) ? vt : kt, 32 * blk + l32, s, hh);
+        };
+        bf16x8 ring[2];
+        ring[0] = opnd(0);
 #pragma unroll
-        for (int s = 0; s < kD / 16; ++s) {
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                st[blk] = mfma32(row_operand(kt, 32 * blk + l32, s, hh), qf[s], st[blk]);
-                pt[blk] = mfma32(row_operand(vt, 32 * blk + l32, s, hh), gf[s], pt[blk]);
-            }
+        for (int j = 0; j < NP; ++j) {
+            const int s = j >> 2, blk = (j >> 1) & 1;
+            if (j + 1 < NP) ring[(j + 1) & 1] = opnd(j + 1);
+            BWD_FENCE();
+            if (j & 1)
+                pt[blk] = mfma32(ring[j & 1], gf[s], pt[blk]);
+            else
+                st[blk] = mfma32(ring[j & 1], qf[s], st[blk]);
+            BWD_FENCE();
         }
         // dS^T = P^T o (dP^T - D): register r of block blk is key kv0 + 32 blk + acc_row(r, hh)
         u32x4 dsw[4];
