@@ -235,7 +235,7 @@ template <int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk,
-    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror) {
+    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias) {
     using T = Tile<D>;
     constexpr int NS = D / 16;          // MFMA steps of one score block
     constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
@@ -518,10 +518,13 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
         // Pair workgroup p of (b, hq): heavy block i = n-1-p and light block p
         // (n query blocks; i == p for the middle block when n is odd).  Group A
         // takes K/V blocks [0, split) of block i; group B the whole of block p,
-        // then [split, 2i + 2) of block i: n + 1 blocks each, and the two
-        // groups run unsynchronised on their own LDS stages.
+        // then [split, 2i + 2) of block i, and the two groups run
+        // unsynchronised on their own LDS stages.  An even split gives each
+        // group n + 1 blocks, but group B also pays a second job start and the
+        // light block's output; `split_bias` blocks move from B to A to even
+        // out the finishing times.
         const int p = rank, i = n_qblk - 1 - p;
-        const int split = i != p ? n_qblk + 1 : (n_qblk + 1) / 2;
+        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : (n_qblk + 1) / 2;
         if (grp == 0) {
             run_job(i, 0, split, false);
         } else {
@@ -529,7 +532,14 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
                 run_job(p, 0, 2 * p + 2, true);
                 gsync();                 // its output staging is read before the next job's loads reuse the LDS
             }
-            run_job(i, split, 2 * i + 2, false);
+            if (split < 2 * i + 2) {
+                run_job(i, split, 2 * i + 2, false);
+            } else {                     // group A takes all of block i: B's share is empty
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+                m_run = kNegInf;
+                l_run = 0.f;
+            }
         }
         // ---- the halves of block i meet: the online-softmax update of two
         // partial states, M = max(m_A, m_B), acc = acc_A 2^(m_A - M) + acc_B
@@ -594,9 +604,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
         const int n_pairs = (n_qblk + 1) / 2;
         if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
             const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+            // K/V blocks moved from group B to group A: B's extra costs (a second
+            // job start, the light block's output) are fixed, A's and B's shares
+            // grow with n; measured best at 3-4, 4-5 and 6-8 blocks for n = 8,
+            // 16 and 32 query blocks.
+            const int split_bias = 2 + n_qblk / 8;
             launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0);
+                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0, split_bias);
             return hipGetLastError();
         }
     }
@@ -606,7 +621,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)cus) ? 1 : 0;
     launch_kernel((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror);
+                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror, 0);
     return hipGetLastError();
 }
 
