@@ -356,15 +356,16 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     const int my_q = qw + l32;          // the query row this lane's scores belong to
     const int n_it = kb1 - kb0;         // K/V blocks of this job
 
-    // Q fragment, the B operand of S^T = K Q^T: 8 contiguous head-dim elements per step.
+    // Q fragment, the B operand of S^T = K Q^T: 8 contiguous head-dim elements
+    // per step.  Lanes past the last query row read row Sq - 1 instead; their
+    // scores are never written out.  The values are not touched before the
+    // first product, so the loads' latency overlaps that of the K/V loads
+    // issued next (a select on them here would wait for them first).
     bf16x8 qf[NS];
     {
         const uint16_t* qp = Q + q_off + (int64_t)min(my_q, Sq - 1) * D + 8 * hh;
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const bf16x8 val = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
-            qf[s] = my_q < Sq ? val : bf16x8{};
-        }
+        for (int s = 0; s < NS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
     }
 
 #pragma unroll
