@@ -179,7 +179,10 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     if (CAUSAL) kv_end = min(Sk, max(0, q0 + kBM8 + diag));
     const int n_it = (kv_end + kBN8 - 1) / kBN8;
 
-    // Q fragment (B operand of S^T = K Q^T): head-dim bytes 64 s + 32 h .. +31
+    // Q fragment (B operand of S^T = K Q^T): head-dim bytes 64 s + 32 h .. +31.
+    // Lanes past the last query row read row Sq - 1; their scores are never
+    // written out, and without a select on the values the loads' latency
+    // overlaps that of the first K/V loads.
     i32x8 qf[2];
     {
         const uint8_t* qp = Q + (bhq * Sq + min(my_q, Sq - 1)) * kD8 + 32 * hh;
@@ -187,7 +190,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         for (int s = 0; s < 2; ++s) {
             const i32x4 a = *reinterpret_cast<const i32x4*>(qp + 64 * s);
             const i32x4 c = *reinterpret_cast<const i32x4*>(qp + 64 * s + 16);
-            qf[s] = my_q < Sq ? i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]} : i32x8{};
+            qf[s] = i32x8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
         }
     }
 
