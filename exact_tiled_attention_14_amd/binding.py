@@ -31,6 +31,31 @@ class FAError(RuntimeError):
         self.status = status
 
 
+_vp, _i, _f, _sz, _u8p = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# (argument types, result type) of every entry point of include/fa.h, in the
+# header's order; a pointer of any type is passed as c_void_p.
+SIGNATURES = {
+    "fa_fwd": ([_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _vp], _i),
+    "fa_bwd_workspace_size": ([_i, _i, _i], _sz),
+    "fa_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "fa_decode_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
+    "fa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "fa_decode_multi_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "fa_decode_multi": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp],
+                        _i),
+    "fa_mla_decode_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
+    "fa_mla_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "fa_quantize_fp8_bytes": ([_i, _i, _i, _i, _i], _sz),
+    "fa_quantize_fp8": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp], _i),
+    "fa_fwd_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "fa_time_next_call": ([_vp, _vp], _i),
+    "fa_limit_next_sync_wait": ([_i], _i),
+    "fa_sync_timeouts": ([_vp], _i),
+    "fa_status_string": ([_i], ctypes.c_char_p),
+}
+
+
 def load() -> ctypes.CDLL:
     """Load ``libfa.so`` once; raise if it has not been built."""
     global _lib
@@ -40,35 +65,10 @@ def load() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m exact_tiled_attention_14_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
-    lib.fa_fwd.restype = i
-    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i]
-    lib.fa_decode_workspace_size.restype = sz
-    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_decode.restype = i
-    lib.fa_bwd_workspace_size.argtypes = [i, i, i]
-    lib.fa_bwd_workspace_size.restype = sz
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_bwd.restype = i
-    lib.fa_quantize_fp8_bytes.argtypes = [i, i, i, i, i]
-    lib.fa_quantize_fp8_bytes.restype = sz
-    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, vp]
-    lib.fa_quantize_fp8.restype = i
-    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
-    lib.fa_fwd_fp8.restype = i
-    lib.fa_decode_multi_workspace_size.argtypes = [i, i, i, i, i, i, i]
-    lib.fa_decode_multi_workspace_size.restype = sz
-    lib.fa_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_decode_multi.restype = i
-    lib.fa_mla_decode_workspace_size.argtypes = [i, i, i, i, i, i]
-    lib.fa_mla_decode_workspace_size.restype = sz
-    lib.fa_mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_mla_decode.restype = i
-    lib.fa_time_next_call.argtypes = [vp, vp]
-    lib.fa_time_next_call.restype = i
-    lib.fa_status_string.argtypes = [i]
-    lib.fa_status_string.restype = ctypes.c_char_p
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = list(args)
+        fn.restype = res
     _lib = lib
     return lib
 
@@ -152,19 +152,30 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check(t, name, dtype, ndim, device=None):
+def _check(t, name, dtype, shape, device=None):
+    """Type, dtype, rank (``shape`` an int) or exact shape (a tuple),
+    contiguity and, with ``device``, the device of a tensor argument.  That
+    the tensors live on a GPU is checked by :func:`_on_gpu` just before the
+    launch, so every shape error is raised first."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if t.dim() != ndim:
-        raise ValueError(f"{name} must have {ndim} dimensions (got {tuple(t.shape)})")
+    if isinstance(shape, int):
+        if t.dim() != shape:
+            raise ValueError(f"{name} must have {shape} dimensions (got {tuple(t.shape)})")
+    elif tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _on_gpu(*tensors):
+    for t in tensors:
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"tensor arguments must be GPU tensors (got {t.device})")
 
 
 def fa_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None,
@@ -193,15 +204,12 @@ def fa_fwd(q, k, v, causal: bool, scale: float | None = None, out=None, lse=None
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", dtype, 4, q.device)
-        if out.shape != q.shape:
-            raise ValueError("out must have q's shape")
+        _check(out, "out", dtype, tuple(q.shape), q.device)
     if lse is None and return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
     elif lse is not None:
-        _check(lse, "lse", torch.float32, 3, q.device)
-        if tuple(lse.shape) != (B, Hq, Sq):
-            raise ValueError("lse must be [B, Hq, Sq]")
+        _check(lse, "lse", torch.float32, (B, Hq, Sq), q.device)
+    _on_gpu(q, k, v, out, lse)
     st = lib.fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Sq, Sk, d,
                     int(bool(causal)), float(scale), code, _stream(q.device))
     if st != FA_OK:
@@ -238,6 +246,7 @@ def fa_quantize_fp8(x, block_rows: int, layout: int = FA_FP8_ROWS, rot=None):
         codes = torch.empty((B, H, S, d), dtype=torch.uint8, device=x.device)
     assert codes.numel() == nbytes
     scales = torch.empty((B, H, nblk), dtype=torch.uint8, device=x.device)
+    _on_gpu(x, rot, codes, scales)
     st = lib.fa_quantize_fp8(_ptr(x), _ptr(rot), _ptr(codes), _ptr(scales), B, H, S, d, int(block_rows),
                              int(layout), _stream(x.device))
     if st != FA_OK:
@@ -270,11 +279,12 @@ def fa_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, scale: float
     if out is None:
         out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=q8.device)
     else:
-        _check(out, "out", torch.bfloat16, 4, q8.device)
+        _check(out, "out", torch.bfloat16, (B, Hq, Sq, d), q8.device)
     if lse is None:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q8.device)
     else:
-        _check(lse, "lse", torch.float32, 3, q8.device)
+        _check(lse, "lse", torch.float32, (B, Hq, Sq), q8.device)
+    _on_gpu(q8, k8, v8, q_scale, k_scale, v_scale, out, lse)
     st = lib.fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(out),
                         _ptr(lse), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _stream(q8.device))
     if st != FA_OK:
@@ -320,6 +330,9 @@ def fa_bwd(q, k, v, o, dout, lse, causal: bool, scale: float | None = None, dq=N
     need = fa_bwd_workspace_size(B, Hq, Sq)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device:
+        raise ValueError("workspace must be on q's device")
+    _on_gpu(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                     B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _ptr(workspace),
                     workspace.numel() * workspace.element_size(), _stream(q.device))
@@ -365,11 +378,12 @@ def fa_decode(q, kcache, vcache, block_table, seqlens, scale: float | None = Non
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 3, dev)
+        _check(out, "out", torch.bfloat16, (nseq, Hq, d), dev)
     if lse is None and return_lse:
         lse = torch.empty((nseq, Hq), dtype=torch.float32, device=dev)
     elif lse is not None:
-        _check(lse, "lse", torch.float32, 2, dev)
+        _check(lse, "lse", torch.float32, (nseq, Hq), dev)
+    _on_gpu(q, kcache, vcache, block_table, seqlens, out, lse, workspace)
     st = lib.fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens),
                        _ptr(out), _ptr(lse), nseq, Hq, Hkv, d, bs, max_blocks, num_blocks,
                        float(scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -416,11 +430,12 @@ def fa_decode_multi(q, kcache, vcache, block_table, seqlens, scale: float | None
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 4, dev)
+        _check(out, "out", torch.bfloat16, (nseq, Sq, Hq, d), dev)
     if lse is None:
         lse = torch.empty((nseq, Sq, Hq), dtype=torch.float32, device=dev)
     else:
-        _check(lse, "lse", torch.float32, 3, dev)
+        _check(lse, "lse", torch.float32, (nseq, Sq, Hq), dev)
+    _on_gpu(q, kcache, vcache, block_table, seqlens, out, lse, workspace)
     st = lib.fa_decode_multi(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(out),
                              _ptr(lse), nseq, Sq, Hq, Hkv, d, bs, max_blocks, num_blocks, float(scale),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
@@ -467,14 +482,35 @@ def fa_mla_decode(q, w_uk, w_uv_t, ccache, block_table, seqlens, scale: float | 
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 3, dev)
+        _check(out, "out", torch.bfloat16, (nseq, H, dh), dev)
     if lse is None:
         lse = torch.empty((nseq, H), dtype=torch.float32, device=dev)
     else:
-        _check(lse, "lse", torch.float32, 2, dev)
+        _check(lse, "lse", torch.float32, (nseq, H), dev)
+    _on_gpu(q, w_uk, w_uv_t, ccache, block_table, seqlens, out, lse, workspace)
     st = lib.fa_mla_decode(_ptr(q), _ptr(w_uk), _ptr(w_uv_t), _ptr(ccache), _ptr(block_table), _ptr(seqlens),
                            _ptr(out), _ptr(lse), nseq, H, dh, dc, bs, max_blocks, num_blocks, float(scale),
                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev))
     if st != FA_OK:
         raise FAError("fa_mla_decode", st)
     return out, lse
+
+
+def fa_limit_next_sync_wait(spins: int) -> None:
+    """Bound the wave-group barriers of the next fa_fwd call on this thread to
+    ``spins`` polls (a test hook; the default bound is restored after that
+    call).  A barrier that runs out counts one timeout (see fa_sync_timeouts)
+    and the rows of the waves it affected come out as NaN."""
+    st = load().fa_limit_next_sync_wait(int(spins))
+    if st != FA_OK:
+        raise FAError("fa_limit_next_sync_wait", st)
+
+
+def fa_sync_timeouts() -> int:
+    """Number of wave-group barrier timeouts on the current device since the
+    last read; the count is cleared.  Synchronises the device."""
+    n = ctypes.c_uint(0)
+    st = load().fa_sync_timeouts(ctypes.byref(n))
+    if st != FA_OK:
+        raise FAError("fa_sync_timeouts", st)
+    return int(n.value)

@@ -28,12 +28,21 @@ struct TimingScope {
     ~TimingScope() { fa::call_timing() = fa::CallTiming{}; }
 };
 
+// Restores the default barrier poll bound when fa_fwd returns.
+struct SpinScope {
+    ~SpinScope() { fa::next_sync_spins() = fa::kDefaultSyncSpins; }
+};
+
 }  // namespace
 
 namespace fa {
 CallTiming& call_timing() {
     static thread_local CallTiming t;
     return t;
+}
+int& next_sync_spins() {
+    static thread_local int n = kDefaultSyncSpins;
+    return n;
 }
 }  // namespace fa
 
@@ -43,6 +52,17 @@ int fa_time_next_call(void* start_event, void* stop_event) {
     if ((start_event == nullptr) != (stop_event == nullptr)) return FA_ERR_INVALID_ARG;
     fa::call_timing() = fa::CallTiming{static_cast<hipEvent_t>(start_event), static_cast<hipEvent_t>(stop_event)};
     return FA_OK;
+}
+
+int fa_limit_next_sync_wait(int spins) {
+    if (spins < 0) return FA_ERR_INVALID_ARG;
+    fa::next_sync_spins() = spins;
+    return FA_OK;
+}
+
+int fa_sync_timeouts(unsigned int* count) {
+    if (count == nullptr) return FA_ERR_INVALID_ARG;
+    return fa::read_sync_timeouts(count) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 const char* fa_status_string(int status) {
@@ -59,6 +79,7 @@ const char* fa_status_string(int status) {
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Sq, int Sk, int d, int causal, float scale, int dtype, void* stream) {
     TimingScope timing_scope;
+    SpinScope spin_scope;
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
@@ -78,7 +99,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     const int64_t rows_per_wg = dtype == FA_BF16 ? 128 : 16;   // query rows per workgroup of each kernel
     if ((int64_t)B * Hq * ((Sq + rows_per_wg - 1) / rows_per_wg) > INT32_MAX) return FA_ERR_UNSUPPORTED;
 
-    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale};
+    fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, d, causal, scale, fa::next_sync_spins()};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const hipError_t e = dtype == FA_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;

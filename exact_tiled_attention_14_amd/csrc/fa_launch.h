@@ -40,7 +40,15 @@ struct FwdArgs {
     int B, Hq, Hkv, Sq, Sk, d;
     int causal;
     float scale;
+    int sync_spins;        // poll bound of the wave-group barriers (pair grid)
 };
+
+// Default poll bound of a wave-group barrier, and the bound the next fa_fwd
+// call on this thread uses (set by fa_limit_next_sync_wait).
+constexpr int kDefaultSyncSpins = 1 << 22;
+int& next_sync_spins();
+// Reads and clears the device's count of wave-group barrier timeouts.
+hipError_t read_sync_timeouts(unsigned int* count);
 
 struct BwdArgs {
     const void* q;

@@ -214,28 +214,41 @@ __device__ __forceinline__ void mask_block(f32x16 (&sacc)[2], int kv0, int Sk, i
         }
 }
 
+// Wave-group barrier waits that ran out, per device (read and cleared by
+// read_sync_timeouts).
+__device__ unsigned int g_sync_timeouts;
+
 // Barrier of the four waves of one wave group, through a counter in LDS:
 // each wave adds 1 on arrival and leaves once all four have arrived for this
 // round (the counter grows by 4 per round; `target` is the wave's running
-// round total).  The wait is bounded, so no wave can spin forever.
-__device__ __forceinline__ void group_barrier(uint8_t* ctr_p, int& target, int lane) {
+// round total).  The wait is bounded by `spins` polls, so no wave can spin
+// forever; a wait that runs out is counted in g_sync_timeouts and returned
+// as true, and the caller marks its rows as failed.
+__device__ __forceinline__ bool group_barrier(uint8_t* ctr_p, int& target, int lane, int spins) {
     int* const ctr = reinterpret_cast<int*>(ctr_p);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     target += kWaves;
     if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    for (int spin = 0; spin < (1 << 22); ++spin) {
+    bool timed_out = false;
+    for (int spin = 0;; ++spin) {
         const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
         if (c >= target) break;
+        if (spin >= spins) {
+            timed_out = true;
+            break;
+        }
         __builtin_amdgcn_s_sleep(1);
     }
+    if (timed_out && lane == 0) __hip_atomic_fetch_add(&g_sync_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return timed_out;
 }
 
 template <int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk,
-    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias) {
+    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias, int sync_spins) {
     using T = Tile<D>;
     constexpr int NS = D / 16;          // MFMA steps of one score block
     constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
@@ -254,6 +267,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     const int hh = lane >> 5;
     const int g = Hq / Hkv;
     int bar_target = 0;
+    bool sync_fail = false;             // a wave-group barrier of this wave ran out (its rows become NaN)
     if constexpr (PAIR) {
         if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
         __syncthreads();
@@ -261,7 +275,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     // barrier of the threads that share this workgroup's (or wave group's) K/V stages
     auto gsync = [&]() __attribute__((always_inline)) {
         if constexpr (PAIR) {
-            group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane);
+            sync_fail |= group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane, sync_spins);
         } else {
             __syncthreads();
         }
@@ -312,7 +326,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
         const int l32 = ln & 31, hh = ln >> 5;
         const int my_q = qw + l32;
         const float l_tot = half_swap_sum(l_run);
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        const float inv = sync_fail ? __builtin_nanf("") : l_tot > 0.f ? 1.f / l_tot : 0.f;
         constexpr int CH = D / 8;                 // 16-byte chunks per row
         constexpr int RPP = 64 / CH;              // rows per wave-wide 16-byte pass
         uint8_t* const ot = kbuf + wave * 32 * T::ROWB;
@@ -334,7 +348,9 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
             if (qw + r < Sq) *reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc) = v;
         }
         if (LSE != nullptr && hh == 0 && my_q < Sq)
-            LSE[((int64_t)b * Hq + hq) * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+            LSE[((int64_t)b * Hq + hq) * Sq + my_q] = sync_fail    ? __builtin_nanf("")
+                                                      : l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2
+                                                                    : kNegInf;
     };
 
     // One job: query block qb against K/V blocks [kb0, kb1); with `final` the
@@ -556,11 +572,13 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
                 for (int a = 0; a < 4; ++a)
                     *reinterpret_cast<f32x4*>(st + ((db * 4 + a) * 64 + lane) * 4) =
                         f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]};
-            sml[lane] = make_float2(m_run, l_run);
+            // (a failed barrier in group B reaches group A's write-out as a NaN sum)
+            sml[lane] = make_float2(m_run, sync_fail ? __builtin_nanf("") : l_run);
         }
         __syncthreads();
         if (grp == 0) {
             const float2 ml = sml[lane];
+            sync_fail |= __builtin_isnan(ml.y);
             const float M = fmaxf(m_run, ml.x);
             const float Mu = M == kNegInf ? 0.f : M;
             const float wa = exp2f_hw(m_run - Mu), wb = exp2f_hw(ml.x - Mu);
@@ -612,7 +630,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
             const int split_bias = 2 + 3 * n_qblk / 16;
             launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0, split_bias);
+                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0, split_bias,
+                          a.sync_spins);
             return hipGetLastError();
         }
     }
@@ -622,7 +641,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)cus) ? 1 : 0;
     launch_kernel((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
-                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror, 0);
+                       a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror, 0,
+                       a.sync_spins);
     return hipGetLastError();
 }
 
@@ -631,6 +651,20 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     if (a.d == 128) return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
     return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+hipError_t read_sync_timeouts(unsigned int* count) {
+    // every kernel that may still add to the counter finishes first
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    unsigned int n = 0;
+    e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_sync_timeouts), sizeof(n), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_sync_timeouts), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    *count = n;
+    return hipDeviceSynchronize();
 }
 
 int64_t fwd_bf16_grid(const FwdArgs& a) {

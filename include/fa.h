@@ -361,6 +361,38 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
  */
 int fa_time_next_call(void* start_event, void* stop_event);
 
+/*
+ * fa_limit_next_sync_wait - diagnostic hook: bound every wave-group barrier
+ * of the next fa_fwd call on this thread to `spins` polls instead of the
+ * default 2^22.
+ *
+ * The causal prefill that pairs a heavy and a light query block in one
+ * workgroup (section 1 of the FlashAttention scaling page: parallel over the
+ * sequence) synchronises each of its two wave groups with a counter in LDS
+ * rather than the workgroup barrier, with a bounded wait.  A wait that runs
+ * out is recorded (see fa_sync_timeouts) and the rows of the waves it touched
+ * are written as NaN (O and lse), so a timed-out call can never pass for a
+ * correct one.  Tests use a small bound to see that report while every
+ * kernel still exits normally.  The setting is cleared when that fa_fwd call
+ * returns, whatever its status.
+ *
+ * Returns FA_OK, or FA_ERR_INVALID_ARG for spins < 0.
+ */
+int fa_limit_next_sync_wait(int spins);
+
+/*
+ * fa_sync_timeouts - number of wave-group barrier waits (see
+ * fa_limit_next_sync_wait) that ran out on the current device since the last
+ * read; the count is then cleared.  Unlike the other entry points this
+ * synchronises the device (it reads a device-side counter).
+ *
+ *   count  host pointer, written with the count.
+ *
+ * Returns FA_OK, FA_ERR_INVALID_ARG for a NULL count, FA_ERR_HIP when the
+ * counter cannot be read.
+ */
+int fa_sync_timeouts(unsigned int* count);
+
 /* fa_status_string - a static, human-readable name for a status code. */
 const char* fa_status_string(int status);
 

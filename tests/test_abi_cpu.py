@@ -30,8 +30,41 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
                            "fa_decode_multi_workspace_size", "fa_decode_workspace_size", "fa_fwd",
-                           "fa_fwd_fp8", "fa_mla_decode", "fa_mla_decode_workspace_size", "fa_quantize_fp8",
-                           "fa_quantize_fp8_bytes", "fa_status_string", "fa_time_next_call"]
+                           "fa_fwd_fp8", "fa_limit_next_sync_wait", "fa_mla_decode", "fa_mla_decode_workspace_size",
+                           "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string", "fa_sync_timeouts",
+                           "fa_time_next_call"]
+
+
+def _prototypes():
+    """{name: (result C type, [parameter C types])} parsed from include/fa.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    protos = {}
+    for res, name, params in re.findall(r"(int|size_t|const char\s*\*)\s+(fa_[a-z_0-9]+)\s*\(([^)]*)\)\s*;",
+                                        text):
+        kinds = []
+        for prm in params.split(","):
+            prm = " ".join(prm.split())
+            if "*" in prm:
+                kinds.append("pointer")
+            else:
+                kinds.append(prm.rsplit(" ", 1)[0])      # the type without the parameter's name
+        protos[name] = (" ".join(res.split()), kinds)
+    return protos
+
+
+def test_binding_signatures_match_the_header():
+    """Every ctypes signature the binding installs agrees with the header's
+    prototype: the same number of parameters, each of the matching C type."""
+    from exact_tiled_attention_14_amd import binding
+    c_of = {ctypes.c_void_p: "pointer", ctypes.c_int: "int", ctypes.c_float: "float", ctypes.c_size_t: "size_t",
+            ctypes.c_char_p: "const char*"}
+    protos = _prototypes()
+    assert sorted(protos) == _declared()
+    assert sorted(binding.SIGNATURES) == sorted(protos)
+    for name, (res, params) in protos.items():
+        args, restype = binding.SIGNATURES[name]
+        assert [c_of[a] for a in args] == params, name
+        assert c_of[restype] == res.replace(" *", "*"), name
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -230,3 +263,74 @@ def test_mla_decode_workspace_size(lib):
     assert f(4096, 16, 128, 512, 16, 2048) == size(4096, 16, 2048)      # capped parts: nseq * max_blocks / 64
     assert f(1, 129, 128, 512, 16, 1) == 0 and f(1, 1, 64, 512, 16, 1) == 0 and f(1, 1, 128, 512, 8, 1) == 0
     assert f(0, 16, 128, 512, 16, 1) == 0
+
+
+# --- the binding's own checks, before anything reaches the library --------
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def _i32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.int32)
+
+
+def _decode_args(nseq=2, Hq=8, Hkv=2, pages=4):
+    return (_bf(nseq, Hq, 128), _bf(pages, Hkv, 16, 128), _bf(pages, Hkv, 16, 128), _i32(nseq, 2), _i32(nseq))
+
+
+@pytest.mark.parametrize("call", ["fwd_out", "fwd_lse", "decode_out", "decode_lse", "multi_out", "multi_lse",
+                                  "mla_out", "mla_lse", "fp8_out", "fp8_lse"])
+def test_binding_rejects_wrong_output_shapes(lib, call):
+    """A caller-supplied output or lse of the wrong shape is refused with a
+    ValueError naming it, before the GPU check and any launch (CPU tensors
+    here, so a launch could not even be attempted)."""
+    from exact_tiled_attention_14_amd import binding as b
+    with pytest.raises(ValueError, match=r"(out|lse) must have shape"):
+        if call.startswith("fwd"):
+            q = _bf(1, 4, 33, 128)
+            kv = _bf(1, 2, 40, 128)
+            kw = {"out": _bf(1, 4, 32, 128)} if call == "fwd_out" else {"lse": _f32(1, 4, 34)}
+            b.fa_fwd(q, kv, kv, True, **kw)
+        elif call.startswith("decode"):
+            kw = {"out": _bf(2, 8, 64)} if call == "decode_out" else {"lse": _f32(1, 8)}
+            b.fa_decode(*_decode_args(), **kw)
+        elif call.startswith("multi"):
+            q, kc, vc, bt, sl = _decode_args()
+            q = _bf(2, 3, 8, 128)
+            kw = {"out": _bf(2, 3, 8, 127)} if call == "multi_out" else {"lse": _f32(2, 8, 3)}
+            b.fa_decode_multi(q, kc, vc, bt, sl, **kw)
+        elif call.startswith("mla"):
+            kw = {"out": _bf(2, 4, 512)} if call == "mla_out" else {"lse": _f32(2, 5)}
+            b.fa_mla_decode(_bf(2, 4, 128), _bf(4, 512, 128), _bf(4, 128, 512), _bf(3, 16, 512), _i32(2, 2),
+                            _i32(2), **kw)
+        else:
+            import torch
+            u8 = lambda *s: torch.zeros(s, dtype=torch.uint8)   # noqa: E731
+            kw = {"out": _bf(1, 2, 128, 64)} if call == "fp8_out" else {"lse": _f32(1, 2, 64)}
+            b.fa_fwd_fp8(u8(1, 2, 128, 128), u8(1, 2, 1), u8(1, 1, 64, 128), u8(1, 1, 1), u8(1, 1, 1, 128, 64),
+                         u8(1, 1, 1), True, **kw)
+
+
+def test_binding_rejects_host_tensors_after_shape_checks(lib):
+    from exact_tiled_attention_14_amd import binding as b
+    with pytest.raises(ValueError, match="GPU tensors"):
+        b.fa_decode(*_decode_args())
+    with pytest.raises(ValueError, match="GPU tensors"):
+        b.fa_fwd(_bf(1, 2, 8, 128), _bf(1, 1, 8, 128), _bf(1, 1, 8, 128), True)
+
+
+def test_sync_hooks_validate_on_the_host(lib):
+    assert lib.fa_limit_next_sync_wait(-1) == -1
+    assert lib.fa_sync_timeouts(None) == -1
+    assert lib.fa_limit_next_sync_wait(5) == 0
+    # the setting is consumed by the next fa_fwd call, even one that fails validation
+    P = ctypes.c_void_p
+    assert lib.fa_fwd(P(16), P(32), P(48), P(64), None, 0, 1, 1, 8, 8, 128, 1, 0.1, 0, None) == -1

@@ -49,7 +49,9 @@ def check(o, lse, O, L, label):
     ninf = np.isneginf(L)
     assert (np.isneginf(lse) == ninf).all(), f"{label}: -inf pattern"
     if (~ninf).any():
-        assert float(np.abs(lse[~ninf] - L[~ninf]).max()) <= LSE_TOL, label
+        e = float(np.abs(lse[~ninf] - L[~ninf]).max())
+        print(f"{label}: lse max_abs={e:.3e}", flush=True)
+        assert e <= LSE_TOL, label
 
 
 @pytest.mark.parametrize("Hq,Hkv,Sq", [(32, 8, 8), (8, 8, 32), (8, 1, 4), (16, 8, 16), (32, 8, 5), (8, 2, 1)])
@@ -100,16 +102,13 @@ def test_empty_sequence_and_bad_block_ids(B):
         check(o[2, t][None], lse[2, t][None], Ot[0, :, 0][None], Lt[0, :, 0][None], f"bad block id, token {t}")
 
 
-def test_verify_workload_sampled(B):
+def test_verify_workload_full(B):
     """The 64-sequence, 8-token verify workload in the benchmark's launch
-    configuration; 10 sequences (shortest and longest included) checked."""
+    configuration, every sequence and every element."""
     d = I.workload("paged_verify_64seq_q8_h32kv8_d128")
     o, lse = run(B, d)
-    rng = np.random.default_rng(606)
-    seqs = sorted(set(rng.choice(64, 8, replace=False).tolist()) | {int(np.argmin(d.seqlens)), int(np.argmax(d.seqlens))})
-    sub = d.subset(seqs)
-    O, L = oracle.paged_multi_query(sub.q, sub.kcache, sub.vcache, sub.block_table, sub.seqlens, sub.scale)
-    check(o[seqs], lse[seqs], O, L, "verify workload")
+    O, L = oracle.paged_multi_query(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check(o, lse, O, L, "verify workload (64 sequences)")
 
 
 def test_one_token_matches_decode(B):

@@ -57,7 +57,9 @@ def check(o, lse, O, L, label):
     ninf = np.isneginf(L)
     assert (np.isneginf(lse) == ninf).all(), f"{label}: -inf pattern"
     if (~ninf).any():
-        assert float(np.abs(lse[~ninf] - L[~ninf]).max()) <= LSE_TOL, label
+        e = float(np.abs(lse[~ninf] - L[~ninf]).max())
+        print(f"{label}: lse max_abs={e:.3e}", flush=True)
+        assert e <= LSE_TOL, label
 
 
 @pytest.mark.parametrize("H", [16, 1, 7, 32, 40, 128])
@@ -145,17 +147,13 @@ def test_selecting_projections_match_paged_decode(B):
     assert np.abs(lse - l1.cpu().numpy()).max() <= LSE_TOL
 
 
-def test_mla_workload_sampled(B):
+def test_mla_workload_full(B):
     """The 64-sequence, 16-head, 512-latent workload in the benchmark's launch
-    configuration; 8 sequences (shortest and longest included) checked."""
+    configuration, every sequence and every element."""
     c = I.workload("mla_decode_64seq_h16_dc512")
     o, lse = run(B, c)
-    lens = c.cache.seqlens
-    rng = np.random.default_rng(707)
-    seqs = sorted(set(rng.choice(64, 6, replace=False).tolist()) | {int(np.argmin(lens)), int(np.argmax(lens))})
-    sub = c.subset(seqs)
-    O, L = ref(sub)
-    check(o[seqs], lse[seqs], O, L, "mla workload")
+    O, L = ref(c)
+    check(o, lse, O, L, "mla workload (64 sequences)")
 
 
 def test_binding_errors(B):

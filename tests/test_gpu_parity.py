@@ -3,8 +3,12 @@
 Tolerances (fixed for this method): fp32 inputs, max |dO| <= 1e-5; bf16
 inputs, max |dO| <= 2e-2 and ||dO||_2 / ||O||_2 <= 5e-3; lse within 1e-3 and
 -inf exactly where the oracle has -inf.  Full-size workloads run in the same
-launch configuration as the benchmark and are checked on seeded row (or
-sequence) samples that the oracle evaluates one by one.
+launch configuration as the benchmark.  The 2k and 8k prefills and the paged
+decode are compared with the oracle on every element of O and lse (the 8k one
+in four groups of 8 query heads, each group a test of its own so that every
+test stays within its time limit; a bound on each group's relative RMS error
+bounds the whole tensor's).  Only the 32k prefill is checked on its seeded
+512-row subset per head, which the oracle evaluates row by row.
 """
 
 import math
@@ -66,6 +70,8 @@ def check_lse(got, want, label=""):
     assert not np.isnan(got).any()
     if (~ninf).any():
         e = float(np.abs(got[~ninf] - want[~ninf]).max())
+        if label:
+            print(f"{label}: lse max_abs={e:.3e}", flush=True)
         assert e <= LSE_TOL, f"{label}: lse err {e:.3e}"
 
 
@@ -152,29 +158,44 @@ def _sampled_rows(c, n_rows, seed):
     return np.concatenate([rows, ends], axis=2)
 
 
-def _check_rows(o, lse, c, rows, label):
-    O, L = oracle.sdpa_rows(c.q, c.k, c.v, rows, c.causal, c.scale)
-    bidx = np.arange(rows.shape[0])[:, None, None]
-    hidx = np.arange(rows.shape[1])[None, :, None]
-    check_o(o[bidx, hidx, rows], O, "bf16", label)
-    check_lse(lse[bidx, hidx, rows], L, label)
-
-
 def test_causal_mha_b2_h16_s2048_d128(B):
+    """Every element of O and lse of the 2k workload (both batch entries, all
+    16 heads, all 2048 rows) against the oracle."""
     c = I.workload("causal_mha_b2_h16_s2048_d128")
     o, lse = run_fwd(B, c)
-    _check_rows(o, lse, c, _sampled_rows(c, 256, 202), "causal mha s2048 rows")
-    # two complete heads, every element
-    O, L = oracle.sdpa(c.q[1:2, 5:7], c.k[1:2, 5:7], c.v[1:2, 5:7], True, c.scale)
-    check_o(o[1:2, 5:7], O, "bf16", "causal mha s2048 heads")
-    check_lse(lse[1:2, 5:7], L)
+    O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
+    check_o(o, O, "bf16", "causal mha s2048 full")
+    check_lse(lse, L, "causal mha s2048 full")
 
 
-def test_causal_gqa_s8192_outliers(B):
+@pytest.fixture(scope="module")
+def gqa8k(B):
+    """The 8k outlier workload and the kernel's full output, computed once."""
     c = I.workload("causal_gqa_h32kv8_s8192_d128_outliers")
     assert c.meta["outliers"] == round(0.001 * c.k.size)
     o, lse = run_fwd(B, c)
-    _check_rows(o, lse, c, _sampled_rows(c, 128, 303), "causal gqa s8192 rows")
+    return c, o, lse, {"err2": 0.0, "ref2": 0.0, "max_abs": 0.0, "lse": 0.0, "groups": set()}
+
+
+@pytest.mark.parametrize("h0", [0, 8, 16, 24])
+def test_causal_gqa_s8192_outliers_full(gqa8k, h0):
+    """Query heads h0 .. h0+7 (K/V heads h0/4 .. h0/4+1) of the 8k workload,
+    every row and every element."""
+    c, o, lse, acc = gqa8k
+    g = c.q.shape[1] // c.k.shape[1]
+    kv0, kv1 = h0 // g, (h0 + 8) // g
+    O, L = oracle.sdpa(c.q[:, h0:h0 + 8], c.k[:, kv0:kv1], c.v[:, kv0:kv1], True, c.scale)
+    got = o[:, h0:h0 + 8]
+    check_o(got, O, "bf16", f"causal gqa s8192 heads {h0}..{h0 + 7}")
+    check_lse(lse[:, h0:h0 + 8], L, f"causal gqa s8192 heads {h0}..{h0 + 7}")
+    acc["err2"] += float(((got - O) ** 2).sum())
+    acc["ref2"] += float((O ** 2).sum())
+    acc["max_abs"] = max(acc["max_abs"], float(np.abs(got - O).max()))
+    acc["lse"] = max(acc["lse"], float(np.abs(lse[:, h0:h0 + 8] - L).max()))
+    acc["groups"].add(h0)
+    if len(acc["groups"]) == 4:
+        print(f"causal gqa s8192 whole tensor: max_abs={acc['max_abs']:.3e} "
+              f"rel_rms={math.sqrt(acc['err2'] / acc['ref2']):.3e} lse={acc['lse']:.3e}", flush=True)
 
 
 def test_causal_gqa_s32768(B):
@@ -267,15 +288,14 @@ def run_decode(B, d, **kw):
 
 
 def test_paged_decode_workload(B):
+    """All 64 sequences of the decode workload, every element."""
     d = I.workload("paged_decode_64seq_h32kv8_d128")
     o, lse = run_decode(B, d)
-    rng = np.random.default_rng(505)
-    seqs = sorted(set(rng.choice(64, 12, replace=False).tolist())
-                  | {int(np.argmin(d.seqlens)), int(np.argmax(d.seqlens))})
-    sub = d.subset(seqs)
-    O, L = oracle.paged_decode(sub.q, sub.kcache, sub.vcache, sub.block_table, sub.seqlens, sub.scale)
-    check_o(o[seqs], O, "bf16", "paged decode workload")
-    check_lse(lse[seqs], L, "paged decode workload")
+    O, L = oracle.paged_decode(d.q, d.kcache, d.vcache, d.block_table, d.seqlens, d.scale)
+    check_o(o, O, "bf16", "paged decode workload (64 sequences)")
+    check_lse(lse, L, "paged decode workload")
+    lerr = float(np.abs(lse - L).max())
+    print(f"paged decode workload lse max err {lerr:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(32, 8), (8, 8), (8, 1), (16, 8)])
@@ -423,3 +443,34 @@ def test_pair_grid_closed_forms(B):
     check_o(_np(o), cum, "bf16", "pair grid q=0")
     check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(np.arange(1, 1025.0)), (1, 2, 1024)),
               "pair grid q=0 lse")
+
+
+def test_pair_grid_reports_no_barrier_timeout(B):
+    B.fa_sync_timeouts()                      # clear what earlier calls left
+    c = I.make_prefill(2, 4, 2, 1024, 1024, 128, causal=True, seed=12)
+    o, lse = run_fwd(B, c)
+    assert np.isfinite(lse).all()
+    assert B.fa_sync_timeouts() == 0
+
+
+def test_pair_grid_barrier_timeout_is_reported(B):
+    """The wave-group barriers' poll bound forced to 0 from the host: waits
+    run out, the device count says so and the rows of the affected waves are
+    NaN, never a plausible result.  Every wait is bounded, so the kernel still
+    exits normally; the bound applies to that one call only."""
+    B.fa_sync_timeouts()
+    c = I.make_prefill(2, 4, 2, 1024, 1024, 128, causal=True, seed=12)
+    q, k, v = _bf(c.bits("q")), _bf(c.bits("k")), _bf(c.bits("v"))
+    B.fa_limit_next_sync_wait(0)
+    o, lse = B.fa_fwd(q, k, v, True, c.scale)
+    torch.cuda.synchronize()
+    n = B.fa_sync_timeouts()
+    print(f"barrier timeouts with a zero poll bound: {n}", flush=True)
+    assert n > 0
+    assert bool(torch.isnan(lse).any())
+    o, lse = B.fa_fwd(q, k, v, True, c.scale)
+    torch.cuda.synchronize()
+    assert B.fa_sync_timeouts() == 0
+    O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
+    check_o(_np(o), O, "bf16", "pair grid after a timed-out call")
+    check_lse(lse.cpu().numpy().astype(np.float64), L, "pair grid after a timed-out call")
