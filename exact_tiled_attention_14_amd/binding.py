@@ -41,6 +41,7 @@ SIGNATURES = {
     "fa_bwd": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "fa_decode_workspace_size": ([_i, _i, _i, _i, _i, _i], _sz),
     "fa_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
+    "fa_decode_noalloc": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "fa_decode_multi_workspace_size": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "fa_decode_multi": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp],
                         _i),
@@ -390,6 +391,42 @@ def fa_decode(q, kcache, vcache, block_table, seqlens, scale: float | None = Non
                        _stream(dev))
     if st != FA_OK:
         raise FAError("fa_decode", st)
+    return out, lse
+
+
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fa_decode_noalloc(q, kcache, vcache, block_table, seqlens, scale: float | None = None, out=None, lse=None):
+    """fa_decode without a workspace: the library's fixed per-GPU scratch
+    array (FA_DECODE_NOALLOC_SCRATCH_BYTES) serves instead, so the C call
+    allocates nothing.  ``out`` and ``lse`` must be given (this wrapper does
+    not allocate them either).  Returns ``(out, lse)``."""
+    lib = load()
+    _check(q, "q", torch.bfloat16, 3)
+    dev = q.device
+    _check(kcache, "kcache", torch.bfloat16, 4, dev)
+    _check(vcache, "vcache", torch.bfloat16, 4, dev)
+    _check(block_table, "block_table", torch.int32, 2, dev)
+    _check(seqlens, "seqlens", torch.int32, 1, dev)
+    nseq, Hq, d = q.shape
+    num_blocks, Hkv, bs, d2 = kcache.shape
+    if vcache.shape != kcache.shape or d2 != d:
+        raise ValueError("cache shape mismatch")
+    if block_table.shape[0] != nseq or seqlens.shape[0] != nseq:
+        raise ValueError("block_table / seqlens must have nseq rows")
+    if out is None or lse is None:
+        raise ValueError("fa_decode_noalloc writes into caller-given out and lse")
+    _check(out, "out", torch.bfloat16, (nseq, Hq, d), dev)
+    _check(lse, "lse", torch.float32, (nseq, Hq), dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _on_gpu(q, kcache, vcache, block_table, seqlens, out, lse)
+    st = lib.fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(out),
+                               _ptr(lse), nseq, Hq, Hkv, d, bs, block_table.shape[1], num_blocks, float(scale),
+                               _stream(dev))
+    if st != FA_OK:
+        raise FAError("fa_decode_noalloc", st)
     return out, lse
 
 

@@ -633,4 +633,34 @@ hipError_t launch_decode(const DecodeArgs& a, void* workspace, hipStream_t strea
     }
 }
 
+// Scratch of the allocation-free entry point: one array per GPU, held until
+// the process ends.  In host code `scratch` only names the symbol; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept below.  Every call on a
+// GPU reuses its array; nothing in it has to start at zero (the decode
+// writes every partial and table entry it reads within the same call), and
+// calls that overlap on one GPU race on it.
+static __device__ __align__(256) uint8_t scratch[kDecodeNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        // (two threads may both get here: they store the same address)
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev].store(ptr, std::memory_order_release);
+    }
+    return launch_decode(a, ptr, stream);
+}
+
 }  // namespace fa

@@ -181,11 +181,14 @@ size_t fa_decode_workspace_size(int nseq, int Hq, int Hkv, int d, int block_size
     return fa::decode_workspace_bytes(nseq, Hq, Hkv);
 }
 
-int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
-              const int32_t* seqlens, void* o, float* lse, int nseq, int Hq, int Hkv, int d, int block_size,
-              int max_blocks_per_seq, int num_blocks, float scale, void* workspace, size_t workspace_bytes,
-              void* stream) {
-    TimingScope timing_scope;
+}  // extern "C"
+
+namespace {
+
+// Host-side checks shared by fa_decode and fa_decode_noalloc.
+int check_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                 const int32_t* seqlens, const void* o, const float* lse, int nseq, int Hq, int Hkv, int d,
+                 int block_size, int max_blocks_per_seq, int num_blocks, float scale) {
     if (!q || !kcache || !vcache || !block_table || !seqlens || !o) return FA_ERR_INVALID_ARG;
     if (nseq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_blocks_per_seq < 1 || num_blocks < 1)
         return FA_ERR_INVALID_ARG;
@@ -203,7 +206,24 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     if ((int64_t)nseq * Hkv * max_blocks_per_seq > INT32_MAX) return FA_ERR_UNSUPPORTED;
     if (!fits(num_blocks, Hkv, block_size, d) || (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
         return FA_ERR_INVALID_ARG;
+    return FA_OK;
+}
 
+}  // namespace
+
+static_assert(fa::kDecodeNoallocScratchBytes == FA_DECODE_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size of fa_decode_noalloc");
+
+extern "C" {
+
+int fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+              const int32_t* seqlens, void* o, float* lse, int nseq, int Hq, int Hkv, int d, int block_size,
+              int max_blocks_per_seq, int num_blocks, float scale, void* workspace, size_t workspace_bytes,
+              void* stream) {
+    TimingScope timing_scope;
+    const int st = check_decode(q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, d, block_size,
+                                max_blocks_per_seq, num_blocks, scale);
+    if (st != FA_OK) return st;
     const size_t need = fa_decode_workspace_size(nseq, Hq, Hkv, d, block_size, max_blocks_per_seq);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
@@ -211,6 +231,21 @@ int fa_decode(const void* q, const void* kcache, const void* vcache, const int32
     fa::DecodeArgs a{q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, max_blocks_per_seq,
                      num_blocks, scale};
     const hipError_t e = fa::launch_decode(a, workspace, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                      const int32_t* seqlens, void* o, float* lse, int nseq, int Hq, int Hkv, int d, int block_size,
+                      int max_blocks_per_seq, int num_blocks, float scale, void* stream) {
+    TimingScope timing_scope;
+    const int st = check_decode(q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, d, block_size,
+                                max_blocks_per_seq, num_blocks, scale);
+    if (st != FA_OK) return st;
+    if (fa_decode_workspace_size(nseq, Hq, Hkv, d, block_size, max_blocks_per_seq) > fa::kDecodeNoallocScratchBytes)
+        return FA_ERR_WORKSPACE;
+    fa::DecodeArgs a{q, kcache, vcache, block_table, seqlens, o, lse, nseq, Hq, Hkv, max_blocks_per_seq,
+                     num_blocks, scale};
+    const hipError_t e = fa::launch_decode_noalloc(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

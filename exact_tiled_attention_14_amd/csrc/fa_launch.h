@@ -144,5 +144,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream);
 // Bytes of device scratch launch_decode uses (256-byte aligned sections).
 size_t decode_workspace_bytes(int nseq, int Hq, int Hkv);
 hipError_t launch_decode(const DecodeArgs& a, void* workspace, hipStream_t stream);
+// The decode with its scratch in a fixed device array of this many bytes per
+// GPU instead of a caller workspace (needs decode_workspace_bytes <= it).
+constexpr size_t kDecodeNoallocScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_noalloc(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace fa

@@ -192,6 +192,31 @@ int fa_decode(const void* q, const void* kcache, const void* vcache,
               void* stream);
 
 /*
+ * fa_decode_noalloc - fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, layouts, results and validation as
+ * fa_decode, without the workspace: its scratch is a fixed device array of
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends.  The call allocates and frees nothing (the array's
+ * address is looked up once per device, on the first call there).
+ *
+ * Limit: the sizes must satisfy fa_decode_workspace_size(...) <=
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES (for Hq / Hkv = 4, up to about 12000
+ * (sequence, K/V head) pairs; for Hq / Hkv = 8, about 4000), else
+ * FA_ERR_WORKSPACE is returned before any launch.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or threads) race and must be serialised by
+ * the caller.  Calls on one stream are ordered and safe.
+ *
+ * Returns FA_OK or a negative fa_status.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* block_table, const int32_t* seqlens, void* o, float* lse,
+                      int nseq, int Hq, int Hkv, int d, int block_size, int max_blocks_per_seq,
+                      int num_blocks, float scale, void* stream);
+
+/*
  * fa_decode_multi_workspace_size - bytes of device scratch fa_decode_multi
  * needs for these sizes (partial outputs of sequences longer than 2048
  * tokens); 0 for invalid or unsupported arguments.

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
-                           "fa_decode_multi_workspace_size", "fa_decode_workspace_size", "fa_fwd",
+                           "fa_decode_multi_workspace_size", "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd",
                            "fa_fwd_fp8", "fa_limit_next_sync_wait", "fa_mla_decode", "fa_mla_decode_workspace_size",
                            "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string", "fa_sync_timeouts",
                            "fa_time_next_call"]
