@@ -4,7 +4,8 @@
 One step runs the whole path once on resident synthetic inputs:
 
   * fp32 prefill, B=1 H=1 S=128 d=64, non-causal (correctness-sized; launch bound)
-  * bf16 causal prefill, B=2 H=16 S=2048 d=128 (the headline workload)
+  * bf16 causal GQA prefill, B=1 Hq=32 Hkv=8 S=32768 d=128 (the headline
+    workload: the largest of the five, on one GPU)
   * bf16 paged decode, 64 sequences x 1 token, Hq=32 Hkv=8 d=128, 16-token
     pages, lengths uniform in [1024, 8192]
 
@@ -13,20 +14,24 @@ Each call is timed with HIP events that its own kernel launches record
 stream the kernels run on; the events skip the system-scope cache fence), the
 interval a kernel trace reports.  A spin kernel queued ahead of each timed
 loop lets the host enqueue every timed launch before the GPU gets there (the
-JSON's `host_lead` says whether it did).  The
-headline `value` is the algorithmic TFLOP/s of the causal prefill (4 d FLOP per
-visible query-key pair) over the prefill launch time; decode reports the
-algorithmic KV bytes (each attended token's K and V once) over the decode
-launch time.  Before each decode launch a 512 MiB buffer is read so that
-neither L2 nor the 256 MB Infinity Cache holds cache lines from the last step
-(outside the decode's own events); the prefill, which follows the previous
-step's decode, also starts from cold caches.  The flush reads rather than
-writes: a write leaves the caches full of dirty lines whose write-back would
-be charged to the next timed kernel.  `traffic` is the HBM bytes per
-launch that the rocprofv3 counter passes summarised under profiles/ measured,
-reported only while the kernel source is the one they measured.  The fp64 CPU
-oracle is timed on the whole prefill workload, repeated until at least 10 s
-of oracle work, as a reported baseline.
+JSON's `host_lead` says whether it did).  The headline `value` is the
+algorithmic TFLOP/s of the 32k causal prefill (4 d FLOP per visible query-key
+pair) over its launch time; decode reports the algorithmic KV bytes (each
+attended token's K and V once) over the decode launch time.  Before each
+decode launch, and before every launch of the other prefill workloads, a
+512 MiB buffer is read so that neither L2 nor the 256 MB Infinity Cache holds
+lines of the previous call (outside the call's own events).  The flush reads
+rather than writes: a write leaves the caches full of dirty lines whose
+write-back would be charged to the next timed kernel.  `traffic` is the HBM
+bytes per launch that the rocprofv3 counter passes summarised under profiles/
+measured, and `mfma_busy` the matrix-core busy fraction of the same runs,
+both reported only while the kernel source is the one they measured.
+
+`per_config` holds every workload: the 2k and 8k prefills with their own
+roofline blocks, the fp32 and decode figures of the step.  The fp64 CPU
+oracle is timed on the same workloads on the host (`cpu_baseline`: the 32k
+workload's 512 checked rows per head at the top level, the others in full
+under `per_config`), as a reported baseline.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -45,20 +50,32 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "prefill attn TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
-PREFILL = "causal_mha_b2_h16_s2048_d128"
+HEADLINE = "causal_gqa_h32kv8_s32768_d128"
 DECODE = "paged_decode_64seq_h32kv8_d128"
 FP32 = "mha1_s128_d64_f32"
-EXTRA = ["causal_gqa_h32kv8_s8192_d128_outliers", "causal_gqa_h32kv8_s32768_d128"]
-# rocprofv3 summaries whose FETCH_SIZE / WRITE_SIZE passes give the HBM traffic
-# per launch; used only while the kernel source still has the recorded hash
-PROFILE_PREFILL = os.path.join(ROOT, "profiles", "fwd_bf16_causal_mha_b2_h16_s2048_d128.md")
-PROFILE_DECODE = os.path.join(ROOT, "profiles", "decode_paged_64seq_h32kv8_d128.md")
-PROFILE_FP8 = os.path.join(ROOT, "profiles", "fwd_fp8_causal_mha_b2_h16_s2048_d128.md")
-PROFILE_VERIFY = os.path.join(ROOT, "profiles", "decode_multi_paged_64seq_q8_h32kv8_d128.md")
+PREFILL2K = "causal_mha_b2_h16_s2048_d128"
+PREFILL8K = "causal_gqa_h32kv8_s8192_d128_outliers"
 VERIFY = "paged_verify_64seq_q8_h32kv8_d128"
-PROFILE_MLA = os.path.join(ROOT, "profiles", "mla_decode_64seq_h16_dc512.md")
 MLA = "mla_decode_64seq_h16_dc512"
-CPU_MIN_SECONDS = 10.0
+
+
+def _profile(name):
+    return os.path.join(ROOT, "profiles", name + ".md")
+
+
+# rocprofv3 summaries whose FETCH_SIZE / WRITE_SIZE and MFMA passes give the
+# HBM traffic and busy fraction per launch; used only while the kernel source
+# still has the recorded hash
+PROFILES = {
+    HEADLINE: _profile("fwd_bf16_causal_gqa_h32kv8_s32768_d128"),
+    PREFILL8K: _profile("fwd_bf16_causal_gqa_h32kv8_s8192_d128_outliers"),
+    PREFILL2K: _profile("fwd_bf16_causal_mha_b2_h16_s2048_d128"),
+    DECODE: _profile("decode_paged_64seq_h32kv8_d128"),
+    "fp8": _profile("fwd_fp8_causal_mha_b2_h16_s2048_d128"),
+    VERIFY: _profile("decode_multi_paged_64seq_q8_h32kv8_d128"),
+    MLA: _profile("mla_decode_64seq_h16_dc512"),
+}
+CPU_MIN_SECONDS = 0.5     # small oracle runs are repeated until they take this long
 
 
 def gpu_lead(stream, ms):
@@ -168,15 +185,14 @@ def log(msg):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-extra", action="store_true", help="skip the 8k/32k GQA prefill timings")
+    ap.add_argument("--no-extra", action="store_true", help="skip the 2k/8k prefill timings")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-fp8", action="store_true", help="skip the FP8 forward timing")
     ap.add_argument("--no-verify", action="store_true", help="skip the multi-query (verify) decode timing")
     ap.add_argument("--no-mla", action="store_true", help="skip the latent-cache (MLA) decode timing")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads per oracle call when timing the CPU baseline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -195,9 +211,14 @@ def main():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")
     binding.load()
+    peak_tf = metrics.MI355X_BF16_DENSE_FLOPS / 1e12
+    peak_gb = metrics.MI355X_HBM_BYTES_PER_S / 1e9
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def us(st):
+        return {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"}
 
     # ---- inputs, built on the host by the seeded generator, copied once ----
     log("generating inputs")
@@ -205,12 +226,12 @@ def main():
     f_q, f_k, f_v = (torch.from_numpy(getattr(cf, n)).to(dev) for n in "qkv")
     f_o, f_l = torch.empty_like(f_q), torch.empty(cf.q.shape[:3], dtype=torch.float32, device=dev)
 
-    cp = inputs.workload(PREFILL)
-    shp = cp.shape
-    p_q, p_k, p_v = to_dev(cp.bits("q")), to_dev(cp.bits("k")), to_dev(cp.bits("v"))
+    ch = inputs.workload(HEADLINE)
+    shp = ch.shape
+    p_q, p_k, p_v = to_dev(ch.bits("q")), to_dev(ch.bits("k")), to_dev(ch.bits("v"))
     p_o = torch.empty_like(p_q)
     p_l = torch.empty((shp["B"], shp["Hq"], shp["Sq"]), dtype=torch.float32, device=dev)
-    log("prefill inputs ready")
+    log("headline prefill inputs ready")
 
     cd = inputs.workload(DECODE)
     dshp = cd.shape
@@ -226,9 +247,7 @@ def main():
     # Between timed calls the caches are flushed by READING a 512 MiB buffer:
     # L2 and the 256 MB Infinity Cache then hold only clean lines of an
     # unrelated buffer.  Writing the buffer instead would leave them full of
-    # dirty lines whose write-back the next kernel pays for (the prefill took
-    # 65-69 us after a 512 MiB fill against 57-60 us after a 512 MiB read and
-    # 55 us warm; the decode was the same after either).
+    # dirty lines whose write-back the next kernel pays for.
     flush_buf = torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
     def flush_caches():
@@ -240,13 +259,14 @@ def main():
         binding.fa_fwd(f_q, f_k, f_v, cf.causal, cf.scale, out=f_o, lse=f_l)
 
     def run_prefill():
-        binding.fa_fwd(p_q, p_k, p_v, True, cp.scale, out=p_o, lse=p_l)
+        binding.fa_fwd(p_q, p_k, p_v, True, ch.scale, out=p_o, lse=p_l)
 
     def run_decode():
         binding.fa_decode(d_q, d_kc, d_vc, d_bt, d_sl, cd.scale, out=d_o, lse=d_l, workspace=d_ws)
 
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    clock = GfxClock()
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -275,26 +295,57 @@ def main():
         run_decode()
     t_end.record(stream)
     host_s = time.perf_counter() - host0
+    # the shader clock while the timed steps run (mostly the 32k prefill)
+    samples = clock.sample_until(t_end, start=lead[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
     lead_main = lead_report(lead, host_s)
     log(f"host lead: {lead_main}")
 
-    ms_f = [a.elapsed_ms(b) for a, b in e_f]
-    ms_p = [a.elapsed_ms(b) for a, b in e_p]
-    ms_d = [a.elapsed_ms(b) for a, b in e_d]
-    sp, sd, sf = metrics.summarize(ms_p), metrics.summarize(ms_d), metrics.summarize(ms_f)
+    sp = metrics.summarize([a.elapsed_ms(b) for a, b in e_p])
+    sd = metrics.summarize([a.elapsed_ms(b) for a, b in e_d])
+    sf = metrics.summarize([a.elapsed_ms(b) for a, b in e_f])
 
     flops_p = metrics.prefill_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
     tflops_p = flops_p / (sp["mean"] * 1e-3) / 1e12
     kv_bytes = metrics.decode_kv_bytes(cd.seqlens, dshp["Hkv"], dshp["d"])
     gbs_d = kv_bytes / (sd["mean"] * 1e-3) / 1e9
-    peak_tf = metrics.MI355X_BF16_DENSE_FLOPS / 1e12
-    peak_gb = metrics.MI355X_HBM_BYTES_PER_S / 1e9
     log(f"prefill {sp['mean']*1e3:.1f} us -> {tflops_p:.1f} TFLOP/s; decode {sd['mean']*1e3:.1f} us -> "
         f"{gbs_d:.0f} GB/s; fp32 {sf['mean']*1e3:.1f} us; step {ms_step:.3f} ms")
 
+    def prefill_roofline(kernel, flops, st, prof, note):
+        pr = profiling.current_profile(prof)
+        tf = flops / (st["mean"] * 1e-3) / 1e12
+        return {
+            "kernel": kernel, "bound": "mfma", "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
+            "frac": round(tf / peak_tf, 4), "traffic": pr["traffic"],
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "mfma_busy": pr["mfma_busy"], "profile": pr["profile"], "profile_kernel_avg_us": pr["kernel_avg_us"],
+            "algorithmic_flops_per_launch": flops, "launch_us": us(st), "caches": note,
+            "launch_timing": "HIP events recorded by the kernel launch itself (hipExtLaunchKernel; "
+                             "no system-scope fence), first kernel start to last kernel end",
+        }
+
+    headline_roof = prefill_roofline("fwd_bf16_kernel<128,causal,grid>", flops_p, sp, PROFILES[HEADLINE],
+                                     "runs after the previous step's decode; 8 ms per launch, so the "
+                                     "caches' start state matters little")
+    headline_roof["gfx_clock_under_load"] = clock_report(samples[len(samples) // 4:])
+    decode_block = {
+        "workload": DECODE,
+        "kernels": "decode_partial_kernel<4> + decode_combine_kernel<4>",
+        "bound": "hbm",
+        "achieved": round(gbs_d, 1),
+        "peak": peak_gb,
+        "unit": "GB/s",
+        "frac": round(gbs_d / peak_gb, 4),
+        "traffic": profiling.current_profile(PROFILES[DECODE])["traffic"],
+        "traffic_unit": "HBM bytes per launch of decode_partial_kernel (rocprofv3, copy-calibrated)",
+        "algorithmic_kv_bytes_per_launch": kv_bytes,
+        "kv_tokens": cd.kv_tokens,
+        "launch_us": us(sd),
+        "caches": "flushed (512 MiB read) before each launch, outside its events",
+    }
     result = {
         "metric": METRIC,
         "value": round(tflops_p, 2),
@@ -309,138 +360,160 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1), bf16-rounded; paged cache with seeded lengths and block permutation)",
         "config": {
-            "workload": PREFILL, "B": shp["B"], "Hq": shp["Hq"], "Hkv": shp["Hkv"], "S": shp["Sq"],
+            "workload": HEADLINE, "B": shp["B"], "Hq": shp["Hq"], "Hkv": shp["Hkv"], "S": shp["Sq"],
             "d": shp["d"], "causal": True,
             "step_also_runs": [FP32, DECODE],
         },
-        "roofline": {
-            "kernel": "fwd_bf16_kernel<128,causal,pair>",
-            "bound": "mfma",
-            "achieved": round(tflops_p, 2),
-            "peak": peak_tf,
-            "unit": "TFLOP/s",
-            "frac": round(tflops_p / peak_tf, 4),
-            "traffic": profiling.current_traffic(PROFILE_PREFILL),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_flops_per_launch": flops_p,
-            "launch_us": {k: round(v * 1e3, 2) for k, v in sp.items() if k != "n"},
-            "launch_timing": "HIP events recorded by the kernel launch itself (hipExtLaunchKernel; "
-                             "no system-scope fence), first kernel start to last kernel end",
+        "roofline": headline_roof,
+        "decode": decode_block,
+        "per_config": {
+            FP32: {"launch_us": us(sf), "bound": "launch", "note": "correctness-sized (4.2 MFLOP)"},
+            HEADLINE: {"see": "roofline"},
+            DECODE: {"see": "decode"},
         },
-        "decode": {
-            "workload": DECODE,
-            "kernels": "decode_partial_kernel<4> + decode_combine_kernel<4>",
-            "bound": "hbm",
-            "achieved": round(gbs_d, 1),
-            "peak": peak_gb,
-            "unit": "GB/s",
-            "frac": round(gbs_d / peak_gb, 4),
-            "traffic": profiling.current_traffic(PROFILE_DECODE),
-            "traffic_unit": "HBM bytes per launch of decode_partial_kernel (rocprofv3, copy-calibrated)",
-            "algorithmic_kv_bytes_per_launch": kv_bytes,
-            "kv_tokens": cd.kv_tokens,
-            "launch_us": {k: round(v * 1e3, 2) for k, v in sd.items() if k != "n"},
-        },
-        "fp32_prefill_us": round(sf["mean"] * 1e3, 2),
         "wall_s_timed_region": round(wall, 4),
         "host_lead": lead_main,
     }
 
-    # ---- attention backward on the headline shape, timed on its own ----
-    if not args.no_backward:
-        log("backward: inputs")
-        g_do = to_dev(inputs.bf16_bits(inputs.make_grad_out(cp.q.shape, seed=2)))
-        binding.fa_fwd(p_q, p_k, p_v, True, cp.scale, out=p_o, lse=p_l)
-        b_dq, b_dk, b_dv = torch.empty_like(p_q), torch.empty_like(p_k), torch.empty_like(p_v)
-        b_ws = torch.empty(binding.fa_bwd_workspace_size(shp["B"], shp["Hq"], shp["Sq"]), dtype=torch.uint8,
+    def time_calls(fn, reps, flush, lead_ms_per_rep):
+        """Launch statistics of `reps` calls of fn, each preceded by a cache flush
+        (outside its events) when `flush`; the shader clock is sampled while they run."""
+        for _ in range(2):
+            fn()
+        evs = kernel_events(reps)
+        torch.cuda.synchronize()
+        lead = gpu_lead(stream, 2.0 + lead_ms_per_rep * reps)
+        host0 = time.perf_counter()
+        for a, b in evs:
+            if flush:
+                flush_caches()
+            binding.fa_time_next_call(a, b)
+            fn()
+        host_s = time.perf_counter() - host0
+        done = torch.cuda.Event()
+        done.record(stream)
+        samples = clock.sample_until(done, start=lead[1])
+        torch.cuda.synchronize()
+        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
+        return st, lead_report(lead, host_s), clock_report(samples[len(samples) // 4:])
+
+    # ---- the 2k and 8k prefill workloads, each on its own, cold caches ----
+    if not args.no_extra:
+        for name, reps in ((PREFILL2K, max(5, min(K * 3, 60))), (PREFILL8K, max(5, min(K * 2, 40)))):
+            log(f"generating {name}")
+            c = inputs.workload(name)
+            s = c.shape
+            q, k, v = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
+            del c
+            o = torch.empty_like(q)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            scale = 1.0 / math.sqrt(s["d"])
+            st, lead_x, clk = time_calls(lambda: binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse), reps, True,
+                                         0.3)
+            fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
+            # (the launch's choice: a causal square problem whose heavy/light query-block
+            # pairs fit one 8-wave workgroup per CU runs as the pair grid)
+            pair = (s["Sq"] == s["Sk"] and s["Sq"] % 128 == 0 and s["Sq"] >= 256
+                    and s["B"] * s["Hq"] * ((s["Sq"] // 128 + 1) // 2) <= torch.cuda.get_device_properties(dev).multi_processor_count)
+            roof = prefill_roofline("fwd_bf16_kernel<128,causal,%s>" % ("pair" if pair else "grid"), fl, st,
+                                    PROFILES[name], "flushed (512 MiB read) before each launch, outside its events")
+            roof.update({"reps": reps, "host_lead": lead_x, "gfx_clock_under_load": clk,
+                         "shape": {k_: s[k_] for k_ in ("B", "Hq", "Hkv", "Sq", "Sk", "d")}})
+            result["per_config"][name] = roof
+            log(f"{name}: {st['mean']*1e3:.1f} us -> {roof['achieved']:.1f} TFLOP/s ({roof['frac']:.3f} of peak)")
+            del q, k, v, o, lse
+            torch.cuda.empty_cache()
+
+    # ---- attention backward and FP8 forward on the 2k workload, each timed on its own ----
+    if not (args.no_backward and args.no_fp8):
+        log("backward / fp8: inputs")
+        cb = inputs.workload(PREFILL2K)
+        bs_ = cb.shape
+        b_q, b_k, b_v = to_dev(cb.bits("q")), to_dev(cb.bits("k")), to_dev(cb.bits("v"))
+        b_o, b_l = torch.empty_like(b_q), torch.empty(b_q.shape[:3], dtype=torch.float32, device=dev)
+        g_do = to_dev(inputs.bf16_bits(inputs.make_grad_out(cb.q.shape, seed=2)))
+        binding.fa_fwd(b_q, b_k, b_v, True, cb.scale, out=b_o, lse=b_l)
+        b_dq, b_dk, b_dv = torch.empty_like(b_q), torch.empty_like(b_k), torch.empty_like(b_v)
+        b_ws = torch.empty(binding.fa_bwd_workspace_size(bs_["B"], bs_["Hq"], bs_["Sq"]), dtype=torch.uint8,
                            device=dev)
 
         def run_bwd():
-            binding.fa_bwd(p_q, p_k, p_v, p_o, g_do, p_l, True, cp.scale, dq=b_dq, dk=b_dk, dv=b_dv, workspace=b_ws)
+            binding.fa_bwd(b_q, b_k, b_v, b_o, g_do, b_l, True, cb.scale, dq=b_dq, dk=b_dk, dv=b_dv, workspace=b_ws)
 
-        for _ in range(2):
-            run_bwd()
-        reps = max(5, min(K, 20))
-        evs = kernel_events(reps)
-        torch.cuda.synchronize()
-        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
-        host0 = time.perf_counter()
-        for a, b in evs:
-            binding.fa_time_next_call(a, b)
-            run_bwd()
-        host_s = time.perf_counter() - host0
-        torch.cuda.synchronize()
-        lead_bwd = lead_report(lead, host_s)
-        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
-        fl = metrics.backward_flops(shp["B"], shp["Hq"], shp["Sq"], shp["Sk"], shp["d"], True)
-        tf = fl / (st["mean"] * 1e-3) / 1e12
-        result["backward"] = {
-            "workload": PREFILL, "kernels": "bwd_delta_kernel + bwd_dq_kernel<causal> + bwd_dkdv_kernel<causal>",
-            "bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
-            "frac": round(tf / peak_tf, 4), "algorithmic_flops_per_launch": fl,
-            "note": "algorithmic = 5 products of 2d FLOP per visible pair; the kernels execute 7 (S and dP are "
-                    "recomputed in both the dQ and the dK/dV kernel)",
-            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
-            "host_lead": lead_bwd,
-        }
-        log(f"backward: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
-        del g_do, b_dq, b_dk, b_dv, b_ws
+        if not args.no_backward:
+            st, lead_b, _ = time_calls(run_bwd, max(5, min(K, 20)), True, 0.4)
+            fl = metrics.backward_flops(bs_["B"], bs_["Hq"], bs_["Sq"], bs_["Sk"], bs_["d"], True)
+            tf = fl / (st["mean"] * 1e-3) / 1e12
+            result["backward"] = {
+                "workload": PREFILL2K, "kernels": "bwd_delta_kernel + bwd_dq_kernel<causal> + bwd_dkdv_kernel<causal>",
+                "bound": "mfma", "achieved": round(tf, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(tf / peak_tf, 4), "algorithmic_flops_per_launch": fl,
+                "note": "algorithmic = 5 products of 2d FLOP per visible pair",
+                "launch_us": us(st), "caches": "flushed (512 MiB read) before each call, outside its events",
+                "host_lead": lead_b,
+            }
+            log(f"backward: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
 
-    # ---- FP8 forward on the headline shape: quantize (rotated Q, K; V blocks), then attend ----
-    if not args.no_fp8:
-        log("fp8: quantize + forward")
-        rot = to_dev(inputs.bf16_bits(inputs.make_rotation(shp["d"], seed=2)))
-
-        def run_fp8(evs=None):
+        # ---- FP8 forward on the 2k workload: quantize (rotated Q, K; V blocks), then attend ----
+        if not args.no_fp8:
+            log("fp8: quantize + forward")
+            rot = to_dev(inputs.bf16_bits(inputs.make_rotation(bs_["d"], seed=2)))
             names = ("quant_q", "quant_k", "quant_v", "fwd_fp8")
-            calls = (lambda: binding.fa_quantize_fp8(p_q, 128, rot=rot),
-                     lambda: binding.fa_quantize_fp8(p_k, 64, rot=rot),
-                     lambda: binding.fa_quantize_fp8(p_v, 64, layout=binding.FA_FP8_VBLOCKS))
-            outs = []
-            for n, fn in zip(names[:3], calls):
-                if evs is not None:
-                    binding.fa_time_next_call(*evs[n])
-                outs.append(fn())
-            (q8, qs), (k8, ks), (v8, vs) = outs
-            if evs is not None:
-                binding.fa_time_next_call(*evs["fwd_fp8"])
-            binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, cp.scale, out=p_o, lse=p_l)
 
-        for _ in range(2):
-            run_fp8()
-        reps = max(5, min(K, 20))
-        names = ("quant_q", "quant_k", "quant_v", "fwd_fp8")
-        evs = [{n: (binding.TimingEvent(), binding.TimingEvent()) for n in names} for _ in range(reps)]
-        torch.cuda.synchronize()
-        lead = gpu_lead(stream, 2.0 + 0.5 * reps)
-        host0 = time.perf_counter()
-        for i in range(reps):
-            flush_caches()        # cold caches, as in the step
-            run_fp8(evs[i])
-        host_s = time.perf_counter() - host0
-        torch.cuda.synchronize()
-        st = {n: metrics.summarize([e[n][0].elapsed_ms(e[n][1]) for e in evs]) for n in names}
-        tf8 = flops_p / (st["fwd_fp8"]["mean"] * 1e-3) / 1e12
-        peak8 = metrics.MI355X_FP8_DENSE_FLOPS / 1e12
-        bh_q, bh_kv = shp["B"] * shp["Hq"], shp["B"] * shp["Hkv"]
-        qbytes = {"quant_q": metrics.fp8_quantize_bytes(bh_q, shp["Sq"], shp["d"], 128),
-                  "quant_k": metrics.fp8_quantize_bytes(bh_kv, shp["Sk"], shp["d"], 64),
-                  "quant_v": metrics.fp8_quantize_bytes(bh_kv, shp["Sk"], shp["d"], 64)}
-        result["fp8"] = {
-            "workload": PREFILL, "kernel": "fwd_fp8_kernel<causal>", "bound": "mfma",
-            "achieved": round(tf8, 1), "peak": peak8, "unit": "TFLOP/s", "frac": round(tf8 / peak8, 4),
-            "vs_bf16_kernel": round(sp["mean"] / st["fwd_fp8"]["mean"], 3),
-            "traffic": profiling.current_traffic(PROFILE_FP8),
-            "algorithmic_flops_per_launch": flops_p,
-            "launch_us": {k: round(v * 1e3, 2) for k, v in st["fwd_fp8"].items() if k != "n"},
-            "quantize": {n: {"us": round(st[n]["mean"] * 1e3, 2), "bytes": qbytes[n],
-                             "GB/s": round(qbytes[n] / (st[n]["mean"] * 1e-3) / 1e9, 1)} for n in qbytes},
-            "note": "E4M3 Q, K (rotated by a seeded orthogonal matrix) and V with power-of-two block scales; "
-                    "caches flushed before each quantize + forward sequence",
-            "host_lead": lead_report(lead, host_s),
-        }
-        log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q/k/v "
-            f"{st['quant_q']['mean']*1e3:.1f}/{st['quant_k']['mean']*1e3:.1f}/{st['quant_v']['mean']*1e3:.1f} us")
+            def run_fp8(evs=None):
+                calls = (lambda: binding.fa_quantize_fp8(b_q, 128, rot=rot),
+                         lambda: binding.fa_quantize_fp8(b_k, 64, rot=rot),
+                         lambda: binding.fa_quantize_fp8(b_v, 64, layout=binding.FA_FP8_VBLOCKS))
+                outs = []
+                for n, fn in zip(names[:3], calls):
+                    if evs is not None:
+                        binding.fa_time_next_call(*evs[n])
+                    outs.append(fn())
+                (q8, qs), (k8, ks), (v8, vs) = outs
+                if evs is not None:
+                    binding.fa_time_next_call(*evs["fwd_fp8"])
+                binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, cb.scale, out=b_o, lse=b_l)
+
+            for _ in range(2):
+                run_fp8()
+            reps = max(5, min(K, 20))
+            evs = [{n: (binding.TimingEvent(), binding.TimingEvent()) for n in names} for _ in range(reps)]
+            torch.cuda.synchronize()
+            lead = gpu_lead(stream, 2.0 + 0.5 * reps)
+            host0 = time.perf_counter()
+            for i in range(reps):
+                flush_caches()
+                run_fp8(evs[i])
+            host_s = time.perf_counter() - host0
+            torch.cuda.synchronize()
+            st = {n: metrics.summarize([e[n][0].elapsed_ms(e[n][1]) for e in evs]) for n in names}
+            fl2k = metrics.prefill_flops(bs_["B"], bs_["Hq"], bs_["Sq"], bs_["Sk"], bs_["d"], True)
+            tf8 = fl2k / (st["fwd_fp8"]["mean"] * 1e-3) / 1e12
+            peak8 = metrics.MI355X_FP8_DENSE_FLOPS / 1e12
+            bh_q, bh_kv = bs_["B"] * bs_["Hq"], bs_["B"] * bs_["Hkv"]
+            qbytes = {"quant_q": metrics.fp8_quantize_bytes(bh_q, bs_["Sq"], bs_["d"], 128),
+                      "quant_k": metrics.fp8_quantize_bytes(bh_kv, bs_["Sk"], bs_["d"], 64),
+                      "quant_v": metrics.fp8_quantize_bytes(bh_kv, bs_["Sk"], bs_["d"], 64)}
+            total_us = sum(st[n]["mean"] for n in names) * 1e3
+            bf16_2k = result["per_config"].get(PREFILL2K, {}).get("launch_us", {}).get("mean")
+            result["fp8"] = {
+                "workload": PREFILL2K, "kernel": "fwd_fp8_kernel<causal>", "bound": "mfma",
+                "achieved": round(tf8, 1), "peak": peak8, "unit": "TFLOP/s", "frac": round(tf8 / peak8, 4),
+                "traffic": profiling.current_profile(PROFILES["fp8"])["traffic"],
+                "algorithmic_flops_per_launch": fl2k,
+                "launch_us": us(st["fwd_fp8"]),
+                "quantize": {n: {"us": round(st[n]["mean"] * 1e3, 2), "bytes": qbytes[n],
+                                 "GB/s": round(qbytes[n] / (st[n]["mean"] * 1e-3) / 1e9, 1)} for n in qbytes},
+                "quantize_plus_forward_us": round(total_us, 2),
+                "bf16_forward_us": bf16_2k,
+                "note": "E4M3 Q, K (rotated by a seeded orthogonal matrix) and V with power-of-two block scales; "
+                        "caches flushed before each quantize + forward sequence",
+                "host_lead": lead_report(lead, host_s),
+            }
+            log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q/k/v "
+                f"{st['quant_q']['mean']*1e3:.1f}/{st['quant_k']['mean']*1e3:.1f}/{st['quant_v']['mean']*1e3:.1f} us")
+        del b_q, b_k, b_v, b_o, b_l, g_do, b_dq, b_dk, b_dv, b_ws
+        torch.cuda.empty_cache()
 
     # ---- multi-query paged attention (verify step, 8 new tokens per sequence) ----
     if not args.no_verify:
@@ -456,35 +529,20 @@ def main():
         v_ws = torch.empty(binding.fa_decode_multi_workspace_size(vshp["nseq"], vshp["Sq"], vshp["Hq"], vshp["Hkv"],
                                                                   vshp["d"], vshp["block_size"], vshp["max_blocks"]),
                            dtype=torch.uint8, device=dev)
-
-        def run_verify():
-            binding.fa_decode_multi(v_q, v_kc, v_vc, v_bt, v_sl, cv.scale, out=v_o, lse=v_l, workspace=v_ws)
-
-        for _ in range(2):
-            run_verify()
-        reps = max(5, min(K, 20))
-        evs = kernel_events(reps)
-        torch.cuda.synchronize()
-        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
-        host0 = time.perf_counter()
-        for i, (a, b) in enumerate(evs):
-            flush_caches()
-            binding.fa_time_next_call(a, b)
-            run_verify()
-        host_s = time.perf_counter() - host0
-        torch.cuda.synchronize()
-        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
+        st, lead_v, _ = time_calls(lambda: binding.fa_decode_multi(v_q, v_kc, v_vc, v_bt, v_sl, cv.scale, out=v_o,
+                                                                   lse=v_l, workspace=v_ws),
+                                   max(5, min(K, 20)), True, 0.4)
         vbytes = metrics.decode_kv_bytes(cv.seqlens, vshp["Hkv"], vshp["d"])
         gbs_v = vbytes / (st["mean"] * 1e-3) / 1e9
         result["verify"] = {
             "workload": VERIFY, "kernels": "mq_partial_kernel<4> + mq_combine_kernel<4>", "bound": "hbm",
             "achieved": round(gbs_v, 1), "peak": peak_gb, "unit": "GB/s", "frac": round(gbs_v / peak_gb, 4),
-            "traffic": profiling.current_traffic(PROFILE_VERIFY),
+            "traffic": profiling.current_profile(PROFILES[VERIFY])["traffic"],
             "algorithmic_kv_bytes_per_launch": vbytes, "kv_tokens": cv.kv_tokens,
             "flops_per_launch": metrics.decode_flops(cv.seqlens, vshp["Hq"], vshp["d"]) * vshp["Sq"],
-            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
+            "launch_us": us(st),
             "note": "caches flushed (512 MiB read) before each launch, outside its events",
-            "host_lead": lead_report(lead, host_s),
+            "host_lead": lead_v,
         }
         log(f"verify: {st['mean']*1e3:.1f} us -> {gbs_v:.0f} GB/s")
         del v_q, v_kc, v_vc, v_o, v_ws
@@ -505,138 +563,130 @@ def main():
         m_ws = torch.empty(binding.fa_mla_decode_workspace_size(msh["nseq"], msh["H"], msh["d_h"], msh["d_c"],
                                                                 msh["block_size"], msh["max_blocks"]),
                            dtype=torch.uint8, device=dev)
-
-        def run_mla():
-            binding.fa_mla_decode(m_q, m_wk, m_wv, m_cc, m_bt, m_sl, cm.scale, out=m_o, lse=m_l, workspace=m_ws)
-
-        for _ in range(2):
-            run_mla()
-        reps = max(5, min(K, 20))
-        evs = kernel_events(reps)
-        torch.cuda.synchronize()
-        lead = gpu_lead(stream, 2.0 + 0.3 * reps)
-        host0 = time.perf_counter()
-        for i, (a, b) in enumerate(evs):
-            flush_caches()
-            binding.fa_time_next_call(a, b)
-            run_mla()
-        host_s = time.perf_counter() - host0
-        torch.cuda.synchronize()
-        st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
+        st, lead_m, _ = time_calls(lambda: binding.fa_mla_decode(m_q, m_wk, m_wv, m_cc, m_bt, m_sl, cm.scale, out=m_o,
+                                                                 lse=m_l, workspace=m_ws),
+                                   max(5, min(K, 20)), True, 0.4)
         lat_bytes = metrics.mla_latent_bytes(cm.cache.seqlens, msh["d_c"])
         gbs_m = lat_bytes / (st["mean"] * 1e-3) / 1e9
         result["mla"] = {
             "workload": MLA, "bound": "hbm",
             "kernels": "mla_absorb_kernel + mla_partial_kernel + mla_combine_kernel + mla_upproj_kernel",
             "achieved": round(gbs_m, 1), "peak": peak_gb, "unit": "GB/s", "frac": round(gbs_m / peak_gb, 4),
-            "traffic": profiling.current_traffic(PROFILE_MLA),
+            "traffic": profiling.current_profile(PROFILES[MLA])["traffic"],
             "algorithmic_latent_bytes_per_launch": lat_bytes,
             "min_bytes_per_launch": metrics.mla_total_bytes(cm.cache.seqlens, msh["H"], msh["d_h"], msh["d_c"]),
             "kv_tokens": cm.cache.kv_tokens,
             "flops_per_launch": metrics.mla_flops(cm.cache.seqlens, msh["H"], msh["d_h"], msh["d_c"]),
             "materialized_kv_bytes_equivalent": metrics.decode_kv_bytes(cm.cache.seqlens, msh["H"], msh["d_h"]),
-            "launch_us": {k: round(v * 1e3, 2) for k, v in st.items() if k != "n"},
-            "note": "achieved = latent bytes over the whole call (4 kernels); caches flushed (512 MiB read) "
-                    "before each call, outside its events",
-            "host_lead": lead_report(lead, host_s),
+            "launch_us": us(st),
+            "note": "achieved = latent bytes over the whole call; caches flushed (512 MiB read) before each call, "
+                    "outside its events",
+            "host_lead": lead_m,
         }
         log(f"mla: {st['mean']*1e3:.1f} us -> {gbs_m:.0f} GB/s of latents")
         del m_q, m_wk, m_wv, m_cc, m_o, m_ws, cm
         torch.cuda.empty_cache()
 
-    # ---- larger prefill workloads, timed on their own ----
-    clock = GfxClock()
-    # ---- shader clock under the headline prefill, repeated back to back ----
-    if clock.h is not None:
-        for _ in range(3):
-            run_prefill()
-        torch.cuda.synchronize()
-        lead = gpu_lead(stream, 40.0)           # the host enqueues every prefill before the GPU starts them
-        for _ in range(400):
-            run_prefill()
-        done = torch.cuda.Event()
-        done.record(stream)
-        samples = clock.sample_until(done, start=lead[1])
-        torch.cuda.synchronize()
-        # (the first quarter of the samples is dropped: the clock settles under the new load)
-        result["roofline"]["gfx_clock_under_load"] = clock_report(samples[len(samples) // 4:])
-
-    if not args.no_extra:
-        extra = {}
-        for name in EXTRA:
-            spec = dict(inputs.WORKLOADS[name])
-            log(f"generating {name}")
-            c = inputs.workload(name)
-            s = c.shape
-            q, k, v = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
-            del c
-            o = torch.empty_like(q)
-            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-            scale = 1.0 / math.sqrt(s["d"])
-            for _ in range(2):
-                binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
-            # at least 50 timed launches of the 8k workload, 20 of the 32k one (with the default --steps)
-            reps = max(3, min(K, 20 if s["Sq"] > 8192 else 50))
-            evs = kernel_events(reps)
-            torch.cuda.synchronize()
-            lead = gpu_lead(stream, 2.0 + 0.3 * reps)
-            host0 = time.perf_counter()
-            for a, b in evs:
-                binding.fa_time_next_call(a, b)
-                binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse)
-            host_s = time.perf_counter() - host0
-            done = torch.cuda.Event()
-            done.record(stream)
-            samples = clock.sample_until(done, start=lead[1])
-            torch.cuda.synchronize()
-            st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
-            fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
-            tf = fl / (st["mean"] * 1e-3) / 1e12
-            extra[name] = {"us": round(st["mean"] * 1e3, 1), "TFLOP/s": round(tf, 1),
-                           "frac_bf16_peak": round(tf / peak_tf, 4), "reps": reps, "causal": spec["causal"],
-                           "host_lead": lead_report(lead, host_s),
-                           "gfx_clock_under_load": clock_report(samples[len(samples) // 4:])}
-            log(f"{name}: {st['mean']*1e3:.1f} us -> {tf:.1f} TFLOP/s")
-            del q, k, v, o, lse
-            torch.cuda.empty_cache()
-        result["extra_prefill"] = extra
-
-    # ---- the fp64 oracle on the host, a bounded sample of the prefill workload ----
+    # ---- the fp64 oracle on the host: the same workloads ----
     if not args.no_cpu_baseline:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max((p.get("num_threads", 1) for p in threadpool_info()
-                           if p.get("user_api") == "blas"), default=1)
-        except Exception:  # threadpoolctl missing or no BLAS reported
-            threads = os.cpu_count() or 1
-        # the whole prefill workload, one batch entry at a time, repeated
-        # until at least CPU_MIN_SECONDS of oracle work has been timed
-        h = max(1, min(args.cpu_heads, shp["Hq"]))
-        log(f"timing the fp64 oracle on the prefill workload ({h} heads per call)")
-        reps, dt = 0, 0.0
-        while dt < CPU_MIN_SECONDS:
-            for b_ in range(shp["B"]):
-                for h0 in range(0, shp["Hq"], h):
-                    t0 = time.perf_counter()
-                    oracle.sdpa(cp.q[b_:b_ + 1, h0:h0 + h], cp.k[b_:b_ + 1, h0:h0 + h], cp.v[b_:b_ + 1, h0:h0 + h],
-                                True, cp.scale)
-                    dt += time.perf_counter() - t0
-            reps += 1
-        fl = reps * flops_p
-        result["cpu_baseline"] = {
-            "value": round(fl / dt / 1e12, 6),
-            "unit": "TFLOP/s",
-            "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"the whole {PREFILL} workload ({shp['B']}x{shp['Hq']} heads, all {shp['Sq']} rows), "
-                      f"{h} heads per oracle call, {reps} pass(es), {dt:.1f} s of fp64 NumPy; algorithmic "
-                      f"causal FLOPs over oracle time",
-            "host_cpus": os.cpu_count(),
-        }
-        log(f"oracle: {dt:.2f} s for {reps} pass(es)")
+        result["cpu_baseline"] = cpu_baseline(ch, cf, cd, metrics)
 
     print(json.dumps(result), flush=True)
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:  # threadpoolctl missing or no BLAS reported
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(ch, cf, cd, metrics):
+    """The fp64 oracle, as it stands, timed on the host with time.perf_counter.
+
+    Top level: the 32k workload's checked rows (512 per head, plus the first
+    and last row), per-row time and algorithmic TFLOP/s of those rows.
+    ``per_config``: the fp32 workload (repeated to at least 0.5 s), the 2k and
+    8k workloads in full (one pass, per head group) and the 64-sequence decode
+    in full.  ``materialized`` rates count the work the oracle actually does
+    (every (query, key) pair, 4 d FLOP each, masked ones included)."""
+    import numpy as np
+
+    import oracle
+    from exact_tiled_attention_14_amd import inputs
+
+    threads = int(_blas_threads())
+    base = {"kind": "oracle", "cores": threads, "host_cpus": os.cpu_count(), "blas_threads": threads}
+    per = {}
+
+    # fp32 workload: tiny; repeated
+    log("oracle: fp32 workload")
+    reps, dt = 0, 0.0
+    while dt < CPU_MIN_SECONDS:
+        t0 = time.perf_counter()
+        oracle.sdpa(cf.q, cf.k, cf.v, cf.causal, cf.scale)
+        dt += time.perf_counter() - t0
+        reps += 1
+    s1 = cf.shape
+    fl1 = metrics.prefill_flops(s1["B"], s1["Hq"], s1["Sq"], s1["Sk"], s1["d"], cf.causal)
+    per[FP32] = {"value": round(fl1 * reps / dt / 1e12, 6), "unit": "TFLOP/s", "seconds_per_call": dt / reps,
+                 "sample": f"the whole workload, {reps} calls"}
+
+    # 2k and 8k prefills in full, 4 / 8 query heads per oracle call
+    for name, hpc in ((PREFILL2K, 4), (PREFILL8K, 8)):
+        log(f"oracle: {name} in full")
+        c = inputs.workload(name)
+        s = c.shape
+        g = s["Hq"] // s["Hkv"]
+        t0 = time.perf_counter()
+        for b in range(s["B"]):
+            for h0 in range(0, s["Hq"], hpc):
+                oracle.sdpa(c.q[b:b + 1, h0:h0 + hpc], c.k[b:b + 1, h0 // g:(h0 + hpc) // g],
+                            c.v[b:b + 1, h0 // g:(h0 + hpc) // g], True, c.scale)
+        dt = time.perf_counter() - t0
+        fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
+        mat = 4.0 * s["B"] * s["Hq"] * s["Sq"] * s["Sk"] * s["d"]
+        per[name] = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "seconds": round(dt, 2),
+                     "materialized_TFLOP/s": round(mat / dt / 1e12, 6),
+                     "sample": f"the whole workload, one pass, {hpc} query heads per oracle call"}
+        log(f"oracle: {name} {dt:.1f} s")
+        del c
+
+    # decode in full
+    log("oracle: decode workload in full")
+    t0 = time.perf_counter()
+    oracle.paged_decode(cd.q, cd.kcache, cd.vcache, cd.block_table, cd.seqlens, cd.scale)
+    dt = time.perf_counter() - t0
+    kv_bytes = metrics.decode_kv_bytes(cd.seqlens, cd.shape["Hkv"], cd.shape["d"])
+    per[DECODE] = {"value": round(kv_bytes / dt / 1e9, 3), "unit": "GB/s", "seconds": round(dt, 2),
+                   "sample": "all 64 sequences (pages gathered, one query row per head)"}
+
+    # headline: the 32k workload's checked rows
+    log("oracle: 32k workload, checked rows")
+    s = ch.shape
+    rows = np.concatenate([ch.rows, np.broadcast_to(np.array([0, s["Sq"] - 1]), (s["B"], s["Hq"], 2))], axis=2)
+    g = s["Hq"] // s["Hkv"]
+    t0 = time.perf_counter()
+    for h0 in range(0, s["Hq"], g):
+        oracle.sdpa_rows(ch.q[:, h0:h0 + g], ch.k[:, h0 // g:h0 // g + 1], ch.v[:, h0 // g:h0 // g + 1],
+                         rows[:, h0:h0 + g], True, ch.scale)
+    dt = time.perf_counter() - t0
+    n_rows = rows.size
+    fl = float(4 * s["d"] * (rows.astype(np.int64) + 1 + (s["Sk"] - s["Sq"])).sum())   # visible pairs of those rows
+    mat = 4.0 * s["d"] * s["Sk"] * n_rows
+    out = dict(base)
+    out.update({
+        "value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+        "sample": f"{HEADLINE}: {rows.shape[2]} checked rows in each of the {s['Hq']} heads ({n_rows} rows), "
+                  f"one oracle call per K/V head group; algorithmic causal FLOPs of those rows over the oracle time",
+        "seconds": round(dt, 2), "ms_per_row": round(dt / n_rows * 1e3, 4),
+        "materialized_TFLOP/s": round(mat / dt / 1e12, 6),
+        "per_config": per,
+    })
+    log(f"oracle: 32k rows {dt:.1f} s")
+    return out
+
 
 
 if __name__ == "__main__":

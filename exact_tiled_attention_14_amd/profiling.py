@@ -264,6 +264,26 @@ def read_profile_values(path: str) -> dict:
     return vals
 
 
+def current_profile(path: str) -> dict:
+    """The figures of a summary that still describe the current kernel source:
+    ``traffic`` (HBM bytes per launch), ``mfma_busy`` (busy fraction) and
+    ``kernel_avg_us`` (rocprofv3's mean duration), each None when missing or
+    when the kernel source has changed since the profile was taken."""
+    vals = read_profile_values(path)
+    out = {"traffic": None, "mfma_busy": None, "kernel_avg_us": None, "profile": os.path.relpath(path, ROOT)}
+    try:
+        fresh = "source" in vals and source_sha256(vals["source"]) == vals.get("source_sha256")
+    except OSError:
+        fresh = False
+    if not fresh:
+        return out
+    for key, name in (("hbm_bytes_per_launch", "traffic"), ("mfma_busy_fraction", "mfma_busy"),
+                      ("kernel_avg_us", "kernel_avg_us")):
+        if key in vals:
+            out[name] = float(vals[key])
+    return out
+
+
 def current_traffic(path: str):
     """HBM bytes per launch from a summary, or None when it is missing or its
     kernel source has changed since the counters were taken."""
