@@ -43,6 +43,8 @@
 // disjoint set of K/V heads.  When the whole grid fits on the GPU at once, the
 // second half of the grid runs the Q blocks in the opposite order, so that the
 // two workgroups that share a CU carry complementary causal work.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -100,10 +102,13 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8
     constexpr int ROW_STEP = kWaves * T::ROWS_PER_LOAD;   // rows between two loads of a lane
     static_assert(ROW_STEP % 16 == 0, "a lane's loads must share one swizzled chunk");
     if (kv0 + kBN <= Sk) {
+        // uniform row base (scalar registers) plus a 32-bit per-lane byte
+        // offset: the load's scalar-base form, no per-load address arithmetic
+        const uint32_t lane_bytes = (uint32_t)lane_off * 2u;
 #pragma unroll
         for (int c = 0; c < T::LOADS; ++c) {
-            const uint16_t* base = src + (int64_t)(kv0 + c * ROW_STEP) * D;      // uniform
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + lane_off),
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(src + (int64_t)(kv0 + c * ROW_STEP) * D);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + lane_bytes),
                                              (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024),
                                              16, 0, 0);
         }
@@ -419,16 +424,24 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
 
     // One K/V block: `scur` holds this block's scores, `snxt` receives the next
     // block's.  The loop is unrolled by two so the buffers swap roles instead
-    // of being copied.  The four LDS stages a step touches (K and V written by
-    // this step's global-to-LDS loads, K and V read as operands) are disjoint;
-    // passing them as restrict pointers tells the compiler so.  Without that
-    // it must assume the transposing V reads may see the loads just issued,
-    // and waits for all of them before the first P V product, which leaves
-    // only the score phase to hide their latency instead of the whole step.
-    auto step = [&](const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2], uint8_t* __restrict__ k_dma,
-                    uint8_t* __restrict__ v_dma, const uint8_t* __restrict__ k_rd,
+    // of being copied, and its last step is peeled (HAS_NEXT false), so a
+    // step has no data-dependent branch inside its product sequence.  The four
+    // LDS stages a step touches (K and V written by this step's global-to-LDS
+    // loads, K and V read as operands) are disjoint; passing them as restrict
+    // pointers tells the compiler so.  Without that it must assume the
+    // transposing V reads may see the loads just issued, and waits for all of
+    // them before the first P V product, which leaves only the score phase to
+    // hide their latency instead of the whole step.
+    //
+    // Empty asm statements that take a value as an in/out operand fix where
+    // it is computed: without them the compiler gathers the scale
+    // multiply-adds at the top of the step and the running-sum additions and
+    // the next block's maximum after the last product, and those runs of
+    // vector work then leave the matrix core idle.
+    auto step = [&](auto has_next_c, const int it, f32x16 (&scur)[2], f32x16 (&snxt)[2],
+                    uint8_t* __restrict__ k_dma, uint8_t* __restrict__ v_dma, const uint8_t* __restrict__ k_rd,
                     const uint8_t* __restrict__ v_rd) __attribute__((always_inline)) {
-        const bool has_next = it + 1 < n_it;
+        constexpr bool HAS_NEXT = decltype(has_next_c)::value;
         const bool has_next2 = it + 2 < n_it;
         const int kb = kb0 + it;        // absolute K/V block of this step
 
@@ -447,8 +460,10 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
 
         // K_{it+2} into the K stage freed by block it, V_{it+1} into the V stage
         // freed by block it-1; both land while this block is computed.
-        if (has_next2) dma_tile<D>(Kh, k_dma, k_lane_off, (kb + 2) * kBN, Sk, wave);
-        if (has_next) dma_tile<D>(Vh, v_dma, v_lane_off, (kb + 1) * kBN, Sk, wave);
+        if (HAS_NEXT) {
+            if (has_next2) dma_tile<D>(Kh, k_dma, k_lane_off, (kb + 2) * kBN, Sk, wave);
+            dma_tile<D>(Vh, v_dma, v_lane_off, (kb + 1) * kBN, Sk, wave);
+        }
 
         // ---- phase X: scores of block it+1 on the matrix core, exponentials of
         // the first 32 keys of block it; phase Y: O^T += V_it^T P_it^T on the
@@ -461,26 +476,33 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
         float rs = 0.f;
         auto exp_unit = [&](int v) {
             const int blk = v >> 4, r = v & 15;
-            pv[v] = exp2f_hw(fmaf(scur[blk][r], scale_log2, -m_use));
+            float t = fmaf(scur[blk][r], scale_log2, -m_use);
+            asm volatile("" : "+v"(t));
+            pv[v] = exp2f_hw(t);
             // the running sum adds the fp32 values: rounding p to bf16 would
             // move a short row's lse by up to 2^-9
             rs += pv[v];
-            if (v & 1) pfw[2 * blk + (r >> 3)][(r & 7) >> 1] = pack_bf16x2(pv[v - 1], pv[v]);
+            asm volatile("" : "+v"(rs));
+            if (v & 1) {
+                uint32_t w = pack_bf16x2(pv[v - 1], pv[v]);
+                asm volatile("" : "+v"(w));
+                pfw[2 * blk + (r >> 3)][(r & 7) >> 1] = w;
+            }
         };
         constexpr int XS = 2 * NS;          // products of phase X
-        snxt[0] = f32x16{};
-        snxt[1] = f32x16{};
-        if (has_next) {
+        if constexpr (HAS_NEXT) {
+            snxt[0] = f32x16{};
+            snxt[1] = f32x16{};
             score_block<D>(snxt, k_rd, qf, l32, hh, [&](int k) {
 #pragma unroll
                 for (int v = k * 16 / XS; v < (k + 1) * 16 / XS; ++v) exp_unit(v);
             });
+            if (needs_mask((kb + 1) * kBN)) mask_block<CAUSAL>(snxt, (kb + 1) * kBN, Sk, my_q, diag, hh);
         } else {
 #pragma unroll
             for (int v = 0; v < 16; ++v) exp_unit(v);
         }
 
-        if (has_next && needs_mask((kb + 1) * kBN)) mask_block<CAUSAL>(snxt, (kb + 1) * kBN, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
             const uint8_t* vt = v_rd;
@@ -504,28 +526,37 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
                         // p of keys 32 + 16 ks .. +15 (P operand of key step ks + 2)
 #pragma unroll
                         for (int v = 16 + 8 * ks + db * 8 / NDB; v < 16 + 8 * ks + (db + 1) * 8 / NDB; ++v) exp_unit(v);
-                    } else {
-                        // (without a next block snxt holds zeros and mxn is not used:
-                        // no branch inside the product sequence)
+                    } else if constexpr (HAS_NEXT) {
                         const int blk = ks - 2;
 #pragma unroll
                         for (int r = db * 16 / NDB; r < (db + 1) * 16 / NDB; ++r) mxn = fmaxf(mxn, snxt[blk][r]);
+                        asm volatile("" : "+v"(mxn));
                     }
                     FA_FENCE();
                 }
             }
         }
         l_run += rs;
-        if (has_next) mx_cur = half_swap_max(mxn) * scale_log2;
+        if constexpr (HAS_NEXT) mx_cur = half_swap_max(mxn) * scale_log2;
 
         wait_dma();
         gsync();
     };
+    using Next = std::integral_constant<bool, true>;
+    using Last = std::integral_constant<bool, false>;
     f32x16 s1[2];
-    for (int it = 0; it < n_it; it += 2) {
-        // even block: K_{it+2} -> K stage 0, V_{it+1} -> V stage 1; reads K stage 1, V stage 0
-        step(it, s0, s1, kbuf, vbuf + T::V_BYTES, kbuf + T::K_BYTES, vbuf);
-        if (it + 1 < n_it) step(it + 1, s1, s0, kbuf + T::K_BYTES, vbuf, kbuf, vbuf + T::V_BYTES);
+    // even steps: K_{it+2} -> K stage 0, V_{it+1} -> V stage 1; read K stage 1, V stage 0
+    // odd steps:  K_{it+2} -> K stage 1, V_{it+1} -> V stage 0; read K stage 0, V stage 1
+    int it = 0;
+    for (; it + 2 < n_it; it += 2) {
+        step(Next{}, it, s0, s1, kbuf, vbuf + T::V_BYTES, kbuf + T::K_BYTES, vbuf);
+        step(Next{}, it + 1, s1, s0, kbuf + T::K_BYTES, vbuf, kbuf, vbuf + T::V_BYTES);
+    }
+    if (it + 1 < n_it) {
+        step(Next{}, it, s0, s1, kbuf, vbuf + T::V_BYTES, kbuf + T::K_BYTES, vbuf);
+        step(Last{}, it + 1, s1, s0, kbuf + T::K_BYTES, vbuf, kbuf, vbuf + T::V_BYTES);
+    } else if (it < n_it) {
+        step(Last{}, it, s0, s1, kbuf, vbuf + T::V_BYTES, kbuf + T::K_BYTES, vbuf);
     }
 
     if (final) write_out(qb);
