@@ -78,15 +78,21 @@ template <int D>
 __device__ __forceinline__ int swz_v(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
 // Copy the 64-row block starting at row kv0 of a [S, D] tensor into an LDS
-// stage with the global-to-LDS load.  Load c of wave w fills the 1 KiB
-// slice c * kWaves + w of the stage, and its lane l lands at byte 16 l of
-// that slice, so each lane fetches the logical chunk that the swizzle places
+// stage with the buffer load to LDS.  Load c of wave w fills the 1 KiB slice
+// c * kWaves + w of the stage, and its lane l lands at byte 16 l of that
+// slice, so each lane fetches the logical chunk that the swizzle places
 // there: row = slice * ROWS_PER_LOAD + l / CHUNKS, physical chunk l % CHUNKS.
 // The swizzles repeat every 16 (K) or 4 (V) rows, a divisor of the rows
 // between two loads of a lane, so a lane's loads share one chunk: a full
-// block is addressed as a uniform per-load base plus one loop-invariant lane
-// offset `lane_off` (in elements).  In the ragged last block rows past Sk
-// repeat row Sk - 1: their scores are masked and their p is exactly zero.
+// block is addressed by a buffer resource at row kv0 (scalar registers), a
+// per-load scalar offset and one loop-invariant lane offset `lane_off` (in
+// elements).  In the ragged last block rows past Sk repeat row Sk - 1: their
+// scores are masked and their p is exactly zero.
+//
+// The buffer form (rather than the global one) matters for the waits: the
+// compiler counts a global-to-LDS load as both a memory and an LDS access,
+// and while one is outstanding it turns every wait for an LDS operand read
+// into a wait for all of them, which undoes the operand read-ahead.
 template <int D, bool IS_K>
 __device__ __forceinline__ int dma_lane_offset(int wave, int lane) {
     using T = Tile<D>;
@@ -101,28 +107,28 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, uint8
     using T = Tile<D>;
     constexpr int ROW_STEP = kWaves * T::ROWS_PER_LOAD;   // rows between two loads of a lane
     static_assert(ROW_STEP % 16 == 0, "a lane's loads must share one swizzled chunk");
+#if defined(__HIP_DEVICE_COMPILE__)   // (the buffer builtins exist only for the device pass)
+    // every byte a lane of this block reads lies within the block's kBN rows
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(src + (int64_t)kv0 * D), 0, kBN * T::ROWB, 0x00020000);
     if (kv0 + kBN <= Sk) {
-        // uniform row base (scalar registers) plus a 32-bit per-lane byte
-        // offset: the load's scalar-base form, no per-load address arithmetic
         const uint32_t lane_bytes = (uint32_t)lane_off * 2u;
 #pragma unroll
-        for (int c = 0; c < T::LOADS; ++c) {
-            const uint8_t* base = reinterpret_cast<const uint8_t*>(src + (int64_t)(kv0 + c * ROW_STEP) * D);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + lane_bytes),
-                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024),
-                                             16, 0, 0);
-        }
+        for (int c = 0; c < T::LOADS; ++c)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024), 16, lane_bytes,
+                c * ROW_STEP * T::ROWB, 0, 0);
     } else {
         const int row0 = lane_off / D;
 #pragma unroll
         for (int c = 0; c < T::LOADS; ++c) {
-            const int row = row0 + c * ROW_STEP;
-            const uint16_t* g = src + (int64_t)min(kv0 + row, Sk - 1) * D + (lane_off - row0 * D);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024),
-                                             16, 0, 0);
+            const int row = min(row0 + c * ROW_STEP, Sk - 1 - kv0);
+            const uint32_t bytes = (uint32_t)(row * D + (lane_off - row0 * D)) * 2u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (__attribute__((address_space(3))) void*)(stage + (c * kWaves + wave) * 1024), 16, bytes, 0, 0, 0);
         }
     }
+#endif
 }
 
 // s_waitcnt vmcnt(0): every global(-to-LDS) load of this wave has landed.
