@@ -68,6 +68,20 @@ __device__ __forceinline__ float row_sum16(float x) {
     return x;
 }
 
+// Buffer load to LDS of 16 bytes per lane: lane l's bytes [voff, voff + 16)
+// past `base` (plus the uniform `soff`) land at byte 16 l of the 1 KiB LDS
+// slice `lds`.  `bytes` bounds the addressed range from `base`.  The buffer
+// form matters for the waits: the compiler counts the global-to-LDS load as
+// both a memory and an LDS access, and while one is outstanding it turns
+// every wait for an LDS operand read into a wait for all of them.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t bytes, uint8_t* lds, uint32_t voff,
+                                                  uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)   // (the buffer builtins exist only for the device pass)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+#endif
+}
+
 // Row (lane % 32 is the column) index of accumulator register r in lane half h.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

@@ -8,7 +8,7 @@
 // tiling):
 //
 //   1. K_j and V_j are copied from HBM/L2 straight into LDS with the
-//      global-to-LDS load (no registers involved, 256-byte coalesced rows),
+//      buffer load to LDS (no registers involved, 256-byte coalesced rows),
 //      K one block ahead of V, each in its own double buffer; one barrier per
 //      block.  Both tiles are row-major with XOR-swizzled 16-byte chunks, so
 //      the operand reads below hit distinct banks.
@@ -212,17 +212,21 @@ __device__ __forceinline__ bf16x8 vt_operand(const uint8_t* vt, int ks, int db, 
 }
 
 // Mask the scores of block kv0 .. kv0+63: keys past Sk, and keys above the
-// causal diagonal of this lane's row.
+// causal diagonal of this lane's row.  Accumulator register r of lane half
+// hh holds key kv0 + 32 blk + acc_row(r, hh), and both conditions are an
+// upper bound on that key, so each half-block needs one per-lane limit and
+// then one compare with the register's constant row offset and one select
+// per score.
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_block(f32x16 (&sacc)[2], int kv0, int Sk, int my_q, int diag, int hh) {
+    const int last = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;    // last visible key of this row
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk) {
+        // visible iff 8 (r / 4) + r % 4 <= lim
+        const int lim = last - kv0 - 32 * blk - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * blk + acc_row(r, hh);
-            const bool ok = key < Sk && (!CAUSAL || key <= my_q + diag);
-            sacc[blk][r] = ok ? sacc[blk][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r) sacc[blk][r] = (8 * (r >> 2) + (r & 3)) <= lim ? sacc[blk][r] : kNegInf;
+    }
 }
 
 // Wave-group barrier waits that ran out, per device (read and cleared by
@@ -432,8 +436,8 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     // block's.  The loop is unrolled by two so the buffers swap roles instead
     // of being copied, and its last step is peeled (HAS_NEXT false), so a
     // step has no data-dependent branch inside its product sequence.  The four
-    // LDS stages a step touches (K and V written by this step's global-to-LDS
-    // loads, K and V read as operands) are disjoint; passing them as restrict
+    // LDS stages a step touches (K and V written by this step's loads to
+    // LDS, K and V read as operands) are disjoint; passing them as restrict
     // pointers tells the compiler so.  Without that it must assume the
     // transposing V reads may see the loads just issued, and waits for all of
     // them before the first P V product, which leaves only the score phase to

@@ -7,7 +7,7 @@
 // scales of Q, K and V are applied inside the product by the hardware (E8M0
 // scale operands), so scores and the output accumulate in true units.  The
 // algorithm is that of the bf16 kernel: one workgroup of 4 waves per 128
-// query rows, 64-key blocks staged into LDS by global-to-LDS loads (K two
+// query rows, 64-key blocks staged into LDS by buffer loads to LDS (K two
 // blocks ahead, V one), S^T = K Q^T so a lane owns one query row, online
 // softmax with a deferred rescale, O^T += V^T P^T, one division at the end.
 //
@@ -59,24 +59,20 @@ __device__ __forceinline__ int k8_lane_offset(int wave, int lane) {
 
 __device__ __forceinline__ void dma_k8(const uint8_t* __restrict__ src, uint8_t* stage, int lane_off, int kv0, int Sk,
                                        int wave) {
+    const uint8_t* blk = src + (int64_t)kv0 * kD8;           // the block's first row
     if (kv0 + kBN8 <= Sk) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint8_t* base = src + (int64_t)(kv0 + 32 * c) * kD8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + lane_off),
-                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves8 + wave) * 1024),
-                                             16, 0, 0);
-        }
+        for (int c = 0; c < 2; ++c)
+            buffer_load_lds16(blk, kBN8 * kD8, stage + (c * kWaves8 + wave) * 1024, (uint32_t)lane_off,
+                              32 * c * kD8);
     } else {
         // ragged last block: rows past Sk repeat row Sk - 1 (their scores are masked)
         const int row0 = lane_off / kD8;
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const int row = row0 + 32 * c;
-            const uint8_t* g = src + (int64_t)min(kv0 + row, Sk - 1) * kD8 + (lane_off - row0 * kD8);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                             (__attribute__((address_space(3))) void*)(stage + (c * kWaves8 + wave) * 1024),
-                                             16, 0, 0);
+            const int row = min(row0 + 32 * c, Sk - 1 - kv0);
+            buffer_load_lds16(blk, kBN8 * kD8, stage + (c * kWaves8 + wave) * 1024,
+                              (uint32_t)(row * kD8 + (lane_off - row0 * kD8)), 0);
         }
     }
 }
@@ -91,9 +87,7 @@ __device__ __forceinline__ int v8_lane_offset(int wave, int lane) {
 __device__ __forceinline__ void dma_v8(const uint8_t* __restrict__ blk, uint8_t* stage, int lane_off, int wave) {
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(blk + c * 4096 + lane_off),
-                                         (__attribute__((address_space(3))) void*)(stage + (c * kWaves8 + wave) * 1024),
-                                         16, 0, 0);
+        buffer_load_lds16(blk, 8192, stage + (c * kWaves8 + wave) * 1024, (uint32_t)lane_off, c * 4096);
 }
 
 __device__ __forceinline__ void wait_dma8() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -235,7 +229,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     const int v_lane_off = v8_lane_offset(wave, lane);
     // Block scales used by a step are loaded one step earlier (the first ones
     // here, ahead of the prologue's wait): a load issued in the step itself
-    // would sit behind that step's global-to-LDS loads in the memory counter,
+    // would sit behind that step's K/V tile loads in the memory counter,
     // so waiting for it would wait for them too.
     const int sk0 = KSh[0];
     int sk_pref = KSh[min(1, n_kblk - 1)];   // K scale of block it + 1
@@ -263,7 +257,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
     __syncthreads();
 
     const int sw_v = swz_v8(l32);   // rows 32 db + l32 share it (period 32)
-    // The LDS stages a step writes (global-to-LDS loads of K_{it+2}, V_{it+1})
+    // The LDS stages a step writes (loads to LDS of K_{it+2}, V_{it+1})
     // and reads (K_{it+1}, V_it) are disjoint; as restrict pointers the
     // compiler knows it, and does not wait for the loads just issued before
     // the first operand read of the step.
