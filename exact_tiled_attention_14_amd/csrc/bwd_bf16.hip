@@ -34,6 +34,8 @@
 // XOR-swizzled by 4 (row mod 4) + (row / 4 mod 4): both the row reads (16
 // rows, one chunk) and the transposing reads (4 rows, 4 chunks) of a tile
 // then hit distinct banks.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -59,7 +61,7 @@ __device__ __forceinline__ int swz(int row) { return 4 * (row & 3) + ((row >> 2)
 #define BWD_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // Copy rows r0 .. r0+ROWS-1 of a [S, 128] bf16 matrix into an LDS tile with
-// the global-to-LDS load; rows past S repeat row S-1.  Load sl fills the
+// the buffer load to LDS; rows past S repeat row S-1.  Load sl fills the
 // 1 KiB slice sl (4 rows); lane l lands at byte 16 l of it and fetches the
 // logical chunk that the swizzle places there.
 template <int ROWS>
@@ -67,13 +69,13 @@ __device__ __forceinline__ void dma_rows(const uint16_t* __restrict__ src, uint8
                                          int wave, int lane) {
     static_assert(ROWS % (4 * kWavesB) == 0, "every wave issues the same number of loads");
     const int rr = lane >> 4, ch = lane & 15;
+    const uint16_t* blk = src + (int64_t)r0 * kD;             // the tile's first row
 #pragma unroll
     for (int i = 0; i < ROWS / 4 / kWavesB; ++i) {
         const int sl = wave + i * kWavesB;
         const int row = 4 * sl + rr;
-        const uint16_t* g = src + (int64_t)min(r0 + row, S - 1) * kD + 8 * (ch ^ swz(row));
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)(tile + sl * 1024), 16, 0, 0);
+        const uint32_t off = (uint32_t)((min(r0 + row, S - 1) - r0) * kD + 8 * (ch ^ swz(row))) * 2u;
+        buffer_load_lds16(blk, ROWS * kD * 2, tile + sl * 1024, off, 0);
     }
 }
 
@@ -266,17 +268,28 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
     store_rows(dQ + bhq * Sq * kD, dq, scale, my_q, Sq, hh);
 }
 
+// One stage of the dK/dV kernel: 32 query rows of Q and of dO (8 KiB each),
+// then the rows' lse offsets and D (32 fp32 each), padded to 1 KiB.
+constexpr int kQStage = 2 * kQBlk * kROWB + 1024;
+constexpr int kQStages = 3;
+
+// dK/dV: one workgroup per (batch, K/V head, 128-key block), each wave owning
+// 32 keys whose K and V rows stay in registers for the whole kernel (the B
+// operands of S = Q K^T and dP = dO V^T).  The workgroup walks the 32-row
+// query blocks of every query head of the GQA group that see its keys; a
+// step's Q and dO rows arrive in LDS by buffer loads one step ahead, with the
+// rows' lse offsets and D, into three rotating stages.  Step t computes S and
+// dP of its rows, then accumulates dV^T += dO^T P and dK^T += Q^T dS of step
+// t-1 (its stage is still intact) while the vector unit turns step t's S and
+// dP into P and dS, one of the 16 rows a lane holds after each product; the
+// last step's dV and dK products follow the loop.
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
     float scale) {
-    // two stages of (Q tile, dO tile) and of the rows' lse offsets and D, and
-    // the K and V rows of this workgroup's keys (operands of S and dP)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kQBlk * kROWB];
-    __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2][kKRows * kROWB];
-    __shared__ float s_lo[2][kQBlk], s_d[2][kQBlk];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[kQStages][kQStage];
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -289,11 +302,16 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     const int k0 = kb * kKRows;
     const int my_k = k0 + wave * 32 + l32;
 
-    dma_rows<kKRows>(K + bhk * Sk * kD, kv_lds[0], k0, Sk, wave, lane);
-    dma_rows<kKRows>(V + bhk * Sk * kD, kv_lds[1], k0, Sk, wave, lane);
-    wait_vm();
-    __syncthreads();
-    const int krow = wave * 32 + l32;          // this lane's key row in kv_lds
+    // this lane's key row of K and V: B operands of S and dP, head-dim step s
+    bf16x8 kf[kD / 16], vf[kD / 16];
+    {
+        const int64_t at = (bhk * Sk + min(my_k, Sk - 1)) * kD + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < kD / 16; ++s) {
+            kf[s] = *reinterpret_cast<const bf16x8*>(K + at + 16 * s);
+            vf[s] = *reinterpret_cast<const bf16x8*>(V + at + 16 * s);
+        }
+    }
 
     f32x16 dk[kD / 32], dv[kD / 32];
 #pragma unroll
@@ -302,120 +320,218 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     // the first query row that sees key k0 (bottom-right causal)
     const int q_first = CAUSAL ? max(0, k0 - diag) : 0;
     const int qb0 = q_first / kQBlk, n_qb = (Sq + kQBlk - 1) / kQBlk;
-    // the (query head, Q block) steps of this workgroup, flattened so that
-    // the next step's tiles are loaded while the current one is computed
+    // the (query head, Q block) steps of this workgroup, flattened
     const int per_head = max(0, n_qb - qb0);
     const int n_steps = g * per_head;
+    if (n_steps == 0) {
+        store_rows(dK + bhk * Sk * kD, dk, scale, my_k, Sk, hh);
+        store_rows(dV + bhk * Sk * kD, dv, 1.f, my_k, Sk, hh);
+        return;
+    }
     auto step_src = [&](int t, int64_t& bhq, int& q0) {
         bhq = (int64_t)b * Hq + kvh * g + t / per_head;
         q0 = (qb0 + t % per_head) * kQBlk;
     };
-    // The next step's Q and dO rows are loaded into registers while the
-    // current step computes (each thread holds two 16-byte chunks of each
-    // tile: chunk c = tid + 256 i is row c / 16, logical chunk c % 16) and
-    // written to the other LDS stage, swizzled, at the start of the next
-    // step; the raw lse and D of the rows (lanes < kQBlk, row clamped to
-    // Sq-1) likewise.  Staging through registers instead of global-to-LDS
-    // loads keeps the compiler from waiting for the prefetch before the
-    // first LDS read of the step.
-    constexpr int kChunks = kQBlk * kD / 8 / kThreadsB;    // 16-byte chunks per thread per tile
-    u32x4 qn[kChunks], gn[kChunks];
-    float lse_next = 0.f, d_next = 0.f;
-    auto fetch = [&](int t) {
+    // Q and dO rows of step t into a stage (rows past Sq repeat row Sq-1);
+    // lanes tid < kQBlk also load the raw lse and D of their row
+    auto fetch = [&](int t, uint8_t* __restrict__ st, float& l, float& d) {
         int64_t bhq;
         int q0;
         step_src(t, bhq, q0);
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + kThreadsB * i, row = c >> 4, ch = c & 15;
-            const int64_t at = (bhq * Sq + min(q0 + row, Sq - 1)) * kD + 8 * ch;
-            qn[i] = *reinterpret_cast<const u32x4*>(Q + at);
-            gn[i] = *reinterpret_cast<const u32x4*>(dO + at);
-        }
+        dma_rows<kQBlk>(Q + bhq * Sq * kD, st, q0, Sq, wave, lane);
+        dma_rows<kQBlk>(dO + bhq * Sq * kD, st + kQBlk * kROWB, q0, Sq, wave, lane);
         if (tid < kQBlk) {
             const int64_t at = bhq * Sq + min(q0 + tid, Sq - 1);
-            lse_next = LSE[at];
-            d_next = delta[at];
+            l = LSE[at];
+            d = delta[at];
         }
     };
-    if (n_steps > 0) fetch(0);
-    for (int t = 0; t < n_steps; ++t) {
-        const int stage = t & 1;
+    // once those loads have landed: the lse offset and D the products use (a
+    // row past Sq or with no visible key gets offset +inf, so p = 0, and D = 0)
+    auto put_rowvals = [&](int t, uint8_t* __restrict__ st, float l, float d) {
+        if (tid < kQBlk) {
+            int64_t bhq_unused;
+            int q0;
+            step_src(t, bhq_unused, q0);
+            const bool ok = q0 + tid < Sq;
+            float* f = reinterpret_cast<float*>(st + 2 * kQBlk * kROWB);
+            f[tid] = ok ? lse_offset(l) : __builtin_inff();
+            f[kQBlk + tid] = ok ? d : 0.f;
+        }
+    };
+
+    // Per-lane byte offsets of every LDS operand read within a stage, formed
+    // once; a step adds its stage's uniform base.  (Empty asm statements make
+    // them opaque, so the compiler neither re-derives them per stage nor
+    // keeps one copy per stage.)
+    uint32_t ro[kD / 16];               // Q / dO row operand of head-dim step s
+    uint32_t to[2][kD / 32][2];         // transposed operand (ks, db), two reads
+    uint32_t fo;                        // this lane half's lse offsets / D
+#pragma unroll
+    for (int s_ = 0; s_ < kD / 16; ++s_) {
+        ro[s_] = (uint32_t)(l32 * kROWB + 16 * ((2 * s_ + hh) ^ swz(l32)));
+        asm volatile("" : "+v"(ro[s_]));
+    }
+    {
+        const int sl = lane & 15, gq = lane >> 4, h = gq >> 1;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db) {
+                const int col = 32 * db + 16 * (gq & 1) + 4 * (sl & 3);
+                const int row0 = 16 * ks + 4 * h + (sl >> 2), row1 = row0 + 8;
+                const int x = col >> 3, half = (col >> 2) & 1;
+                to[ks][db][0] = (uint32_t)(row0 * kROWB + 16 * (x ^ swz(row0)) + 8 * half);
+                to[ks][db][1] = (uint32_t)(row1 * kROWB + 16 * (x ^ swz(row1)) + 8 * half);
+                asm volatile("" : "+v"(to[ks][db][0]), "+v"(to[ks][db][1]));
+            }
+    }
+    fo = (uint32_t)(2 * kQBlk * kROWB + 4 * 4 * hh);
+    asm volatile("" : "+v"(fo));
+
+    float lraw = 0.f, draw = 0.f;
+    fetch(0, lds[0], lraw, draw);
+    wait_vm();
+    put_rowvals(0, lds[0], lraw, draw);
+    __syncthreads();
+
+    u32x4 pw_prev[2], dsw_prev[2];   // P and dS of the previous step, bf16 B operands
+
+    // dV^T += dO^T P and dK^T += Q^T dS of the step whose stage is `st`; the
+    // transposed operands read three products ahead; `between(j)` after product j
+    auto dkdv = [&](const uint8_t* __restrict__ st, const u32x4 (&pw)[2], const u32x4 (&dsw)[2], auto&& between) {
+        constexpr int NJ = 2 * 2 * (kD / 32);  // (ks, db, dV or dK)
+        auto top = [&](int j) {
+            const int ks = j / (2 * (kD / 32)), db = (j >> 1) % (kD / 32);
+            const uint8_t* t0 = st + ((j & 1) ? 0 : kQBlk * kROWB);      // Q^T for dK, dO^T for dV
+            const s16x4 a = lds_read_tr16(t0 + to[ks][db][0]), c = lds_read_tr16(t0 + to[ks][db][1]);
+            const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+            return __builtin_bit_cast(bf16x8, v);
+        };
+        bf16x8 ring[4];
+        ring[0] = top(0);
+        ring[1] = top(1);
+        ring[2] = top(2);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int ks = j / (2 * (kD / 32)), db = (j >> 1) % (kD / 32);
+            if (j + 3 < NJ) ring[(j + 3) % 4] = top(j + 3);
+            BWD_FENCE();
+            if (j & 1)
+                dk[db] = mfma32(ring[j % 4], __builtin_bit_cast(bf16x8, dsw[ks]), dk[db]);
+            else
+                dv[db] = mfma32(ring[j % 4], __builtin_bit_cast(bf16x8, pw[ks]), dv[db]);
+            BWD_FENCE();
+            between(j);
+            BWD_FENCE();
+        }
+    };
+
+    // Step t: its rows are in stage cur, step t-1's in prev (FIRST: none),
+    // step t+1's rows go to nxt.  The stages come in as restrict pointers, so
+    // the operand reads of two do not wait for the loads into the third.
+    auto step = [&](auto first_c, const int t, uint8_t* __restrict__ cur, uint8_t* __restrict__ prev,
+                    uint8_t* __restrict__ nxt) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first_c)::value;
+        const bool has_next = t + 1 < n_steps;
+        float lnext = 0.f, dnext = 0.f;
+        if (has_next) fetch(t + 1, nxt, lnext, dnext);
+
+        // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh),
+        // lane = key; Q and dO operands read two products ahead
+        f32x16 sc = f32x16{}, pc = f32x16{};
+        {
+            constexpr int NP = kD / 16 * 2;        // products: (s, S or dP)
+            bf16x8 ring[3];
+            auto opnd = [&](int j) {
+                return *reinterpret_cast<const bf16x8*>(cur + ((j & 1) ? kQBlk * kROWB : 0) + ro[j >> 1]);
+            };
+            ring[0] = opnd(0);
+            ring[1] = opnd(1);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                if (j + 2 < NP) ring[(j + 2) % 3] = opnd(j + 2);
+                BWD_FENCE();
+                if (j & 1)
+                    pc = mfma32(ring[j % 3], vf[j >> 1], pc);
+                else
+                    sc = mfma32(ring[j % 3], kf[j >> 1], sc);
+                BWD_FENCE();
+            }
+        }
+        // the rows' lse offsets and D: four groups of four consecutive rows
+        float lo_r[16], dd_r[16];
+        {
+            const float* f = reinterpret_cast<const float*>(cur + fo);
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(f + 8 * grp);
+                const f32x4 y = *reinterpret_cast<const f32x4*>(f + kQBlk + 8 * grp);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    lo_r[4 * grp + e] = x[e];
+                    dd_r[4 * grp + e] = y[e];
+                }
+            }
+        }
         int64_t bhq_unused;
         int q0;
         step_src(t, bhq_unused, q0);
-        uint8_t* const qt = lds[stage];
-        uint8_t* const gt = qt + kQBlk * kROWB;
-#pragma unroll
-        for (int i = 0; i < kChunks; ++i) {
-            const int c = tid + kThreadsB * i, row = c >> 4, ch = c & 15;
-            const int off = row * kROWB + 16 * (ch ^ swz(row));
-            *reinterpret_cast<u32x4*>(qt + off) = qn[i];
-            *reinterpret_cast<u32x4*>(gt + off) = gn[i];
-        }
-        if (tid < kQBlk) {
-            const bool row_ok = q0 + tid < Sq;
-            s_lo[stage][tid] = row_ok ? lse_offset(lse_next) : __builtin_inff();
-            s_d[stage][tid] = row_ok ? d_next : 0.f;
-        }
-        // step t's tiles and row values are in place, and every wave is done
-        // with step t-1 (the other stage, rewritten at the start of step t+1)
-        __syncthreads();
-        if (t + 1 < n_steps) fetch(t + 1);
-        const float* lo_s = s_lo[stage];
-        const float* d_s = s_d[stage];
-
-        // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh), lane = key
-        // (one wave per SIMD: the operands of head-dim step s + 1 are read while
-        // step s computes, and the rows' lse offsets and D before the products)
-        float lo_r[16], dd_r[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            lo_r[r] = lo_s[acc_row(r, hh)];
-            dd_r[r] = d_s[acc_row(r, hh)];
-        }
-        f32x16 st = f32x16{}, pt = f32x16{};
-        bf16x8 qa[2], ka[2], ga[2], va[2];
-        qa[0] = row_operand(qt, l32, 0, hh);
-        ka[0] = row_operand(kv_lds[0], krow, 0, hh);
-        ga[0] = row_operand(gt, l32, 0, hh);
-        va[0] = row_operand(kv_lds[1], krow, 0, hh);
-#pragma unroll
-        for (int s = 0; s < kD / 16; ++s) {
-            const int c = s & 1;
-            if (s + 1 < kD / 16) {
-                qa[c ^ 1] = row_operand(qt, l32, s + 1, hh);
-                ka[c ^ 1] = row_operand(kv_lds[0], krow, s + 1, hh);
-                ga[c ^ 1] = row_operand(gt, l32, s + 1, hh);
-                va[c ^ 1] = row_operand(kv_lds[1], krow, s + 1, hh);
-            }
-            BWD_FENCE();
-            st = mfma32(qa[c], ka[c], st);
-            pt = mfma32(ga[c], va[c], pt);
-            BWD_FENCE();
-        }
-        float p[16], ds[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qi = acc_row(r, hh), q = q0 + qi;
-            const bool ok = q < Sq && my_k < Sk && (!CAUSAL || my_k <= q + diag);
-            const float e = exp2f_hw(fmaf(st[r], scale_log2, -lo_r[r]));
-            p[r] = ok ? e : 0.f;
-            ds[r] = p[r] * (pt[r] - dd_r[r]);
-        }
+        // causal: key my_k is visible to row q iff q >= my_k - diag, i.e. the
+        // register's constant row offset 8 (r / 4) + r % 4 >= thr
+        const int thr = my_k - diag - q0 - 4 * hh;
         u32x4 pw[2], dsw[2];
-        pack_operand(pw, p);
-        pack_operand(dsw, ds);
-        // dV^T += dO^T P and dK^T += Q^T dS over the 32 query rows (2 steps of 16)
-#pragma unroll
-        for (int ks = 0; ks < kQBlk / 16; ++ks) {
-            const bf16x8 bp = __builtin_bit_cast(bf16x8, pw[ks]), bd = __builtin_bit_cast(bf16x8, dsw[ks]);
-#pragma unroll
-            for (int db = 0; db < kD / 32; ++db) {
-                dv[db] = mfma32(tr_operand(gt, ks, db, lane), bp, dv[db]);
-                dk[db] = mfma32(tr_operand(qt, ks, db, lane), bd, dk[db]);
+        float pv[16], dsv[16];
+        auto unit = [&](int r) {
+            float x = fmaf(sc[r], scale_log2, -lo_r[r]);
+            asm volatile("" : "+v"(x));
+            float e = exp2f_hw(x);
+            if (CAUSAL) e = (8 * (r >> 2) + (r & 3)) >= thr ? e : 0.f;
+            pv[r] = e;
+            dsv[r] = e * (pc[r] - dd_r[r]);
+            if (r & 1) {
+                uint32_t wp = pack_bf16x2(pv[r - 1], pv[r]), wd = pack_bf16x2(dsv[r - 1], dsv[r]);
+                asm volatile("" : "+v"(wp), "+v"(wd));
+                pw[r >> 3][(r & 7) >> 1] = wp;
+                dsw[r >> 3][(r & 7) >> 1] = wd;
             }
+        };
+        if constexpr (FIRST) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) unit(r);
+        } else {
+            dkdv(prev, pw_prev, dsw_prev, [&](int j) { unit(j); });
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            pw_prev[i] = pw[i];
+            dsw_prev[i] = dsw[i];
+        }
+        if (has_next) {
+            wait_vm();
+            put_rowvals(t + 1, nxt, lnext, dnext);
+        }
+        // step t+1's rows are in place; every wave is done with stage prev
+        __syncthreads();
+    };
+    using First = std::integral_constant<bool, true>;
+    using Later = std::integral_constant<bool, false>;
+    // unrolled by three so that each step's stages are fixed addresses
+    uint8_t* const st0 = lds[0];
+    uint8_t* const st1 = lds[1];
+    uint8_t* const st2 = lds[2];
+    step(First{}, 0, st0, st2, st1);
+    for (int t = 1; t < n_steps; ++t) {
+        // the three stage bases as opaque scalars: one add per operand address
+        uint32_t bc = (uint32_t)(t % kQStages) * kQStage, bp = (uint32_t)((t + 2) % kQStages) * kQStage,
+                 bn = (uint32_t)((t + 1) % kQStages) * kQStage;
+        asm volatile("" : "+s"(bc), "+s"(bp), "+s"(bn));
+        step(Later{}, t, &lds[0][0] + bc, &lds[0][0] + bp, &lds[0][0] + bn);
+    }
+    // the last step's dV and dK products
+    {
+        uint8_t* const last = lds[(n_steps - 1) % kQStages];
+        dkdv(last, pw_prev, dsw_prev, [](int) {});
     }
     store_rows(dK + bhk * Sk * kD, dk, scale, my_k, Sk, hh);
     store_rows(dV + bhk * Sk * kD, dv, 1.f, my_k, Sk, hh);
