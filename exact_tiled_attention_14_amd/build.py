@@ -30,6 +30,15 @@ FLAGS = [
 ]
 
 
+# Extra options for single sources.  The backward's dK/dV kernel runs one wave
+# per SIMD with its gradient accumulators in AGPRs; by default the compiler
+# also puts the S and dP products there and copies them back for the
+# softmax arithmetic (64 register moves per step), which the VGPR form of the
+# matrix-core results avoids (same-box A/B: 209.9 -> 203.7 us for the whole
+# backward at B2 H16 S2048).
+SOURCE_FLAGS = {"bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -39,7 +48,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
