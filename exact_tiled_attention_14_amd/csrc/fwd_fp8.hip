@@ -101,16 +101,18 @@ __device__ __forceinline__ i32x8 read32(const uint8_t* row_base, int c0, int sw)
     return i32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Keys past Sk and above this lane's causal diagonal: both bound the key
+// kv0 + 32 blk + acc_row(r, hh) from above, so one per-lane limit per
+// half-block, then one compare with the register's row offset and a select.
 template <bool CAUSAL>
 __device__ __forceinline__ void mask_block8(f32x16 (&sacc)[2], int kv0, int Sk, int my_q, int diag, int hh) {
+    const int last = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;    // last visible key of this row
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
+    for (int blk = 0; blk < 2; ++blk) {
+        const int lim = last - kv0 - 32 * blk - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + 32 * blk + acc_row(r, hh);
-            const bool ok = key < Sk && (!CAUSAL || key <= my_q + diag);
-            sacc[blk][r] = ok ? sacc[blk][r] : kNegInf;
-        }
+        for (int r = 0; r < 16; ++r) sacc[blk][r] = (8 * (r >> 2) + (r & 3)) <= lim ? sacc[blk][r] : kNegInf;
+    }
 }
 
 template <bool CAUSAL>
