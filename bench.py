@@ -458,18 +458,12 @@ def main():
         if not args.no_fp8:
             log("fp8: quantize + forward")
             rot = to_dev(inputs.bf16_bits(inputs.make_rotation(bs_["d"], seed=2)))
-            names = ("quant_q", "quant_k", "quant_v", "fwd_fp8")
+            names = ("quantize", "fwd_fp8")
 
             def run_fp8(evs=None):
-                calls = (lambda: binding.fa_quantize_fp8(b_q, 128, rot=rot),
-                         lambda: binding.fa_quantize_fp8(b_k, 64, rot=rot),
-                         lambda: binding.fa_quantize_fp8(b_v, 64, layout=binding.FA_FP8_VBLOCKS))
-                outs = []
-                for n, fn in zip(names[:3], calls):
-                    if evs is not None:
-                        binding.fa_time_next_call(*evs[n])
-                    outs.append(fn())
-                (q8, qs), (k8, ks), (v8, vs) = outs
+                if evs is not None:
+                    binding.fa_time_next_call(*evs["quantize"])
+                q8, qs, k8, ks, v8, vs = binding.fa_quantize_fp8_qkv(b_q, b_k, b_v, rot=rot)
                 if evs is not None:
                     binding.fa_time_next_call(*evs["fwd_fp8"])
                 binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, cb.scale, out=b_o, lse=b_l)
@@ -491,9 +485,8 @@ def main():
             tf8 = fl2k / (st["fwd_fp8"]["mean"] * 1e-3) / 1e12
             peak8 = metrics.MI355X_FP8_DENSE_FLOPS / 1e12
             bh_q, bh_kv = bs_["B"] * bs_["Hq"], bs_["B"] * bs_["Hkv"]
-            qbytes = {"quant_q": metrics.fp8_quantize_bytes(bh_q, bs_["Sq"], bs_["d"], 128),
-                      "quant_k": metrics.fp8_quantize_bytes(bh_kv, bs_["Sk"], bs_["d"], 64),
-                      "quant_v": metrics.fp8_quantize_bytes(bh_kv, bs_["Sk"], bs_["d"], 64)}
+            qbytes = (metrics.fp8_quantize_bytes(bh_q, bs_["Sq"], bs_["d"], 128)
+                      + 2 * metrics.fp8_quantize_bytes(bh_kv, bs_["Sk"], bs_["d"], 64))
             total_us = sum(st[n]["mean"] for n in names) * 1e3
             bf16_2k = result["per_config"].get(PREFILL2K, {}).get("launch_us", {}).get("mean")
             result["fp8"] = {
@@ -502,16 +495,16 @@ def main():
                 "traffic": profiling.current_profile(PROFILES["fp8"])["traffic"],
                 "algorithmic_flops_per_launch": fl2k,
                 "launch_us": us(st["fwd_fp8"]),
-                "quantize": {n: {"us": round(st[n]["mean"] * 1e3, 2), "bytes": qbytes[n],
-                                 "GB/s": round(qbytes[n] / (st[n]["mean"] * 1e-3) / 1e9, 1)} for n in qbytes},
+                "quantize": {"kernel": "quant_kernel (Q, K and V in one launch)", "us": round(st["quantize"]["mean"] * 1e3, 2),
+                             "bytes": qbytes, "GB/s": round(qbytes / (st["quantize"]["mean"] * 1e-3) / 1e9, 1)},
                 "quantize_plus_forward_us": round(total_us, 2),
                 "bf16_forward_us": bf16_2k,
                 "note": "E4M3 Q, K (rotated by a seeded orthogonal matrix) and V with power-of-two block scales; "
                         "caches flushed before each quantize + forward sequence",
                 "host_lead": lead_report(lead, host_s),
             }
-            log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q/k/v "
-                f"{st['quant_q']['mean']*1e3:.1f}/{st['quant_k']['mean']*1e3:.1f}/{st['quant_v']['mean']*1e3:.1f} us")
+            log(f"fp8: forward {st['fwd_fp8']['mean']*1e3:.1f} us -> {tf8:.1f} TFLOP/s; quantize q+k+v "
+                f"{st['quantize']['mean']*1e3:.1f} us")
         del b_q, b_k, b_v, b_o, b_l, g_do, b_dq, b_dk, b_dv, b_ws
         torch.cuda.empty_cache()
 

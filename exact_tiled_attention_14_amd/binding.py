@@ -49,6 +49,7 @@ SIGNATURES = {
     "fa_mla_decode": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp, _sz, _vp], _i),
     "fa_quantize_fp8_bytes": ([_i, _i, _i, _i, _i], _sz),
     "fa_quantize_fp8": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp], _i),
+    "fa_quantize_fp8_qkv": ([_vp] * 10 + [_i] * 6 + [_vp], _i),
     "fa_fwd_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "fa_time_next_call": ([_vp, _vp], _i),
     "fa_limit_next_sync_wait": ([_i], _i),
@@ -253,6 +254,41 @@ def fa_quantize_fp8(x, block_rows: int, layout: int = FA_FP8_ROWS, rot=None):
     if st != FA_OK:
         raise FAError("fa_quantize_fp8", st)
     return codes, scales
+
+
+def fa_quantize_fp8_qkv(q, k, v, rot=None):
+    """Q (128-row blocks), K (64-row blocks), both times ``rot`` if given, and
+    V (FA_FP8_VBLOCKS) quantized in one launch.  Returns
+    ``(q8, q_scales, k8, k_scales, v8, v_scales)``, laid out as the three
+    :func:`fa_quantize_fp8` calls would return them."""
+    lib = load()
+    _check(q, "q", torch.bfloat16, 4)
+    _check(k, "k", torch.bfloat16, 4, q.device)
+    _check(v, "v", torch.bfloat16, 4, q.device)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, d) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k={tuple(k.shape)} v={tuple(v.shape)}")
+    if rot is not None:
+        _check(rot, "rot", torch.bfloat16, 2, q.device)
+        if tuple(rot.shape) != (d, d):
+            raise ValueError("rot must be [d, d]")
+    if d != 128:
+        raise FAError("fa_quantize_fp8_qkv", FA_ERR_UNSUPPORTED)
+    u8, dev = torch.uint8, q.device
+    nk = -(-Sk // 64)
+    q8 = torch.empty((B, Hq, Sq, d), dtype=u8, device=dev)
+    qs = torch.empty((B, Hq, -(-Sq // 128)), dtype=u8, device=dev)
+    k8 = torch.empty((B, Hkv, Sk, d), dtype=u8, device=dev)
+    ks = torch.empty((B, Hkv, nk), dtype=u8, device=dev)
+    v8 = torch.empty((B, Hkv, nk, d, 64), dtype=u8, device=dev)
+    vs = torch.empty((B, Hkv, nk), dtype=u8, device=dev)
+    _on_gpu(q, k, v, rot, q8, qs, k8, ks, v8, vs)
+    st = lib.fa_quantize_fp8_qkv(_ptr(q), _ptr(k), _ptr(v), _ptr(rot), _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks),
+                                 _ptr(v8), _ptr(vs), B, Hq, Hkv, Sq, Sk, d, _stream(dev))
+    if st != FA_OK:
+        raise FAError("fa_quantize_fp8_qkv", st)
+    return q8, qs, k8, ks, v8, vs
 
 
 def fa_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, scale: float | None = None, out=None,

@@ -158,6 +158,24 @@ int fa_quantize_fp8(const void* x, const void* rot, void* x8, uint8_t* scales, i
     return fa::launch_quant_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_quantize_fp8_qkv(const void* q, const void* k, const void* v, const void* rot, void* q8,
+                        uint8_t* q_scales, void* k8, uint8_t* k_scales, void* v8, uint8_t* v_scales, int B,
+                        int Hq, int Hkv, int Sq, int Sk, int d, void* stream) {
+    TimingScope timing_scope;
+    if (!q || !k || !v || !q8 || !k8 || !v8 || !q_scales || !k_scales || !v_scales) return FA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8) ||
+        (rot && !aligned16(rot)))
+        return FA_ERR_INVALID_ARG;
+    if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk + 63, d)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    const fa::QuantArgs aq{q, rot, q8, q_scales, (int64_t)B * Hq, Sq, 128, FA_FP8_ROWS};
+    const fa::QuantArgs ak{k, rot, k8, k_scales, (int64_t)B * Hkv, Sk, 64, FA_FP8_ROWS};
+    const fa::QuantArgs av{v, nullptr, v8, v_scales, (int64_t)B * Hkv, Sk, 64, FA_FP8_VBLOCKS};
+    return fa::launch_quant_fp8_qkv(aq, ak, av, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK
+                                                                                                     : FA_ERR_HIP;
+}
+
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
                const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
                float scale, void* stream) {

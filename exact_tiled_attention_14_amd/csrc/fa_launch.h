@@ -137,6 +137,9 @@ struct Fp8FwdArgs {
 };
 
 hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t stream);
+// Q (128-row blocks, rotated), K (64-row blocks, rotated) and V (64-key d-major
+// blocks) in one launch; the rotation is q.rot (k.rot must be the same).
+hipError_t launch_quant_fp8_qkv(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t stream);
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);

@@ -40,8 +40,8 @@
  * Entry points: fa_fwd (prefill, bf16 or fp32), fa_bwd (its gradients),
  * fa_decode (one new token per sequence, paged cache), fa_decode_multi (Sq new
  * tokens per sequence, paged cache), fa_mla_decode (one new token per
- * sequence, paged latent cache), fa_quantize_fp8 and fa_fwd_fp8 (FP8
- * forward with block scales), fa_time_next_call (measurement), plus the
+ * sequence, paged latent cache), fa_quantize_fp8, fa_quantize_fp8_qkv and
+ * fa_fwd_fp8 (FP8 forward with block scales), fa_time_next_call (measurement), plus the
  * *_workspace_size / *_bytes size queries and fa_status_string.
  */
 #ifndef EXACT_TILED_ATTENTION_FA_H
@@ -339,6 +339,31 @@ size_t fa_quantize_fp8_bytes(int B, int H, int S, int d, int layout);
  */
 int fa_quantize_fp8(const void* x, const void* rot, void* x8, uint8_t* scales, int B, int H, int S, int d,
                     int block_rows, int layout, void* stream);
+
+/*
+ * fa_quantize_fp8_qkv - the three quantizations fa_fwd_fp8 needs, in one
+ * launch: Q in 128-row blocks and K in 64-row blocks (FA_FP8_ROWS, both
+ * multiplied by the same rot, or neither when rot is NULL) and V in
+ * FA_FP8_VBLOCKS 64-key blocks.
+ *
+ * Passage: as fa_quantize_fp8 ("FlashAttention scaling, multi-GPU training
+ * and weight quantization", section 1, FP8 support and incoherent
+ * processing).
+ *
+ *   q [B, Hq, Sq, d], k and v [B, Hkv, Sk, d]: bf16, device, read-only.
+ *   q8/q_scales, k8/k_scales, v8/v_scales: outputs laid out and sized
+ *   exactly as the three fa_quantize_fp8 calls (q, rot, 128, FA_FP8_ROWS),
+ *   (k, rot, 64, FA_FP8_ROWS) and (v, NULL, 64, FA_FP8_VBLOCKS) would write
+ *   them; the codes and scales are bit-identical to theirs.
+ *
+ * Pointers to tensors and codes must be 16-byte aligned and the outputs must
+ * not overlap the inputs or each other.  d must be 128, else
+ * FA_ERR_UNSUPPORTED.  Runs on `stream`; allocates nothing.
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_quantize_fp8_qkv(const void* q, const void* k, const void* v, const void* rot, void* q8,
+                        uint8_t* q_scales, void* k8, uint8_t* k_scales, void* v8, uint8_t* v_scales, int B,
+                        int Hq, int Hkv, int Sq, int Sk, int d, void* stream);
 
 /*
  * fa_fwd_fp8 - attention forward on FP8 inputs (FP8 matrix-core products).

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
                            "fa_decode_multi_workspace_size", "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd",
                            "fa_fwd_fp8", "fa_limit_next_sync_wait", "fa_mla_decode", "fa_mla_decode_workspace_size",
-                           "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_status_string", "fa_sync_timeouts",
+                           "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_quantize_fp8_qkv", "fa_status_string",
+                           "fa_sync_timeouts",
                            "fa_time_next_call"]
 
 
@@ -178,6 +179,22 @@ def _quant(lib, x=16, rot=0, x8=32, sc=48, B=1, H=2, S=100, d=128, rows=64, layo
 ])
 def test_quantize_fp8_rejects_before_launch(lib, kw, status):
     assert _quant(lib, **kw) == status
+
+
+def _quant_qkv(lib, q=16, k=32, v=48, rot=0, q8=64, qs=1, k8=80, ks=2, v8=96, vs=3, B=1, Hq=2, Hkv=1, Sq=8, Sk=8,
+               d=128):
+    P = ctypes.c_void_p
+    return lib.fa_quantize_fp8_qkv(P(q), P(k), P(v), P(rot) if rot else None, P(q8), P(qs), P(k8), P(ks), P(v8),
+                                   P(vs), B, Hq, Hkv, Sq, Sk, d, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(v=0), -1), (dict(q8=0), -1), (dict(vs=0), -1), (dict(B=0), -1), (dict(Sk=0), -1),
+    (dict(k=40), -1), (dict(v8=104), -1), (dict(rot=72), -1), (dict(Hkv=0), -1),
+    (dict(d=64), -2),
+])
+def test_quantize_fp8_qkv_rejects_before_launch(lib, kw, status):
+    assert _quant_qkv(lib, **kw) == status
 
 
 def _fwd8(lib, q=16, k=32, v=48, qs=1, ks=2, vs=3, o=64, lse=0, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=128, causal=1,

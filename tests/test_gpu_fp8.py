@@ -194,13 +194,61 @@ def test_quantize_rotated(B):
     assert (np.sign(a) * np.sign(b_) >= 0).all()
 
 
+def _scaled_heads(x):
+    """x with its heads multiplied by factors from 0.01 to 40 (several block
+    scale exponents), rounded to bf16."""
+    f = np.float32(np.linspace(0.01, 40, x.shape[1]))[None, :, None, None]
+    return I.round_to_bf16((x * f).astype(np.float32))
+
+
+@pytest.mark.parametrize("Bn,Hq,Hkv,Sq,Sk", [(2, 4, 2, 200, 333), (1, 3, 1, 1, 64), (1, 2, 2, 383, 65)])
+def test_quantize_qkv_unrotated_bit_exact(B, Bn, Hq, Hkv, Sq, Sk):
+    """The one-launch quantizer without rotation: Q (128-row blocks), K
+    (64-row blocks) and V (d-major 64-key blocks) equal the oracle's codes and
+    scales bit for bit, ragged ends included."""
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=False, seed=400 + Sq + Sk)
+    q, k, v = _scaled_heads(c.q), _scaled_heads(c.k), _scaled_heads(c.v)
+    q8, qs, k8, ks, v8, vs = B.fa_quantize_fp8_qkv(_bf(q), _bf(k), _bf(v))
+    for got_c, got_s, x, rows in ((q8.cpu().numpy(), qs, q, 128), (k8.cpu().numpy(), ks, k, 64),
+                                  (unblock_v(v8), vs, v, 64)):
+        want_c, want_e = F.quantize_blocks(x, rows)
+        S = x.shape[2]
+        assert np.array_equal(got_c[:, :, :S], want_c)
+        assert (got_c[:, :, S:] == 0).all()
+        assert np.array_equal(got_s.cpu().numpy().astype(np.int64) - 127, want_e)
+
+
+@pytest.mark.parametrize("shape", [(2, 16, 16, 2048, 2048), (1, 8, 2, 1000, 777)], ids=["b2h16s2048", "gqa-ragged"])
+def test_quantize_qkv_rotated_matches_oracle_and_separate_calls(B, shape):
+    """With the rotation: the one launch writes exactly what the three
+    single-tensor calls write, its scales equal the oracle's, and its Q and K
+    codes differ from the oracle's only at elements the oracle finds
+    ambiguous."""
+    Bn, Hq, Hkv, Sq, Sk = shape
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=True, seed=500 + Sq, outlier_frac=0.001)
+    R = I.make_rotation(128, seed=500)
+    bq, bk, bv, bR = _bf(c.q), _bf(c.k), _bf(c.v), _bf(R)
+    fused = B.fa_quantize_fp8_qkv(bq, bk, bv, rot=bR)
+    sep = (*B.fa_quantize_fp8(bq, 128, rot=bR), *B.fa_quantize_fp8(bk, 64, rot=bR),
+           *B.fa_quantize_fp8(bv, 64, layout=B.FA_FP8_VBLOCKS))
+    torch.cuda.synchronize()
+    for a, b_ in zip(fused, sep):
+        assert a.shape == b_.shape and torch.equal(a, b_)
+    for codes, sc, x, rows in ((fused[0], fused[1], c.q, 128), (fused[2], fused[3], c.k, 64)):
+        want_c, want_e = F.quantize_blocks(x, rows, rot=R)
+        assert np.array_equal(sc.cpu().numpy().astype(np.int64) - 127, want_e)
+        diff = codes.cpu().numpy() != want_c
+        assert not (diff & ~ambiguous_mask(x, R, rows)).any()
+    want_c, want_e = F.quantize_blocks(c.v, 64)
+    assert np.array_equal(unblock_v(fused[4])[:, :, :Sk], want_c)
+    assert np.array_equal(fused[5].cpu().numpy().astype(np.int64) - 127, want_e)
+
+
 # --- attention -----------------------------------------------------------------------
 
 def run_fp8(Bm, c, rot):
     R = _bf(rot) if rot is not None else None
-    q8, qs = Bm.fa_quantize_fp8(_bf(c.q), 128, rot=R)
-    k8, ks = Bm.fa_quantize_fp8(_bf(c.k), 64, rot=R)
-    v8, vs = Bm.fa_quantize_fp8(_bf(c.v), 64, layout=Bm.FA_FP8_VBLOCKS)
+    q8, qs, k8, ks, v8, vs = Bm.fa_quantize_fp8_qkv(_bf(c.q), _bf(c.k), _bf(c.v), rot=R)
     o, lse = Bm.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, c.causal, c.scale)
     torch.cuda.synchronize()
     return _np(o), lse.cpu().numpy().astype(np.float64)
