@@ -95,13 +95,11 @@ def _run(args) -> None:
         c = inputs.workload(PREFILL)
         fq, fk, fv = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
         rot = to_dev(inputs.bf16_bits(inputs.make_rotation(c.q.shape[-1], seed=2)))
-        q8, qs = binding.fa_quantize_fp8(fq, 128, rot=rot)
-        k8, ks = binding.fa_quantize_fp8(fk, 64, rot=rot)
-        v8, vs = binding.fa_quantize_fp8(fv, 64, layout=binding.FA_FP8_VBLOCKS)
+        q8, qs, k8, ks, v8, vs = binding.fa_quantize_fp8_qkv(fq, fk, fv, rot=rot)
         fo = torch.empty_like(fq)
         fl = torch.empty(fq.shape[:3], dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
-        launches.append(("fp8_quantize_q", lambda: binding.fa_quantize_fp8(fq, 128, rot=rot)))
+        launches.append(("fp8_quantize_qkv", lambda: binding.fa_quantize_fp8_qkv(fq, fk, fv, rot=rot)))
         launches.append(("fp8_forward", lambda: binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale, out=fo,
                                                                    lse=fl)))
     if args.workload in ("verify", "all"):
