@@ -99,79 +99,6 @@ def lead_report(lead, host_s):
             "host_ahead": bool(host_s * 1e3 < spin_ms)}
 
 
-class GfxClock:
-    """Samples the shader (GFX) clock and the socket power with amdsmi while
-    the GPU works through a queued loop.  Fractions of peak are quoted against
-    the 2.4 GHz peak clock; under sustained matrix-core load the clock and power
-    limits say how far the chip actually ran from it.  Every method returns
-    None / [] when amdsmi is not usable on the machine."""
-
-    def __init__(self):
-        self.h = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            hs = amdsmi.amdsmi_get_processor_handles()
-            if hs:
-                self.h, self.smi = hs[0], amdsmi
-        except Exception:
-            self.h = None
-
-    @staticmethod
-    def _num(x):
-        if isinstance(x, (list, tuple)):
-            v = [float(e) for e in x if isinstance(e, (int, float))]
-            return sorted(v)[len(v) // 2] if v else None
-        return float(x) if isinstance(x, (int, float)) else None
-
-    def read(self):
-        """{name: value} of this instant (MHz, W), values that the driver does not report left out."""
-        if self.h is None:
-            return {}
-        out = {}
-        try:
-            m = self.smi.amdsmi_get_gpu_metrics_info(self.h)
-            for key, name in (("current_gfxclks", "current_gfxclk_mhz"), ("current_gfxclk", "current_gfxclk_mhz"),
-                              ("average_gfxclk_frequency", "average_gfxclk_mhz"),
-                              ("average_socket_power", "socket_power_w")):
-                v = self._num(m.get(key))
-                if v is not None and name not in out:
-                    out[name] = v
-        except Exception:
-            pass
-        if "current_gfxclk_mhz" not in out:
-            try:
-                out["current_gfxclk_mhz"] = float(
-                    self.smi.amdsmi_get_clock_info(self.h, self.smi.AmdSmiClkType.GFX)["clk"])
-            except Exception:
-                pass
-        return out
-
-    def sample_until(self, done, start=None, period_s=0.0005, max_s=10.0):
-        """Samples from the completion of the torch event `start` (if given)
-        until the completion of `done`."""
-        out, t0 = [], time.perf_counter()
-        while start is not None and not start.query() and time.perf_counter() - t0 < max_s:
-            time.sleep(period_s)
-        while self.h is not None and not done.query() and time.perf_counter() - t0 < max_s:
-            v = self.read()
-            if v:
-                out.append(v)
-            time.sleep(period_s)
-        return out
-
-
-def clock_report(samples):
-    """Medians (and the sample count) of each quantity; None without samples."""
-    if not samples:
-        return None
-    rep = {"samples": len(samples)}
-    for name in sorted({k for s in samples for k in s}):
-        x = sorted(s[name] for s in samples if name in s)
-        rep[name] = x[len(x) // 2]
-    return rep
-
-
 def kernel_events(n):
     """n (start, stop) pairs of timing events for fa_time_next_call."""
     from exact_tiled_attention_14_amd import binding
@@ -266,7 +193,6 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    clock = GfxClock()
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -295,8 +221,6 @@ def main():
         run_decode()
     t_end.record(stream)
     host_s = time.perf_counter() - host0
-    # the shader clock while the timed steps run (mostly the 32k prefill)
-    samples = clock.sample_until(t_end, start=lead[1])
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / K
@@ -330,7 +254,6 @@ def main():
     headline_roof = prefill_roofline("fwd_bf16_kernel<128,causal,grid>", flops_p, sp, PROFILES[HEADLINE],
                                      "runs after the previous step's decode; 8 ms per launch, so the "
                                      "caches' start state matters little")
-    headline_roof["gfx_clock_under_load"] = clock_report(samples[len(samples) // 4:])
     decode_block = {
         "workload": DECODE,
         "kernels": "decode_partial_kernel<4> + decode_combine_kernel<4>",
@@ -377,7 +300,7 @@ def main():
 
     def time_calls(fn, reps, flush, lead_ms_per_rep):
         """Launch statistics of `reps` calls of fn, each preceded by a cache flush
-        (outside its events) when `flush`; the shader clock is sampled while they run."""
+        (outside its events) when `flush`."""
         for _ in range(2):
             fn()
         evs = kernel_events(reps)
@@ -390,12 +313,9 @@ def main():
             binding.fa_time_next_call(a, b)
             fn()
         host_s = time.perf_counter() - host0
-        done = torch.cuda.Event()
-        done.record(stream)
-        samples = clock.sample_until(done, start=lead[1])
         torch.cuda.synchronize()
         st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
-        return st, lead_report(lead, host_s), clock_report(samples[len(samples) // 4:])
+        return st, lead_report(lead, host_s)
 
     # ---- the 2k and 8k prefill workloads, each on its own, cold caches ----
     if not args.no_extra:
@@ -408,7 +328,7 @@ def main():
             o = torch.empty_like(q)
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
             scale = 1.0 / math.sqrt(s["d"])
-            st, lead_x, clk = time_calls(lambda: binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse), reps, True,
+            st, lead_x = time_calls(lambda: binding.fa_fwd(q, k, v, True, scale, out=o, lse=lse), reps, True,
                                          0.3)
             fl = metrics.prefill_flops(s["B"], s["Hq"], s["Sq"], s["Sk"], s["d"], True)
             # (the launch's choice: a causal square problem whose heavy/light query-block
@@ -417,8 +337,7 @@ def main():
                     and s["B"] * s["Hq"] * ((s["Sq"] // 128 + 1) // 2) <= torch.cuda.get_device_properties(dev).multi_processor_count)
             roof = prefill_roofline("fwd_bf16_kernel<128,causal,%s>" % ("pair" if pair else "grid"), fl, st,
                                     PROFILES[name], "flushed (512 MiB read) before each launch, outside its events")
-            roof.update({"reps": reps, "host_lead": lead_x, "gfx_clock_under_load": clk,
-                         "shape": {k_: s[k_] for k_ in ("B", "Hq", "Hkv", "Sq", "Sk", "d")}})
+            roof.update({"reps": reps, "host_lead": lead_x, "shape": {k_: s[k_] for k_ in ("B", "Hq", "Hkv", "Sq", "Sk", "d")}})
             result["per_config"][name] = roof
             log(f"{name}: {st['mean']*1e3:.1f} us -> {roof['achieved']:.1f} TFLOP/s ({roof['frac']:.3f} of peak)")
             del q, k, v, o, lse
@@ -441,7 +360,7 @@ def main():
             binding.fa_bwd(b_q, b_k, b_v, b_o, g_do, b_l, True, cb.scale, dq=b_dq, dk=b_dk, dv=b_dv, workspace=b_ws)
 
         if not args.no_backward:
-            st, lead_b, _ = time_calls(run_bwd, max(5, min(K, 20)), True, 0.4)
+            st, lead_b = time_calls(run_bwd, max(5, min(K, 20)), True, 0.4)
             fl = metrics.backward_flops(bs_["B"], bs_["Hq"], bs_["Sq"], bs_["Sk"], bs_["d"], True)
             tf = fl / (st["mean"] * 1e-3) / 1e12
             result["backward"] = {
@@ -522,7 +441,7 @@ def main():
         v_ws = torch.empty(binding.fa_decode_multi_workspace_size(vshp["nseq"], vshp["Sq"], vshp["Hq"], vshp["Hkv"],
                                                                   vshp["d"], vshp["block_size"], vshp["max_blocks"]),
                            dtype=torch.uint8, device=dev)
-        st, lead_v, _ = time_calls(lambda: binding.fa_decode_multi(v_q, v_kc, v_vc, v_bt, v_sl, cv.scale, out=v_o,
+        st, lead_v = time_calls(lambda: binding.fa_decode_multi(v_q, v_kc, v_vc, v_bt, v_sl, cv.scale, out=v_o,
                                                                    lse=v_l, workspace=v_ws),
                                    max(5, min(K, 20)), True, 0.4)
         vbytes = metrics.decode_kv_bytes(cv.seqlens, vshp["Hkv"], vshp["d"])
@@ -556,7 +475,7 @@ def main():
         m_ws = torch.empty(binding.fa_mla_decode_workspace_size(msh["nseq"], msh["H"], msh["d_h"], msh["d_c"],
                                                                 msh["block_size"], msh["max_blocks"]),
                            dtype=torch.uint8, device=dev)
-        st, lead_m, _ = time_calls(lambda: binding.fa_mla_decode(m_q, m_wk, m_wv, m_cc, m_bt, m_sl, cm.scale, out=m_o,
+        st, lead_m = time_calls(lambda: binding.fa_mla_decode(m_q, m_wk, m_wv, m_cc, m_bt, m_sl, cm.scale, out=m_o,
                                                                  lse=m_l, workspace=m_ws),
                                    max(5, min(K, 20)), True, 0.4)
         lat_bytes = metrics.mla_latent_bytes(cm.cache.seqlens, msh["d_c"])
