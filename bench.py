@@ -72,6 +72,7 @@ PROFILES = {
     PREFILL2K: _profile("fwd_bf16_causal_mha_b2_h16_s2048_d128"),
     DECODE: _profile("decode_paged_64seq_h32kv8_d128"),
     "fp8": _profile("fwd_fp8_causal_mha_b2_h16_s2048_d128"),
+    "quant": _profile("quant_fp8_qkv_b2_h16_s2048_d128"),
     VERIFY: _profile("decode_multi_paged_64seq_q8_h32kv8_d128"),
     MLA: _profile("mla_decode_64seq_h16_dc512"),
 }
@@ -415,7 +416,9 @@ def main():
                 "algorithmic_flops_per_launch": fl2k,
                 "launch_us": us(st["fwd_fp8"]),
                 "quantize": {"kernel": "quant_kernel (Q, K and V in one launch)", "us": round(st["quantize"]["mean"] * 1e3, 2),
-                             "bytes": qbytes, "GB/s": round(qbytes / (st["quantize"]["mean"] * 1e-3) / 1e9, 1)},
+                             "bytes": qbytes, "GB/s": round(qbytes / (st["quantize"]["mean"] * 1e-3) / 1e9, 1),
+                             "frac": round(qbytes / (st["quantize"]["mean"] * 1e-3) / 1e9 / peak_gb, 4),
+                             "traffic": profiling.current_profile(PROFILES["quant"])["traffic"]},
                 "quantize_plus_forward_us": round(total_us, 2),
                 "bf16_forward_us": bf16_2k,
                 "note": "E4M3 Q, K (rotated by a seeded orthogonal matrix) and V with power-of-two block scales; "

@@ -344,6 +344,27 @@ def test_binding_rejects_host_tensors_after_shape_checks(lib):
         b.fa_fwd(_bf(1, 2, 8, 128), _bf(1, 1, 8, 128), _bf(1, 1, 8, 128), True)
 
 
+@pytest.mark.parametrize("case", ["k_shape", "v_shape", "rot_shape", "head_dim"])
+def test_quantize_qkv_binding_checks_shapes_first(lib, case):
+    """The one-launch quantizer's binding refuses mismatched shapes (and a
+    head dimension the kernels do not build) before the GPU check and any
+    launch; CPU tensors with consistent shapes reach the GPU check."""
+    from exact_tiled_attention_14_amd import binding as b
+    q, k, v, rot = _bf(1, 4, 100, 128), _bf(1, 2, 70, 128), _bf(1, 2, 70, 128), None
+    if case == "k_shape":
+        k = _bf(1, 2, 70, 64)
+    elif case == "v_shape":
+        v = _bf(1, 2, 71, 128)
+    elif case == "rot_shape":
+        rot = _bf(128, 64)
+    else:
+        q, k, v = _bf(1, 4, 100, 64), _bf(1, 2, 70, 64), _bf(1, 2, 70, 64)
+    with pytest.raises((ValueError, b.FAError)):
+        b.fa_quantize_fp8_qkv(q, k, v, rot=rot)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        b.fa_quantize_fp8_qkv(_bf(1, 4, 100, 128), _bf(1, 2, 70, 128), _bf(1, 2, 70, 128))
+
+
 def test_sync_hooks_validate_on_the_host(lib):
     assert lib.fa_limit_next_sync_wait(-1) == -1
     assert lib.fa_sync_timeouts(None) == -1
