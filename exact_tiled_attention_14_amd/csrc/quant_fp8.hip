@@ -27,6 +27,8 @@
 #include "fa_device.h"
 #include "fa_launch.h"
 
+#include <atomic>
+
 namespace fa {
 namespace {
 
@@ -356,12 +358,22 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantParts parts, c
     }
 }
 
+// Resident workgroups of quant_kernel on the current device (queried once per
+// device).
 int quant_slots() {
-    int dev = 0, n = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0, per_cu = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
         n = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_kernel, kQThreads, 0) != hipSuccess || per_cu <= 0)
         per_cu = 2;
+    if (dev >= 0 && dev < 64) cache[dev].store(per_cu * n, std::memory_order_relaxed);
     return per_cu * n;
 }
 
