@@ -328,16 +328,25 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         store_rows(dV + bhk * Sk * kD, dv, 1.f, my_k, Sk, hh);
         return;
     }
-    auto step_src = [&](int t, int64_t& bhq, int& q0) {
-        bhq = (int64_t)b * Hq + kvh * g + t / per_head;
-        q0 = (qb0 + t % per_head) * kQBlk;
+    // A step is (query head h of the group, Q block qb0 + i); the loop carries
+    // (h, i) and advances it with one compare instead of dividing the step
+    // index by the blocks per head.
+    struct StepIx {
+        int h, i;
     };
-    // Q and dO rows of step t into a stage (rows past Sq repeat row Sq-1);
+    auto next_ix = [&](StepIx x) {
+        return ++x.i == per_head ? StepIx{x.h + 1, 0} : x;
+    };
+    auto step_src = [&](StepIx x, int64_t& bhq, int& q0) {
+        bhq = (int64_t)b * Hq + kvh * g + x.h;
+        q0 = (qb0 + x.i) * kQBlk;
+    };
+    // Q and dO rows of step x into a stage (rows past Sq repeat row Sq-1);
     // lanes tid < kQBlk also load the raw lse and D of their row
-    auto fetch = [&](int t, uint8_t* __restrict__ st, float& l, float& d) {
+    auto fetch = [&](StepIx x, uint8_t* __restrict__ st, float& l, float& d) {
         int64_t bhq;
         int q0;
-        step_src(t, bhq, q0);
+        step_src(x, bhq, q0);
         dma_rows<kQBlk>(Q + bhq * Sq * kD, st, q0, Sq, wave, lane);
         dma_rows<kQBlk>(dO + bhq * Sq * kD, st + kQBlk * kROWB, q0, Sq, wave, lane);
         if (tid < kQBlk) {
@@ -348,11 +357,11 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     };
     // once those loads have landed: the lse offset and D the products use (a
     // row past Sq or with no visible key gets offset +inf, so p = 0, and D = 0)
-    auto put_rowvals = [&](int t, uint8_t* __restrict__ st, float l, float d) {
+    auto put_rowvals = [&](StepIx x, uint8_t* __restrict__ st, float l, float d) {
         if (tid < kQBlk) {
             int64_t bhq_unused;
             int q0;
-            step_src(t, bhq_unused, q0);
+            step_src(x, bhq_unused, q0);
             const bool ok = q0 + tid < Sq;
             float* f = reinterpret_cast<float*>(st + 2 * kQBlk * kROWB);
             f[tid] = ok ? lse_offset(l) : __builtin_inff();
@@ -390,9 +399,9 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     asm volatile("" : "+v"(fo));
 
     float lraw = 0.f, draw = 0.f;
-    fetch(0, lds[0], lraw, draw);
+    fetch(StepIx{0, 0}, lds[0], lraw, draw);
     wait_vm();
-    put_rowvals(0, lds[0], lraw, draw);
+    put_rowvals(StepIx{0, 0}, lds[0], lraw, draw);
     __syncthreads();
 
     u32x4 pw_prev[2], dsw_prev[2];   // P and dS of the previous step, bf16 B operands
@@ -430,12 +439,13 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     // Step t: its rows are in stage cur, step t-1's in prev (FIRST: none),
     // step t+1's rows go to nxt.  The stages come in as restrict pointers, so
     // the operand reads of two do not wait for the loads into the third.
-    auto step = [&](auto first_c, const int t, uint8_t* __restrict__ cur, uint8_t* __restrict__ prev,
+    auto step = [&](auto first_c, const int t, const StepIx x, uint8_t* __restrict__ cur, uint8_t* __restrict__ prev,
                     uint8_t* __restrict__ nxt) __attribute__((always_inline)) {
         constexpr bool FIRST = decltype(first_c)::value;
         const bool has_next = t + 1 < n_steps;
+        const StepIx xn = next_ix(x);
         float lnext = 0.f, dnext = 0.f;
-        if (has_next) fetch(t + 1, nxt, lnext, dnext);
+        if (has_next) fetch(xn, nxt, lnext, dnext);
 
         // S = Q K^T and dP = dO V^T: register r is query row q0 + acc_row(r, hh),
         // lane = key; Q and dO operands read two products ahead
@@ -476,7 +486,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         }
         int64_t bhq_unused;
         int q0;
-        step_src(t, bhq_unused, q0);
+        step_src(x, bhq_unused, q0);
         // causal: key my_k is visible to row q iff q >= my_k - diag, i.e. the
         // register's constant row offset 8 (r / 4) + r % 4 >= thr
         const int thr = my_k - diag - q0 - 4 * hh;
@@ -509,7 +519,7 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         }
         if (has_next) {
             wait_vm();
-            put_rowvals(t + 1, nxt, lnext, dnext);
+            put_rowvals(xn, nxt, lnext, dnext);
         }
         // step t+1's rows are in place; every wave is done with stage prev
         __syncthreads();
@@ -520,13 +530,15 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     uint8_t* const st0 = lds[0];
     uint8_t* const st1 = lds[1];
     uint8_t* const st2 = lds[2];
-    step(First{}, 0, st0, st2, st1);
+    StepIx x{0, 0};
+    step(First{}, 0, x, st0, st2, st1);
     for (int t = 1; t < n_steps; ++t) {
+        x = next_ix(x);
         // the three stage bases as opaque scalars: one add per operand address
         uint32_t bc = (uint32_t)(t % kQStages) * kQStage, bp = (uint32_t)((t + 2) % kQStages) * kQStage,
                  bn = (uint32_t)((t + 1) % kQStages) * kQStage;
         asm volatile("" : "+s"(bc), "+s"(bp), "+s"(bn));
-        step(Later{}, t, &lds[0][0] + bc, &lds[0][0] + bp, &lds[0][0] + bn);
+        step(Later{}, t, x, &lds[0][0] + bc, &lds[0][0] + bp, &lds[0][0] + bn);
     }
     // the last step's dV and dK products
     {
