@@ -240,17 +240,27 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
                 st[blk] = mfma32(ring[j & 1], qf[s], st[blk]);
             BWD_FENCE();
         }
-        // dS^T = P^T o (dP^T - D): register r of block blk is key kv0 + 32 blk + acc_row(r, hh)
+        // dS^T = P^T o (dP^T - D): register r of block blk is key kv0 + 32 blk +
+        // acc_row(r, hh).  Only a block that crosses the wave's diagonal or
+        // runs past Sk is masked (a wave-uniform test); there key acc_row(r)
+        // of half-block blk is kept iff 8 (r / 4) + r % 4 <= lim, one limit
+        // per lane and half-block.
+        const bool masked = (kv0 + kKVBlk > Sk) || (CAUSAL && kv0 + kKVBlk - 1 > qb * kQRows + wave * 32 + diag);
+        const int last = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;     // last key this row may see
         u32x4 dsw[4];
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             float ds[16];
+            if (masked) {
+                const int lim = last - kv0 - 32 * blk - 4 * hh;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kv0 + 32 * blk + acc_row(r, hh);
-                const bool ok = key < Sk && (!CAUSAL || key <= my_q + diag);
-                const float p = ok ? exp2f_hw(fmaf(st[blk][r], scale_log2, -lo)) : 0.f;
-                ds[r] = p * (pt[blk][r] - Dq);
+                for (int r = 0; r < 16; ++r) {
+                    const float p = 8 * (r >> 2) + (r & 3) <= lim ? exp2f_hw(fmaf(st[blk][r], scale_log2, -lo)) : 0.f;
+                    ds[r] = p * (pt[blk][r] - Dq);
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) ds[r] = exp2f_hw(fmaf(st[blk][r], scale_log2, -lo)) * (pt[blk][r] - Dq);
             }
             u32x4 two[2];
             pack_operand(two, ds);
