@@ -186,15 +186,24 @@ __global__ __launch_bounds__(kThreadsM, 2) void mq_partial_kernel(
             const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * i + hh) ^ sw_k));
             sacc = mfma32(ka, qf[i], sacc);
         }
-        // mask: keys of the step are pages pa, pa + 1 of this wave
+        // mask: keys of the step are pages pa, pa + 1 of this wave.  A step
+        // whose 32 keys all lie in usable pages and at or before the first new
+        // token's position (so every row sees them) needs none (a wave-uniform
+        // test); padding rows past R then score against zero queries, and
+        // their results are never written.
         float mx = kNegInf;
+        if (ok0 && ok1 && pa * kPage + 31 <= len - Sq) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int kk = acc_row(r, hh);                // key of the step, 0 .. 31
-            const int pos = pa * kPage + kk;
-            const bool ok = row_ok && (kk < 16 ? ok0 : ok1) && pos < len && pos <= lim;
-            sacc[r] = ok ? sacc[r] : kNegInf;
-            mx = fmaxf(mx, sacc[r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = acc_row(r, hh);            // key of the step, 0 .. 31
+                const int pos = pa * kPage + kk;
+                const bool ok = row_ok && (kk < 16 ? ok0 : ok1) && pos < len && pos <= lim;
+                sacc[r] = ok ? sacc[r] : kNegInf;
+                mx = fmaxf(mx, sacc[r]);
+            }
         }
         mx = half_swap_max(mx) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kTauM)) {
