@@ -312,17 +312,27 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
         for (int w = 0; w < 4; ++w)
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb) sa[tb] += *reinterpret_cast<const f32x4*>(xs[w][tb] + lane * 4);
-        // mask; token of (tb, e) is 16 tb + 4 g + e
+        // mask; token of (tb, e) is 16 tb + 4 g + e.  A step whose 32 tokens
+        // all lie in usable pages before the length needs none (a
+        // wave-uniform test); padding heads then score against zero
+        // queries, and their results are never written.
         float mx = kNegInf;
+        if (ok0 && ok1 && pa * kPageM + 32 <= len) {
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+            for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int kk = 16 * tb + 4 * g + e;
-                const bool ok = row_ok && (tb == 0 ? ok0 : ok1) && pa * kPageM + kk < len;
-                sa[tb][e] = ok ? sa[tb][e] : kNegInf;
-                mx = fmaxf(mx, sa[tb][e]);
-            }
+                for (int e = 0; e < 4; ++e) mx = fmaxf(mx, sa[tb][e]);
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int kk = 16 * tb + 4 * g + e;
+                    const bool ok = row_ok && (tb == 0 ? ok0 : ok1) && pa * kPageM + kk < len;
+                    sa[tb][e] = ok ? sa[tb][e] : kNegInf;
+                    mx = fmaxf(mx, sa[tb][e]);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
         if (__builtin_amdgcn_ballot_w64(mx > m_run + kTauL)) {
