@@ -479,21 +479,13 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
                 BWD_FENCE();
             }
         }
-        // the rows' lse offsets and D: four groups of four consecutive rows
-        float lo_r[16], dd_r[16];
-        {
-            const float* f = reinterpret_cast<const float*>(cur + fo);
-#pragma unroll
-            for (int grp = 0; grp < 4; ++grp) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(f + 8 * grp);
-                const f32x4 y = *reinterpret_cast<const f32x4*>(f + kQBlk + 8 * grp);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lo_r[4 * grp + e] = x[e];
-                    dd_r[4 * grp + e] = y[e];
-                }
-            }
-        }
+        // the rows' lse offsets and D come in four groups of four consecutive
+        // rows; a group is read from the stage one group ahead of its use (two
+        // groups in registers instead of all 32 values)
+        const float* const rowf = reinterpret_cast<const float*>(cur + fo);
+        f32x4 lo_g[2], dd_g[2];
+        lo_g[0] = *reinterpret_cast<const f32x4*>(rowf);
+        dd_g[0] = *reinterpret_cast<const f32x4*>(rowf + kQBlk);
         int64_t bhq_unused;
         int q0;
         step_src(x, bhq_unused, q0);
@@ -503,12 +495,18 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         u32x4 pw[2], dsw[2];
         float pv[16], dsv[16];
         auto unit = [&](int r) {
-            float x = fmaf(sc[r], scale_log2, -lo_r[r]);
+            const int grp = r >> 2;
+            if ((r & 3) == 0 && grp + 1 < 4) {
+                lo_g[(grp + 1) & 1] = *reinterpret_cast<const f32x4*>(rowf + 8 * (grp + 1));
+                dd_g[(grp + 1) & 1] = *reinterpret_cast<const f32x4*>(rowf + kQBlk + 8 * (grp + 1));
+            }
+            const float lo_r = lo_g[grp & 1][r & 3], dd_r = dd_g[grp & 1][r & 3];
+            float x = fmaf(sc[r], scale_log2, -lo_r);
             asm volatile("" : "+v"(x));
             float e = exp2f_hw(x);
             if (CAUSAL) e = (8 * (r >> 2) + (r & 3)) >= thr ? e : 0.f;
             pv[r] = e;
-            dsv[r] = e * (pc[r] - dd_r[r]);
+            dsv[r] = e * (pc[r] - dd_r);
             if (r & 1) {
                 uint32_t wp = pack_bf16x2(pv[r - 1], pv[r]), wd = pack_bf16x2(dsv[r - 1], dsv[r]);
                 asm volatile("" : "+v"(wp), "+v"(wd));
