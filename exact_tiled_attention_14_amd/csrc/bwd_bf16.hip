@@ -384,7 +384,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     // them opaque, so the compiler neither re-derives them per stage nor
     // keeps one copy per stage.)
     uint32_t ro[kD / 16];               // Q / dO row operand of head-dim step s
-    uint32_t to[2][kD / 32][2];         // transposed operand (ks, db), two reads
+    uint32_t to[kD / 32][2];            // transposed operand (ks = 0, db), two reads; ks = 1 is
+                                        // 16 rows (4 KiB) further with the same swizzle
     uint32_t fo;                        // this lane half's lse offsets / D
 #pragma unroll
     for (int s_ = 0; s_ < kD / 16; ++s_) {
@@ -394,16 +395,14 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     {
         const int sl = lane & 15, gq = lane >> 4, h = gq >> 1;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int db = 0; db < kD / 32; ++db) {
-                const int col = 32 * db + 16 * (gq & 1) + 4 * (sl & 3);
-                const int row0 = 16 * ks + 4 * h + (sl >> 2), row1 = row0 + 8;
-                const int x = col >> 3, half = (col >> 2) & 1;
-                to[ks][db][0] = (uint32_t)(row0 * kROWB + 16 * (x ^ swz(row0)) + 8 * half);
-                to[ks][db][1] = (uint32_t)(row1 * kROWB + 16 * (x ^ swz(row1)) + 8 * half);
-                asm volatile("" : "+v"(to[ks][db][0]), "+v"(to[ks][db][1]));
-            }
+        for (int db = 0; db < kD / 32; ++db) {
+            const int col = 32 * db + 16 * (gq & 1) + 4 * (sl & 3);
+            const int row0 = 4 * h + (sl >> 2), row1 = row0 + 8;
+            const int x = col >> 3, half = (col >> 2) & 1;
+            to[db][0] = (uint32_t)(row0 * kROWB + 16 * (x ^ swz(row0)) + 8 * half);
+            to[db][1] = (uint32_t)(row1 * kROWB + 16 * (x ^ swz(row1)) + 8 * half);
+            asm volatile("" : "+v"(to[db][0]), "+v"(to[db][1]));
+        }
     }
     fo = (uint32_t)(2 * kQBlk * kROWB + 4 * 4 * hh);
     asm volatile("" : "+v"(fo));
@@ -423,7 +422,8 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
         auto top = [&](int j) {
             const int ks = j / (2 * (kD / 32)), db = (j >> 1) % (kD / 32);
             const uint8_t* t0 = st + ((j & 1) ? 0 : kQBlk * kROWB);      // Q^T for dK, dO^T for dV
-            const s16x4 a = lds_read_tr16(t0 + to[ks][db][0]), c = lds_read_tr16(t0 + to[ks][db][1]);
+            const uint8_t* const tk = t0 + 16 * kROWB * ks;   // swz(row + 16) == swz(row)
+            const s16x4 a = lds_read_tr16(tk + to[db][0]), c = lds_read_tr16(tk + to[db][1]);
             const s16x8 v = {a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
             return __builtin_bit_cast(bf16x8, v);
         };
