@@ -34,6 +34,7 @@
 // XOR-swizzled by 4 (row mod 4) + (row / 4 mod 4): both the row reads (16
 // rows, one chunk) and the transposing reads (4 rows, 4 chunks) of a tile
 // then hit distinct banks.
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -163,59 +164,105 @@ __global__ __launch_bounds__(kThreadsB) void bwd_delta_kernel(const uint16_t* __
     if (row < rows && t == 0) delta[row] = acc;
 }
 
+// Wave-group barrier waits of the pair-grid dQ kernel that ran out, per
+// device (read and cleared by read_bwd_sync_timeouts).
+__device__ unsigned int g_bwd_sync_timeouts;
+static_assert(kWavesB == 4, "group_barrier counts four waves per group");
+
 // lse (natural log) -> the log2-domain offset of exp2; a row with no visible
 // key (lse = -inf) gets +inf so that every p of it is exactly 0.
 __device__ __forceinline__ float lse_offset(float lse) { return lse == kNegInf ? __builtin_inff() : lse * kLog2e; }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
+// dQ: one workgroup per (batch, query head, 128-row Q block), heaviest causal
+// blocks first; or, as a pair grid (PAIR: causal, Sq = Sk, every pair resident
+// at once), one 8-wave workgroup per pair (heavy block i = n-1-p, light block
+// p) of a (batch, query head), its two 4-wave groups each with their own K/V
+// stages and barrier: group A walks key blocks [0, split) of block i, group B
+// all of block p and then [split, 2 i + 2) of block i, so both walk about
+// n + 1 blocks and no CU keeps a heavy block running alone while its partner
+// has finished.  The two halves of block i's dQ are added through LDS.
+template <bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2, float scale, int n_qblk) {
-    // two stages of (K tile, V tile): the next block lands while this one is used
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[2][2 * kKVBlk * kROWB];
+    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2, float scale, int n_qblk,
+    int split_bias, int sync_spins) {
+    // per wave group two stages of (K tile, V tile): the next block lands
+    // while this one is used; pair mode adds the groups' barrier counters
+    constexpr int GROUP_LDS = 2 * 2 * kKVBlk * kROWB;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[PAIR ? 2 * GROUP_LDS + 64 : GROUP_LDS];
 
     const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = PAIR ? wave_id / kWavesB : 0;                 // wave group (pair mode: 0 = A, 1 = B)
+    const int wave = PAIR ? wave_id % kWavesB : wave_id;
+    uint8_t* const kvs0 = lds + grp * GROUP_LDS;       // the group's stages 0 and 1
+    uint8_t* const kvs1 = kvs0 + GROUP_LDS / 2;
+    int bar_target = 0;
+    bool sync_fail = false;             // a group barrier of this wave ran out (its rows become NaN)
+    if constexpr (PAIR) {
+        if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
+        __syncthreads();
+    }
+    // barrier of the waves that share this group's K/V stages
+    auto gsync = [&]() __attribute__((always_inline)) {
+        if constexpr (PAIR)
+            sync_fail |= group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane, sync_spins,
+                                       &g_bwd_sync_timeouts);
+        else
+            __syncthreads();
+    };
+
     const int bh_n = B * Hq;
     const int rank = blockIdx.x / bh_n, rem = blockIdx.x % bh_n;
-    const int qb = CAUSAL ? n_qblk - 1 - rank : rank;     // heaviest causal blocks first
     const int b = rem / Hq, hq = rem % Hq, kvh = hq / (Hq / Hkv);
     const int64_t bhq = (int64_t)b * Hq + hq;
     const uint16_t* Kh = K + ((int64_t)b * Hkv + kvh) * Sk * kD;
     const uint16_t* Vh = V + ((int64_t)b * Hkv + kvh) * Sk * kD;
     const int diag = Sk - Sq;
-    const int my_q = qb * kQRows + wave * 32 + l32;
+    // key blocks query block qb sees
+    auto blocks_of = [&](int qb) {
+        int kv_end = Sk;
+        if (CAUSAL) kv_end = min(Sk, max(0, qb * kQRows + kQRows + diag));
+        return (kv_end + kKVBlk - 1) / kKVBlk;
+    };
 
+    f32x16 dq[kD / 32];
+
+    // One job: query block qb against key blocks [kb0, kb1); with `final` its
+    // dQ is written, else it stays in dq.
+    auto run_job = [&](const int qb, const int kb0, const int kb1, const bool final) __attribute__((always_inline)) {
+    const int qw = qb * kQRows + wave * 32;        // first query row of this wave
+    const int my_q = qw + l32;
     bf16x8 qf[kD / 16], gf[kD / 16];
     load_row_operands(qf, Q + bhq * Sq * kD, my_q, Sq, hh);
     load_row_operands(gf, dO + bhq * Sq * kD, my_q, Sq, hh);
     const float lo = my_q < Sq ? lse_offset(LSE[bhq * Sq + my_q]) : __builtin_inff();
     const float Dq = my_q < Sq ? delta[bhq * Sq + my_q] : 0.f;
-
-    int kv_end = Sk;
-    if (CAUSAL) kv_end = min(Sk, max(0, qb * kQRows + kQRows + diag));
-    const int n_it = (kv_end + kKVBlk - 1) / kKVBlk;
-
-    f32x16 dq[kD / 32];
 #pragma unroll
     for (int i = 0; i < kD / 32; ++i) dq[i] = f32x16{};
 
-    if (n_it > 0) {
-        dma_rows<kKVBlk>(Kh, lds[0], 0, Sk, wave, lane);
-        dma_rows<kKVBlk>(Vh, lds[0] + kKVBlk * kROWB, 0, Sk, wave, lane);
+    if (kb0 < kb1) {
+        dma_rows<kKVBlk>(Kh, kvs0, kb0 * kKVBlk, Sk, wave, lane);
+        dma_rows<kKVBlk>(Vh, kvs0 + kKVBlk * kROWB, kb0 * kKVBlk, Sk, wave, lane);
     }
-    for (int it = 0; it < n_it; ++it) {
-        const int kv0 = it * kKVBlk;
-        // block it has landed for every wave, and every wave is done with block it-1,
-        // whose stage the next block goes to
+    for (int it = 0; it < kb1 - kb0; ++it) {
+        const int kv0 = (kb0 + it) * kKVBlk;
+        // the lane index made opaque: the operand addresses derived from it
+        // are formed in the step instead of being kept live across the loop
+        int ln_ = tid & 63;
+        asm volatile("" : "+v"(ln_));
+        const int lane = ln_, l32 = ln_ & 31, hh = ln_ >> 5;
+        // block it has landed for every wave of the group, and every wave is
+        // done with block it-1, whose stage the next block goes to
         wait_vm();
-        __syncthreads();
-        if (it + 1 < n_it) {
-            dma_rows<kKVBlk>(Kh, lds[(it + 1) & 1], kv0 + kKVBlk, Sk, wave, lane);
-            dma_rows<kKVBlk>(Vh, lds[(it + 1) & 1] + kKVBlk * kROWB, kv0 + kKVBlk, Sk, wave, lane);
+        gsync();
+        if (kb0 + it + 1 < kb1) {
+            uint8_t* const nx = (it & 1) ? kvs0 : kvs1;
+            dma_rows<kKVBlk>(Kh, nx, kv0 + kKVBlk, Sk, wave, lane);
+            dma_rows<kKVBlk>(Vh, nx + kKVBlk * kROWB, kv0 + kKVBlk, Sk, wave, lane);
         }
-        const uint8_t* kt = lds[it & 1];
+        const uint8_t* kt = (it & 1) ? kvs1 : kvs0;
         const uint8_t* vt = kt + kKVBlk * kROWB;
 
         // S^T = K Q^T and dP^T = V dO^T for keys kv0 .. kv0+63 (two 32-key blocks)
@@ -245,7 +292,7 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
         // runs past Sk is masked (a wave-uniform test); there key acc_row(r)
         // of half-block blk is kept iff 8 (r / 4) + r % 4 <= lim, one limit
         // per lane and half-block.
-        const bool masked = (kv0 + kKVBlk > Sk) || (CAUSAL && kv0 + kKVBlk - 1 > qb * kQRows + wave * 32 + diag);
+        const bool masked = (kv0 + kKVBlk > Sk) || (CAUSAL && kv0 + kKVBlk - 1 > qw + diag);
         const int last = CAUSAL ? min(Sk - 1, my_q + diag) : Sk - 1;     // last key this row may see
         u32x4 dsw[4];
 #pragma unroll
@@ -275,7 +322,51 @@ __global__ __launch_bounds__(kThreadsB, 2) void bwd_dq_kernel(
             for (int db = 0; db < kD / 32; ++db) dq[db] = mfma32(tr_operand(kt, ks, db, lane), bop, dq[db]);
         }
     }
-    store_rows(dQ + bhq * Sq * kD, dq, scale, my_q, Sq, hh);
+    if (final) store_rows(dQ + bhq * Sq * kD, dq, sync_fail ? __builtin_nanf("") : scale, my_q, Sq, hh);
+    };   // run_job
+
+    if constexpr (PAIR) {
+        const int p = rank, i = n_qblk - 1 - p;
+        const int ni = blocks_of(i);
+        const int split = i != p ? min(n_qblk + 1 + split_bias, ni) : (ni + 1) / 2;
+        if (grp == 0) {
+            run_job(i, 0, split, false);
+        } else {
+            if (i != p) {
+                run_job(p, 0, blocks_of(p), true);
+                gsync();                 // every wave is done with the light block's stages
+            }
+            run_job(i, split, ni, false);   // (an empty range leaves dq = 0)
+        }
+        // the halves of block i's dQ meet: A's plus B's, through B's stages
+        __syncthreads();                 // both groups done; every stage is free
+        float* const st = reinterpret_cast<float*>(lds + GROUP_LDS) + wave * (64 * 16 * (kD / 32));
+        if (grp == 1) {
+            const float f = sync_fail ? __builtin_nanf("") : 1.f;   // a failed B barrier reaches A's rows
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4)
+                    *reinterpret_cast<f32x4*>(st + ((db * 4 + a4) * 64 + lane) * 4) =
+                        f32x4{dq[db][4 * a4] * f, dq[db][4 * a4 + 1] * f, dq[db][4 * a4 + 2] * f, dq[db][4 * a4 + 3] * f};
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+            for (int db = 0; db < kD / 32; ++db)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 o = *reinterpret_cast<const f32x4*>(st + ((db * 4 + a4) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dq[db][4 * a4 + e] += o[e];
+                }
+            store_rows(dQ + bhq * Sq * kD, dq, sync_fail ? __builtin_nanf("") : scale, i * kQRows + wave * 32 + l32,
+                       Sq, hh);
+        }
+    } else {
+        const int qb = CAUSAL ? n_qblk - 1 - rank : rank;     // heaviest causal blocks first
+        run_job(qb, 0, blocks_of(qb), true);
+    }
 }
 
 // One stage of the dK/dV kernel: 32 query rows of Q and of dO (8 KiB each),
@@ -557,6 +648,24 @@ __global__ __launch_bounds__(kThreadsB, 1) void bwd_dkdv_kernel(
     store_rows(dV + bhk * Sk * kD, dv, 1.f, my_k, Sk, hh);
 }
 
+int bwd_cus() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+// K/V blocks of the heavy query block moved from group B to group A of a dQ
+// pair (B also pays a second job start and the light block's output).
+constexpr int kDqSplitBias = 0;
+
 template <bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
     const float scale_log2 = a.scale * kLog2e;
@@ -566,10 +675,21 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_qblk = (a.Sq + kQRows - 1) / kQRows;
-    launch_kernel<false>((bwd_dq_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)), dim3(kThreadsB), 0,
-                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
-                       scale_log2, a.scale, n_qblk);
+    const int n_pairs = (n_qblk + 1) / 2;
+    // pair grid for dQ: a causal square problem whose heavy/light query-block
+    // pairs all fit one 8-wave workgroup per CU
+    if (CAUSAL && a.Sq == a.Sk && a.Sq % kQRows == 0 && n_qblk >= 2 &&
+        (int64_t)a.B * a.Hq * n_pairs <= bwd_cus()) {
+        launch_kernel<false>((bwd_dq_kernel<CAUSAL, true>), dim3((unsigned)((int64_t)a.B * a.Hq * n_pairs)),
+                             dim3(2 * kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                             (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq,
+                             a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, kDqSplitBias, a.sync_spins);
+    } else {
+        launch_kernel<false>((bwd_dq_kernel<CAUSAL, false>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)),
+                             dim3(kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                             (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq,
+                             a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, 0, a.sync_spins);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kblk = (a.Sk + kKRows - 1) / kKRows;
@@ -584,6 +704,20 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
     return a.causal ? launch<true>(a, stream) : launch<false>(a, stream);
+}
+
+hipError_t read_bwd_sync_timeouts(unsigned int* count) {
+    // every kernel that may still add to the counter finishes first
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    unsigned int n = 0;
+    e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_bwd_sync_timeouts), sizeof(n), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_sync_timeouts), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    *count = n;
+    return hipDeviceSynchronize();
 }
 
 }  // namespace fa

@@ -28,7 +28,7 @@ struct TimingScope {
     ~TimingScope() { fa::call_timing() = fa::CallTiming{}; }
 };
 
-// Restores the default barrier poll bound when fa_fwd returns.
+// Restores the default barrier poll bound when fa_fwd or fa_bwd returns.
 struct SpinScope {
     ~SpinScope() { fa::next_sync_spins() = fa::kDefaultSyncSpins; }
 };
@@ -62,7 +62,10 @@ int fa_limit_next_sync_wait(int spins) {
 
 int fa_sync_timeouts(unsigned int* count) {
     if (count == nullptr) return FA_ERR_INVALID_ARG;
-    return fa::read_sync_timeouts(count) == hipSuccess ? FA_OK : FA_ERR_HIP;
+    unsigned int nf = 0, nb = 0;
+    if (fa::read_sync_timeouts(&nf) != hipSuccess || fa::read_bwd_sync_timeouts(&nb) != hipSuccess) return FA_ERR_HIP;
+    *count = nf + nb;
+    return FA_OK;
 }
 
 const char* fa_status_string(int status) {
@@ -114,6 +117,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
            void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal, float scale,
            void* workspace, size_t workspace_bytes, void* stream) {
     TimingScope timing_scope;
+    SpinScope spin_scope;
     if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
@@ -131,7 +135,7 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const voi
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return FA_ERR_WORKSPACE;
 
     fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv, Sq, Sk, d,
-                  causal, scale};
+                  causal, scale, fa::next_sync_spins()};
     const hipError_t e = fa::launch_bwd_bf16(a, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -82,6 +82,34 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t byt
 #endif
 }
 
+// Barrier of the four waves of one wave group (two groups share a
+// workgroup), through a counter in LDS: each wave adds 1 on arrival and
+// leaves once all four have arrived for this round (the counter grows by 4
+// per round; `target` is the wave's running round total).  The wait is
+// bounded by `spins` polls, so no wave can spin forever; a wait that runs out
+// is counted in `*timeouts` (a device-wide counter of the calling source) and
+// returned as true, and the caller marks its rows as failed.
+__device__ __forceinline__ bool group_barrier(uint8_t* ctr_p, int& target, int lane, int spins,
+                                              unsigned int* timeouts) {
+    int* const ctr = reinterpret_cast<int*>(ctr_p);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    target += 4;
+    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    bool timed_out = false;
+    for (int spin = 0;; ++spin) {
+        const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (c >= target) break;
+        if (spin >= spins) {
+            timed_out = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    if (timed_out && lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return timed_out;
+}
+
 // Row (lane % 32 is the column) index of accumulator register r in lane half h.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

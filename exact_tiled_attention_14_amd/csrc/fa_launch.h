@@ -49,6 +49,8 @@ constexpr int kDefaultSyncSpins = 1 << 22;
 int& next_sync_spins();
 // Reads and clears the device's count of wave-group barrier timeouts.
 hipError_t read_sync_timeouts(unsigned int* count);
+// The same for the backward's pair-grid dQ kernel.
+hipError_t read_bwd_sync_timeouts(unsigned int* count);
 
 struct BwdArgs {
     const void* q;
@@ -64,6 +66,7 @@ struct BwdArgs {
     int B, Hq, Hkv, Sq, Sk, d;
     int causal;
     float scale;
+    int sync_spins;        // poll bound of the wave-group barriers (pair-grid dQ)
 };
 
 struct DecodeArgs {

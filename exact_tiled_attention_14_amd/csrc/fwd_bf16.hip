@@ -232,32 +232,7 @@ __device__ __forceinline__ void mask_block(f32x16 (&sacc)[2], int kv0, int Sk, i
 // Wave-group barrier waits that ran out, per device (read and cleared by
 // read_sync_timeouts).
 __device__ unsigned int g_sync_timeouts;
-
-// Barrier of the four waves of one wave group, through a counter in LDS:
-// each wave adds 1 on arrival and leaves once all four have arrived for this
-// round (the counter grows by 4 per round; `target` is the wave's running
-// round total).  The wait is bounded by `spins` polls, so no wave can spin
-// forever; a wait that runs out is counted in g_sync_timeouts and returned
-// as true, and the caller marks its rows as failed.
-__device__ __forceinline__ bool group_barrier(uint8_t* ctr_p, int& target, int lane, int spins) {
-    int* const ctr = reinterpret_cast<int*>(ctr_p);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    target += kWaves;
-    if (lane == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    bool timed_out = false;
-    for (int spin = 0;; ++spin) {
-        const int c = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (c >= target) break;
-        if (spin >= spins) {
-            timed_out = true;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
-    if (timed_out && lane == 0) __hip_atomic_fetch_add(&g_sync_timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    return timed_out;
-}
+static_assert(kWaves == 4, "group_barrier counts four waves per group");
 
 template <int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void fwd_bf16_kernel(
@@ -290,7 +265,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     // barrier of the threads that share this workgroup's (or wave group's) K/V stages
     auto gsync = [&]() __attribute__((always_inline)) {
         if constexpr (PAIR) {
-            sync_fail |= group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane, sync_spins);
+            sync_fail |= group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane, sync_spins, &g_sync_timeouts);
         } else {
             __syncthreads();
         }

@@ -73,7 +73,9 @@ SHAPES = [
     (1, 4, 1, 333, 200, True),     # MQA, Sq > Sk: rows with no visible key
     (1, 2, 2, 100, 260, False),
     (1, 2, 2, 1, 77, True),        # a single query row
-    (1, 8, 2, 640, 640, True),     # several full blocks, GQA
+    (1, 8, 2, 640, 640, True),     # several full blocks, GQA; dQ pair grid with a middle block
+    (1, 4, 4, 256, 256, True),     # dQ pair grid, two query blocks
+    (2, 2, 1, 512, 512, True),     # dQ pair grid, MQA, four query blocks
 ]
 
 
@@ -88,7 +90,8 @@ def test_backward_small_shapes(B, shape):
 
 
 def test_backward_causal_mha_b2_h16_s2048(B):
-    """The headline prefill shape; all heads computed, four compared in full."""
+    """The headline prefill shape (the dQ kernel runs as a pair grid): every
+    head compared in full against the oracle."""
     c = I.workload("causal_mha_b2_h16_s2048_d128")
     do = I.make_grad_out(c.q.shape, seed=2)
     # the kernel needs O and lse of every head: the oracle computes them all
@@ -99,7 +102,7 @@ def test_backward_causal_mha_b2_h16_s2048(B):
     dq, dk, dv = B.fa_bwd(q, k, v, o, g, lse, True, c.scale)
     torch.cuda.synchronize()
     dq, dk, dv = _np(dq), _np(dk), _np(dv)
-    for b, h in ((0, 0), (0, 15), (1, 7), (1, 9)):
+    for b, h in [(b, h) for b in range(2) for h in range(16)]:
         rq, rk, rv = oracle.sdpa_backward(c.q[b:b + 1, h:h + 1], c.k[b:b + 1, h:h + 1], c.v[b:b + 1, h:h + 1],
                                           do[b:b + 1, h:h + 1], True, c.scale)
         check_grad(dq[b:b + 1, h:h + 1], rq, f"dq b{b} h{h}")
@@ -153,3 +156,31 @@ def test_backward_binding_errors(B):
     with pytest.raises(B.FAError) as e:
         B.fa_bwd(q, q, q, q, q, lse, True, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == B.FA_ERR_WORKSPACE
+
+
+def test_backward_pair_barrier_timeout_is_reported(B):
+    """The dQ pair grid's wave-group barriers with their poll bound forced to
+    0 from the host: waits run out, the device count says so and the rows of
+    the affected waves of dQ are NaN, never a plausible result.  Every wait is
+    bounded, so the kernels still exit normally; the bound applies to that
+    one call only, and the next call matches the oracle."""
+    B.fa_sync_timeouts()
+    c = I.make_prefill(1, 4, 4, 512, 512, 128, causal=True, seed=13)
+    do = I.make_grad_out(c.q.shape, seed=13)
+    O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
+    q, k, v = _bf(c.q), _bf(c.k), _bf(c.v)
+    o, g = _bf(I.round_to_bf16(O.astype(np.float32))), _bf(do)
+    lse = torch.from_numpy(L.astype(np.float32)).to(DEV)
+    B.fa_limit_next_sync_wait(0)
+    dq, dk, dv = B.fa_bwd(q, k, v, o, g, lse, True, c.scale)
+    torch.cuda.synchronize()
+    n = B.fa_sync_timeouts()
+    print(f"backward barrier timeouts with a zero poll bound: {n}", flush=True)
+    assert n > 0
+    assert bool(torch.isnan(dq.float()).any())
+    dq, dk, dv = B.fa_bwd(q, k, v, o, g, lse, True, c.scale)
+    torch.cuda.synchronize()
+    assert B.fa_sync_timeouts() == 0
+    ref = oracle.sdpa_backward(c.q, c.k, c.v, do, True, c.scale)
+    for name, x, y in zip(("dq", "dk", "dv"), (_np(dq), _np(dk), _np(dv)), ref):
+        check_grad(x, y, f"{name} after a timed-out call")
