@@ -570,8 +570,8 @@ def fa_mla_decode(q, w_uk, w_uv_t, ccache, block_table, seqlens, scale: float | 
 
 
 def fa_limit_next_sync_wait(spins: int) -> None:
-    """Bound the wave-group barriers of the next fa_fwd call on this thread to
-    ``spins`` polls (a test hook; the default bound is restored after that
+    """Bound the wave-group barriers of the next fa_fwd, fa_fwd_fp8 or fa_bwd
+    call on this thread to ``spins`` polls (a test hook; the default bound is restored after that
     call).  A barrier that runs out counts one timeout (see fa_sync_timeouts)
     and the rows of the waves it affected come out as NaN."""
     st = load().fa_limit_next_sync_wait(int(spins))

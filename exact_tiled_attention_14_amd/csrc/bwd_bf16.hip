@@ -707,17 +707,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t read_bwd_sync_timeouts(unsigned int* count) {
-    // every kernel that may still add to the counter finishes first
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return e;
-    unsigned int n = 0;
-    e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_bwd_sync_timeouts), sizeof(n), 0, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return e;
-    const unsigned int zero = 0;
-    e = hipMemcpyToSymbol(HIP_SYMBOL(g_bwd_sync_timeouts), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return e;
-    *count = n;
-    return hipDeviceSynchronize();
+    return read_device_counter(&HIP_SYMBOL(g_bwd_sync_timeouts), count);
 }
 
 }  // namespace fa

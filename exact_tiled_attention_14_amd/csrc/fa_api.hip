@@ -28,7 +28,8 @@ struct TimingScope {
     ~TimingScope() { fa::call_timing() = fa::CallTiming{}; }
 };
 
-// Restores the default barrier poll bound when fa_fwd or fa_bwd returns.
+// Restores the default barrier poll bound when fa_fwd, fa_fwd_fp8 or fa_bwd
+// returns.
 struct SpinScope {
     ~SpinScope() { fa::next_sync_spins() = fa::kDefaultSyncSpins; }
 };
@@ -43,6 +44,19 @@ CallTiming& call_timing() {
 int& next_sync_spins() {
     static thread_local int n = kDefaultSyncSpins;
     return n;
+}
+hipError_t read_device_counter(const void* symbol, unsigned int* count) {
+    // every kernel that may still add to the counter finishes first
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return e;
+    unsigned int n = 0;
+    e = hipMemcpyFromSymbol(&n, symbol, sizeof(n), 0, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return e;
+    const unsigned int zero = 0;
+    e = hipMemcpyToSymbol(symbol, &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return e;
+    *count = n;
+    return hipDeviceSynchronize();
 }
 }  // namespace fa
 
@@ -62,9 +76,11 @@ int fa_limit_next_sync_wait(int spins) {
 
 int fa_sync_timeouts(unsigned int* count) {
     if (count == nullptr) return FA_ERR_INVALID_ARG;
-    unsigned int nf = 0, nb = 0;
-    if (fa::read_sync_timeouts(&nf) != hipSuccess || fa::read_bwd_sync_timeouts(&nb) != hipSuccess) return FA_ERR_HIP;
-    *count = nf + nb;
+    unsigned int nf = 0, nb = 0, n8 = 0;
+    if (fa::read_sync_timeouts(&nf) != hipSuccess || fa::read_bwd_sync_timeouts(&nb) != hipSuccess ||
+        fa::read_fp8_sync_timeouts(&n8) != hipSuccess)
+        return FA_ERR_HIP;
+    *count = nf + nb + n8;
     return FA_OK;
 }
 
@@ -184,6 +200,7 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
                const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d, int causal,
                float scale, void* stream) {
     TimingScope timing_scope;
+    SpinScope spin_scope;
     if (!q8 || !k8 || !v8 || !q_scale || !k_scale || !v_scale || !o) return FA_ERR_INVALID_ARG;
     if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
     if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
@@ -193,7 +210,8 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
     if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk + 63, d)) return FA_ERR_INVALID_ARG;
     if (d != 128) return FA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * ((Sq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
-    fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale};
+    fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale,
+                     fa::next_sync_spins()};
     return fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

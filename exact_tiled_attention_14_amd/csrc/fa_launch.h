@@ -44,13 +44,19 @@ struct FwdArgs {
 };
 
 // Default poll bound of a wave-group barrier, and the bound the next fa_fwd
-// call on this thread uses (set by fa_limit_next_sync_wait).
+// (or fa_fwd_fp8 or fa_bwd) call on this thread uses (set by
+// fa_limit_next_sync_wait).
 constexpr int kDefaultSyncSpins = 1 << 22;
 int& next_sync_spins();
 // Reads and clears the device's count of wave-group barrier timeouts.
 hipError_t read_sync_timeouts(unsigned int* count);
-// The same for the backward's pair-grid dQ kernel.
+// The same for the backward's pair-grid dQ kernel and the FP8 forward.
 hipError_t read_bwd_sync_timeouts(unsigned int* count);
+hipError_t read_fp8_sync_timeouts(unsigned int* count);
+// Reads a device-side unsigned counter (the address of a __device__ variable
+// in host code, which names its symbol) of the current device once every queued kernel has finished,
+// and clears it.
+hipError_t read_device_counter(const void* symbol, unsigned int* count);
 
 struct BwdArgs {
     const void* q;
@@ -137,6 +143,7 @@ struct Fp8FwdArgs {
     int B, Hq, Hkv, Sq, Sk;
     int causal;
     float scale;
+    int sync_spins;        // poll bound of the wave-group barriers (pair grid)
 };
 
 hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t stream);

@@ -670,17 +670,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
 }
 
 hipError_t read_sync_timeouts(unsigned int* count) {
-    // every kernel that may still add to the counter finishes first
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return e;
-    unsigned int n = 0;
-    e = hipMemcpyFromSymbol(&n, HIP_SYMBOL(g_sync_timeouts), sizeof(n), 0, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return e;
-    const unsigned int zero = 0;
-    e = hipMemcpyToSymbol(HIP_SYMBOL(g_sync_timeouts), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return e;
-    *count = n;
-    return hipDeviceSynchronize();
+    return read_device_counter(&HIP_SYMBOL(g_sync_timeouts), count);
 }
 
 int64_t fwd_bf16_grid(const FwdArgs& a) {

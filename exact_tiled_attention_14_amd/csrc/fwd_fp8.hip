@@ -115,28 +115,58 @@ __device__ __forceinline__ void mask_block8(f32x16 (&sacc)[2], int kv0, int Sk, 
     }
 }
 
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
+// Wave-group barrier waits of this source that ran out, per device (read and
+// cleared by read_fp8_sync_timeouts).
+__device__ unsigned int g_fp8_sync_timeouts;
+static_assert(kWaves8 == 4, "group_barrier counts four waves per group");
+
+// One workgroup of 4 waves per (batch, query head, 128-row Q block), heaviest
+// causal blocks first; or, as a pair grid (PAIR: causal, Sq = Sk, every pair
+// resident at once), one 8-wave workgroup per pair (heavy block i = n-1-p,
+// light block p) of a (batch, query head), as the bf16 kernel does: two
+// 4-wave groups with their own K/V stages and barrier, group A walking key
+// blocks [0, split) of block i, group B all of block p and then the rest of
+// block i, and the two partial softmax states of block i merged through LDS.
+template <bool CAUSAL, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
-    int n_qblk, int xcd_groups, int mirror) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[4 * kTile8];
-    uint8_t* const kbuf = lds;                 // K stages 0, 1
-    uint8_t* const vbuf = lds + 2 * kTile8;    // V stages 0, 1
+    int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias, int sync_spins) {
+    constexpr int GROUP_LDS = 4 * kTile8;      // K stages 0, 1 and V stages 0, 1
+    // pair mode: both groups' stages, their barrier counters, the merge's (m, l)
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[PAIR ? 2 * GROUP_LDS + 64 + kWaves8 * 64 * 8 : GROUP_LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = PAIR ? wave_id / kWaves8 : 0;       // wave group (pair mode: 0 = A, 1 = B)
+    const int wave = PAIR ? wave_id % kWaves8 : wave_id;
+    uint8_t* const kbuf = lds + grp * GROUP_LDS;         // K stages 0, 1
+    uint8_t* const vbuf = kbuf + 2 * kTile8;             // V stages 0, 1
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int g = Hq / Hkv;
+    int bar_target = 0;
+    bool sync_fail = false;             // a wave-group barrier of this wave ran out (its rows become NaN)
+    if constexpr (PAIR) {
+        if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
+        __syncthreads();
+    }
+    // barrier of the threads that share this workgroup's (or wave group's) K/V stages
+    auto gsync = [&]() __attribute__((always_inline)) {
+        if constexpr (PAIR) {
+            sync_fail |=
+                group_barrier(lds + 2 * GROUP_LDS + 16 * grp, bar_target, lane, sync_spins, &g_fp8_sync_timeouts);
+        } else {
+            __syncthreads();
+        }
+    };
 
-    // ---- which (batch, head, query block) this workgroup owns (as the bf16 kernel) ----
-    int b, hq, kvh, qb;
+    // ---- which (batch, head) and rank this workgroup owns (as the bf16 kernel) ----
+    int b, hq, kvh, rank;
     {
         const int w = blockIdx.x;
-        int rank;
         if (xcd_groups) {
             const int xcd = w & 7, j = w >> 3;
             const int per_rank = xcd_groups * g;
@@ -154,26 +184,62 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
             hq = rem % Hq;
             kvh = hq / g;
         }
-        if (mirror && rank >= (n_qblk + 1) / 2) rank = n_qblk - 1 - (rank - (n_qblk + 1) / 2);
-        qb = CAUSAL ? n_qblk - 1 - rank : rank;
+        if (mirror && rank >= (n_rank + 1) / 2) rank = n_rank - 1 - (rank - (n_rank + 1) / 2);
     }
 
     const int n_kblk = (Sk + kBN8 - 1) / kBN8;
     const int64_t bhq = (int64_t)b * Hq + hq;
     const int64_t bhk = (int64_t)b * Hkv + kvh;
-    const uint8_t* Kh = K + bhk * Sk * kD8;
-    const uint8_t* Vh = V + bhk * n_kblk * kTile8;
     const uint8_t* KSh = KS + bhk * n_kblk;
     const uint8_t* VSh = VS + bhk * n_kblk;
+    const int diag = Sk - Sq;
+    f32x16 oacc[4];
+    float m_run, l_run;
+
+    // ---- epilogue of a query block: one division per row, bf16 output,
+    // natural-log lse ----
+    auto write_out = [&](const int qb) __attribute__((always_inline)) {
+        const int my_q = qb * kBM8 + wave * 32 + l32;
+        const float l_tot = half_swap_sum(l_run);
+        const float inv = sync_fail ? __builtin_nanf("") : l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (my_q < Sq) {
+            uint16_t* op = O + (bhq * Sq + my_q) * kD8;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const int d0 = 32 * db + 8 * a + 4 * hh;
+                    const u32x2 w = {pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv),
+                                     pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
+                    *reinterpret_cast<u32x2*>(op + d0) = w;
+                }
+            if (LSE != nullptr && hh == 0)
+                LSE[bhq * Sq + my_q] = sync_fail    ? __builtin_nanf("")
+                                       : l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2
+                                                     : kNegInf;
+        }
+    };
+
+    // One job: query block qb against K/V blocks [kb0, kb1); with `final` the
+    // output of the block is written, else the state stays in oacc/m_run/l_run.
+    auto run_job = [&](const int qb, const int kb0, const int kb1, const bool final) __attribute__((always_inline)) {
+    // (empty asm statements: the per-lane addresses are formed inside each job,
+    // not kept live across the other job of a pair workgroup)
+    int64_t k_off = bhk * Sk * kD8;
+    int64_t v_off = bhk * n_kblk * kTile8;
+    int k_lane_off = k8_lane_offset(wave, lane);
+    int v_lane_off = v8_lane_offset(wave, lane);
+    if constexpr (PAIR) {
+        asm volatile("" : "+s"(k_off), "+s"(v_off));
+        asm volatile("" : "+v"(k_lane_off), "+v"(v_lane_off));
+    }
+    const uint8_t* Kh = K + k_off;
+    const uint8_t* Vh = V + v_off;
     const int q0 = qb * kBM8;
     const int qw = q0 + wave * 32;
     const int my_q = qw + l32;
-    const int diag = Sk - Sq;
     const int sq = QS[bhq * n_qblk + qb];
-
-    int kv_end = Sk;
-    if (CAUSAL) kv_end = min(Sk, max(0, q0 + kBM8 + diag));
-    const int n_it = (kv_end + kBN8 - 1) / kBN8;
+    const int n_it = kb1 - kb0;
 
     // Q fragment (B operand of S^T = K Q^T): head-dim bytes 64 s + 32 h .. +31.
     // Lanes past the last query row read row Sq - 1; their scores are never
@@ -190,11 +256,10 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         }
     }
 
-    f32x16 oacc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
-    float m_run = kNegInf;
-    float l_run = 0.f;
+    m_run = kNegInf;
+    l_run = 0.f;
 
     auto needs_mask = [&](int kv0) { return (kv0 + kBN8 > Sk) || (CAUSAL && kv0 + kBN8 - 1 > qw + diag); };
 
@@ -206,8 +271,8 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         const uint8_t* r1 = r0 + 32 * kD8;
         i32x8 ka0 = read32(r0, 2 * hh, sw_k);
         i32x8 ka1 = read32(r1, 2 * hh, sw_k);
-        const i32x8 kb0 = read32(r0, 4 + 2 * hh, sw_k);
-        const i32x8 kb1 = read32(r1, 4 + 2 * hh, sw_k);
+        const i32x8 kb0_ = read32(r0, 4 + 2 * hh, sw_k);
+        const i32x8 kb1_ = read32(r1, 4 + 2 * hh, sw_k);
         FA8_FENCE();
         sacc[0] = mfma_f8(ka0, qf[0], sacc[0], sk, sq);
         FA8_FENCE();
@@ -217,38 +282,36 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         FA8_FENCE();
         between(1);
         FA8_FENCE();
-        sacc[0] = mfma_f8(kb0, qf[1], sacc[0], sk, sq);
+        sacc[0] = mfma_f8(kb0_, qf[1], sacc[0], sk, sq);
         FA8_FENCE();
         between(2);
         FA8_FENCE();
-        sacc[1] = mfma_f8(kb1, qf[1], sacc[1], sk, sq);
+        sacc[1] = mfma_f8(kb1_, qf[1], sacc[1], sk, sq);
         FA8_FENCE();
         between(3);
         FA8_FENCE();
     };
 
-    const int k_lane_off = k8_lane_offset(wave, lane);
-    const int v_lane_off = v8_lane_offset(wave, lane);
     // Block scales used by a step are loaded one step earlier (the first ones
     // here, ahead of the prologue's wait): a load issued in the step itself
     // would sit behind that step's K/V tile loads in the memory counter,
     // so waiting for it would wait for them too.
-    const int sk0 = KSh[0];
-    int sk_pref = KSh[min(1, n_kblk - 1)];   // K scale of block it + 1
-    int sv_pref = VSh[0];                    // V scale of block it
+    const int sk0 = KSh[min(kb0, n_kblk - 1)];
+    int sk_pref = KSh[min(kb0 + 1, n_kblk - 1)];   // K scale of block kb0 + it + 1
+    int sv_pref = VSh[min(kb0, n_kblk - 1)];       // V scale of block kb0 + it
     if (n_it > 0) {
-        dma_k8(Kh, kbuf, k_lane_off, 0, Sk, wave);
-        dma_v8(Vh, vbuf, v_lane_off, wave);
+        dma_k8(Kh, kbuf, k_lane_off, kb0 * kBN8, Sk, wave);
+        dma_v8(Vh + (int64_t)kb0 * kTile8, vbuf, v_lane_off, wave);
     }
-    if (n_it > 1) dma_k8(Kh, kbuf + kTile8, k_lane_off, kBN8, Sk, wave);
+    if (n_it > 1) dma_k8(Kh, kbuf + kTile8, k_lane_off, (kb0 + 1) * kBN8, Sk, wave);
     wait_dma8();
-    __syncthreads();
+    gsync();
 
     f32x16 s0[2] = {f32x16{}, f32x16{}};
     float mx_cur = kNegInf;
     if (n_it > 0) {
         score(s0, kbuf, sk0, [](int) {});
-        if (needs_mask(0)) mask_block8<CAUSAL>(s0, 0, Sk, my_q, diag, hh);
+        if (needs_mask(kb0 * kBN8)) mask_block8<CAUSAL>(s0, kb0 * kBN8, Sk, my_q, diag, hh);
         float mx = kNegInf;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -256,7 +319,9 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s0[blk][r]);
         mx_cur = half_swap_max(mx) * scale_log2;
     }
-    __syncthreads();
+    // K stage 0 is rewritten (with block kb0 + 2) in the first step: every
+    // wave must have finished reading it above.
+    gsync();
 
     const int sw_v = swz_v8(l32);   // rows 32 db + l32 share it (period 32)
     // The LDS stages a step writes (loads to LDS of K_{it+2}, V_{it+1})
@@ -268,6 +333,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
                     const uint8_t* __restrict__ v_rd) __attribute__((always_inline)) {
         const bool has_next = it + 1 < n_it;
         const bool has_next2 = it + 2 < n_it;
+        const int kb = kb0 + it;        // absolute K/V block of this step
 
         if (__builtin_amdgcn_ballot_w64(mx_cur > m_run + kTau8)) {
             const float m_new = fmaxf(m_run, mx_cur);
@@ -280,11 +346,11 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         const float m_use = m_run == kNegInf ? 0.f : m_run;
         const int sv = sv_pref;
         const int sk_next = has_next ? sk_pref : 127;
-        sk_pref = KSh[min(it + 2, n_kblk - 1)];
-        sv_pref = VSh[min(it + 1, n_kblk - 1)];
+        sk_pref = KSh[min(kb + 2, n_kblk - 1)];
+        sv_pref = VSh[min(kb + 1, n_kblk - 1)];
 
-        if (has_next2) dma_k8(Kh, k_dma, k_lane_off, (it + 2) * kBN8, Sk, wave);
-        if (has_next) dma_v8(Vh + (int64_t)(it + 1) * kTile8, v_dma, v_lane_off, wave);
+        if (has_next2) dma_k8(Kh, k_dma, k_lane_off, (kb + 2) * kBN8, Sk, wave);
+        if (has_next) dma_v8(Vh + (int64_t)(kb + 1) * kTile8, v_dma, v_lane_off, wave);
 
         // ---- phase X: scores of block it+1, exponentials of block it ----
         int pw[8];
@@ -313,7 +379,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         l_run += rs;
 
         // ---- phase Y: O^T += V_it^T P_it^T, maximum of block it+1 ----
-        if (has_next && needs_mask((it + 1) * kBN8)) mask_block8<CAUSAL>(snxt, (it + 1) * kBN8, Sk, my_q, diag, hh);
+        if (has_next && needs_mask((kb + 1) * kBN8)) mask_block8<CAUSAL>(snxt, (kb + 1) * kBN8, Sk, my_q, diag, hh);
         float mxn = kNegInf;
         {
             const uint8_t* vt = v_rd + l32 * 64;
@@ -337,7 +403,7 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         if (has_next) mx_cur = half_swap_max(mxn) * scale_log2;
 
         wait_dma8();
-        __syncthreads();
+        gsync();
     };
     f32x16 s1[2];
     for (int it = 0; it < n_it; it += 2) {
@@ -345,21 +411,70 @@ __global__ __launch_bounds__(kThreads8, 2) void fwd_fp8_kernel(
         if (it + 1 < n_it) step(it + 1, s1, s0, kbuf + kTile8, vbuf, kbuf, vbuf + kTile8);
     }
 
-    const float l_tot = half_swap_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (my_q < Sq) {
-        uint16_t* op = O + (bhq * Sq + my_q) * kD8;
+    if (final) write_out(qb);
+    };   // run_job
+
+    if constexpr (PAIR) {
+        // Pair workgroup p of (b, hq): heavy block i = n-1-p and light block p
+        // (i == p for the middle block when n is odd).  Group A takes K/V
+        // blocks [0, split) of block i; group B the whole of block p, then
+        // [split, 2i + 2) of block i; `split_bias` blocks move from B to A,
+        // since B also pays a second job start and the light block's output.
+        const int p = rank, i = n_qblk - 1 - p;
+        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : (n_qblk + 1) / 2;
+        if (grp == 0) {
+            run_job(i, 0, split, false);
+        } else {
+            if (i != p) run_job(p, 0, 2 * p + 2, true);     // its output goes straight to memory
+            if (split < 2 * i + 2) {
+                run_job(i, split, 2 * i + 2, false);
+            } else {                     // group A takes all of block i: B's share is empty
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const int d0 = 32 * db + 8 * a + 4 * hh;
-                const u32x2 w = {pack_bf16x2(oacc[db][4 * a + 0] * inv, oacc[db][4 * a + 1] * inv),
-                                 pack_bf16x2(oacc[db][4 * a + 2] * inv, oacc[db][4 * a + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + d0) = w;
+                for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+                m_run = kNegInf;
+                l_run = 0.f;
             }
-        if (LSE != nullptr && hh == 0)
-            LSE[bhq * Sq + my_q] = l_tot > 0.f ? (m_run + log2f_hw(l_tot)) * kLn2 : kNegInf;
+        }
+        // ---- the halves of block i meet: M = max(m_A, m_B), acc = acc_A
+        // 2^(m_A - M) + acc_B 2^(m_B - M), l likewise.  Group B's waves hold
+        // the same rows and columns, lane for lane, as group A's. ----
+        __syncthreads();                 // both groups done; every K/V stage is free
+        float* const st = reinterpret_cast<float*>(lds) + wave * (64 * 64);
+        float2* const sml = reinterpret_cast<float2*>(lds + 2 * GROUP_LDS + 64) + wave * 64;
+        if (grp == 1) {
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+                    *reinterpret_cast<f32x4*>(st + ((db * 4 + a) * 64 + lane) * 4) =
+                        f32x4{oacc[db][4 * a], oacc[db][4 * a + 1], oacc[db][4 * a + 2], oacc[db][4 * a + 3]};
+            // (a failed barrier in group B reaches group A's write-out as a NaN sum)
+            sml[lane] = make_float2(m_run, sync_fail ? __builtin_nanf("") : l_run);
+        }
+        __syncthreads();
+        if (grp == 0) {
+            const float2 ml = sml[lane];
+            sync_fail |= __builtin_isnan(ml.y);
+            const float M = fmaxf(m_run, ml.x);
+            const float Mu = M == kNegInf ? 0.f : M;
+            const float wa = exp2f_hw(m_run - Mu), wb = exp2f_hw(ml.x - Mu);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int a = 0; a < 4; ++a) {
+                    const f32x4 o = *reinterpret_cast<const f32x4*>(st + ((db * 4 + a) * 64 + lane) * 4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oacc[db][4 * a + e] = oacc[db][4 * a + e] * wa + o[e] * wb;
+                }
+            l_run = l_run * wa + ml.y * wb;
+            m_run = M;
+            write_out(i);
+        }
+    } else {
+        const int qb = CAUSAL ? n_qblk - 1 - rank : rank;
+        int kv_end = Sk;
+        if (CAUSAL) kv_end = min(Sk, max(0, qb * kBM8 + kBM8 + diag));
+        run_job(qb, 0, (kv_end + kBN8 - 1) / kBN8, true);
     }
 }
 
@@ -370,16 +485,38 @@ int num_cus8() {
     return n > 0 ? n : 256;
 }
 
+// K/V blocks of the heavy query block moved from group B to group A of a pair
+// workgroup, for n query blocks.
+int fp8_split_bias(int n_qblk) { return 2 + 3 * n_qblk / 16; }
+
 template <bool CAUSAL>
 hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     const int n_qblk = (a.Sq + kBM8 - 1) / kBM8;
-    const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
     const int units = a.B * a.Hkv;
     const int xcd_groups = (units % 8 == 0) ? units / 8 : 0;
-    const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)num_cus8()) ? 1 : 0;
-    launch_kernel((fwd_fp8_kernel<CAUSAL>), dim3((unsigned)n_wg), dim3(kThreads8), 0, stream, (const uint8_t*)a.q8,
-                  (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale, a.v_scale, (uint16_t*)a.o, a.lse,
-                  a.B, a.Hq, a.Hkv, a.Sq, a.Sk, a.scale * kLog2e, n_qblk, xcd_groups, mirror);
+    const float scale_log2 = a.scale * kLog2e;
+    const int cus = num_cus8();
+    // Pair grid: a causal square problem whose query blocks, paired heavy with
+    // light, fit one 8-wave workgroup per CU.
+    if constexpr (CAUSAL) {
+        const int n_pairs = (n_qblk + 1) / 2;
+        if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
+            const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+            launch_kernel((fwd_fp8_kernel<CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,
+                          (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale,
+                          a.v_scale, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs,
+                          xcd_groups, 0, fp8_split_bias(n_qblk), a.sync_spins);
+            return hipGetLastError();
+        }
+    }
+    const int64_t n_wg = (int64_t)a.B * a.Hq * n_qblk;
+    // Two workgroups fit on a CU; if the whole grid is resident at once, pair
+    // heavy and light causal Q blocks on the same CU.
+    const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)cus) ? 1 : 0;
+    launch_kernel((fwd_fp8_kernel<CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads8), 0, stream,
+                  (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale, a.v_scale,
+                  (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror,
+                  0, a.sync_spins);
     return hipGetLastError();
 }
 
@@ -387,6 +524,10 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
     return a.causal ? launch8<true>(a, stream) : launch8<false>(a, stream);
+}
+
+hipError_t read_fp8_sync_timeouts(unsigned int* count) {
+    return read_device_counter(&HIP_SYMBOL(g_fp8_sync_timeouts), count);
 }
 
 }  // namespace fa

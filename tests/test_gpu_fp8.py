@@ -279,7 +279,9 @@ SHAPES = [
     (1, 4, 1, 333, 200, True),     # rows with no visible key
     (1, 2, 2, 100, 260, False),
     (1, 2, 2, 1, 77, True),
-    (1, 8, 2, 640, 640, True),
+    (1, 8, 2, 640, 640, True),     # pair grid, odd number of query blocks
+    (1, 4, 4, 256, 256, True),     # pair grid, group A takes all of the heavy block
+    (2, 2, 1, 384, 384, True),     # pair grid, MQA, odd
 ]
 
 
@@ -304,7 +306,7 @@ def test_fp8_forward_small_shapes(B, shape, rotate):
 
 def test_fp8_forward_headline_shape(B):
     """B2 H16 S2048 causal, rotation inside the quantizer (the benchmark's
-    path); four heads compared in full.  A rotated element within the fp32
+    path, a pair grid); every head compared in full.  A rotated element within the fp32
     summation bound of an E4M3 midpoint may take either code, so lse is
     allowed the score slack of such elements (ambiguous_slack) and O is held
     to the relative RMS bound, which a few one-step code differences cannot
@@ -312,10 +314,35 @@ def test_fp8_forward_headline_shape(B):
     c = I.workload("causal_mha_b2_h16_s2048_d128")
     rot = I.make_rotation(128, seed=2)
     o, lse = run_fp8(B, c, rot)
-    for b, h in ((0, 0), (0, 15), (1, 7), (1, 9)):
-        O, L, vd, slack = oracle_fp8(c, rot, heads=(b, h))
-        check_fp8_o(o[b:b + 1, h:h + 1], O, vd, f"fp8 headline b{b} h{h}", slack, max_abs=False)
-        check_lse(lse[b:b + 1, h:h + 1], L, f"fp8 headline b{b} h{h}", slack)
+    for b in range(2):
+        for h in range(16):
+            O, L, vd, slack = oracle_fp8(c, rot, heads=(b, h))
+            check_fp8_o(o[b:b + 1, h:h + 1], O, vd, f"fp8 headline b{b} h{h}", slack, max_abs=False)
+            check_lse(lse[b:b + 1, h:h + 1], L, f"fp8 headline b{b} h{h}", slack)
+
+
+def test_fp8_pair_barrier_timeout_is_reported(B):
+    """The pair grid's wave-group barriers with their poll bound forced to 0
+    from the host: waits run out, the device count says so and rows of the
+    output and lse are NaN, never a plausible result.  Every wait is bounded,
+    so the kernel still exits normally; the bound applies to that one call
+    only, and the next call matches the oracle."""
+    B.fa_sync_timeouts()
+    c = I.make_prefill(1, 4, 4, 512, 512, 128, causal=True, seed=14)
+    q8, qs, k8, ks, v8, vs = B.fa_quantize_fp8_qkv(_bf(c.q), _bf(c.k), _bf(c.v))
+    B.fa_limit_next_sync_wait(0)
+    o, lse = B.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale)
+    torch.cuda.synchronize()
+    n = B.fa_sync_timeouts()
+    print(f"fp8 barrier timeouts with a zero poll bound: {n}", flush=True)
+    assert n > 0
+    assert bool(torch.isnan(o.float()).any()) and bool(torch.isnan(lse).any())
+    o, lse = B.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale)
+    torch.cuda.synchronize()
+    assert B.fa_sync_timeouts() == 0
+    O, L, vd, _ = oracle_fp8(c, None)
+    check_fp8_o(_np(o), O, vd, "fp8 after a timed-out call")
+    check_lse(lse.cpu().numpy().astype(np.float64), L, "fp8 after a timed-out call")
 
 
 def test_rotation_reduces_error_with_key_outliers(B):
