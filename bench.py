@@ -485,7 +485,7 @@ def main():
         gbs_m = lat_bytes / (st["mean"] * 1e-3) / 1e9
         result["mla"] = {
             "workload": MLA, "bound": "hbm",
-            "kernels": "mla_absorb_kernel + mla_partial_kernel + mla_combine_kernel + mla_upproj_kernel",
+            "kernels": "mla_absorb_kernel + mla_partial_kernel + mla_merge_upproj_kernel",
             "achieved": round(gbs_m, 1), "peak": peak_gb, "unit": "GB/s", "frac": round(gbs_m / peak_gb, 4),
             "traffic": profiling.current_profile(PROFILES[MLA])["traffic"],
             "algorithmic_latent_bytes_per_launch": lat_bytes,

@@ -27,8 +27,9 @@
 //      wave w accumulates slice w of sum_j p_hj c_j.  Online softmax as in
 //      the prefill kernel.  16 x 16 x 32 matrix-core products
 //      (16 tokens x 16 heads), so 16 heads fill the tile with no padding.
-//   3. mla_combine_kernel: merges the parts of each sequence (log-sum-exp
-//      weights) into the normalised latent output (fp32).
+//   3. mla_merge_upproj_kernel: merges the parts of each sequence
+//      (log-sum-exp weights) into the normalised latent output (fp32) and
+//      computes o_h = (sum_j p_hj c_j) W_V[h] from it on the matrix cores.
 //
 // Work split: sequence lengths differ widely and live on the device, so the
 // scheduling workgroup sums the pages P of all sequences and cuts each
@@ -37,7 +38,6 @@
 // resident, less one per sequence for the rounding).  Every part then takes
 // about the same time and the whole grid runs in one wave; a sequence of one
 // part writes its final latent output directly.
-//   4. mla_upproj_kernel: o_h = (sum_j p_hj c_j) W_V[h] on the matrix cores.
 //
 // q~ and the latent output are intermediate results, not inputs: rounding
 // them to bf16 would add about 2^-9 relative error to every score and output
@@ -397,107 +397,119 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
     for (int blk = 0; blk < 8; ++blk) *reinterpret_cast<f32x4*>(op + 16 * blk + 4 * g) = oacc[blk] * inv;
 }
 
-// ---- 3. merge the parts of a sequence ----
-// Workgroup (sequence, head); thread t owns latent entries 4t .. 4t + 3 and
-// reads them from every part (one 2 KiB row per part, coalesced).
-constexpr int kThreadsC = kDC / 4;
-__global__ __launch_bounds__(kThreadsC) void mla_combine_kernel(const float* __restrict__ ws_o,
-                                                                const float* __restrict__ ws_lse,
-                                                                const int2* __restrict__ part,
-                                                                float* __restrict__ Olat, float* __restrict__ LSE,
-                                                                int H, int Hp) {
-    const int s = blockIdx.x, row = blockIdx.y;
-    const int2 pt = part[s];
-    const int nch = pt.y;
-    if (nch <= 1) return;
-    const int t = threadIdx.x;
-    const int64_t slot0 = pt.x;
-    // the parts' maximum lse: each thread reads every kThreadsC-th part, so all
-    // reads are in flight at once, then a reduction over the workgroup
-    __shared__ float s_red[kThreadsC / 64];
-    float M = kNegInf;
-    for (int c = t; c < nch; c += kThreadsC) M = fmaxf(M, ws_lse[(slot0 + c) * Hp + row]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    if ((t & 63) == 0) s_red[t >> 6] = M;
-    __syncthreads();
-#pragma unroll
-    for (int w = 0; w < kThreadsC / 64; ++w) M = fmaxf(M, s_red[w]);
-    float L = 0.f;
-    f32x4 acc = f32x4{};
-#pragma unroll 8
-    for (int c = 0; c < nch; ++c) {
-        const float lc = ws_lse[(slot0 + c) * Hp + row];
-        const float w = M == kNegInf ? 0.f : exp2f_hw((lc - M) * kLog2e);
-        L += w;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(ws_o + ((slot0 + c) * Hp + row) * kDC + 4 * t);
-        acc[0] = fmaf(w, v[0], acc[0]);
-        acc[1] = fmaf(w, v[1], acc[1]);
-        acc[2] = fmaf(w, v[2], acc[2]);
-        acc[3] = fmaf(w, v[3], acc[3]);
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    *reinterpret_cast<f32x4*>(Olat + ((int64_t)s * H + row) * kDC + 4 * t) =
-        f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    if (LSE != nullptr && t == 0) LSE[(int64_t)s * H + row] = L > 0.f ? M + log2f_hw(L) * kLn2 : kNegInf;
-}
+// ---- 3. merge the parts of each sequence, then up-project:
+// o[s, h, j] = sum_i W_V^T[h][j][i] olat[s, h, i] ----
+// Workgroup (h, 4 sequences).  Merge: wave w takes sequence 4 b + w, each
+// lane 8 latent entries of every part's 2 KiB row (one coalesced row per
+// part), folding the parts in with the online log-sum-exp update (running
+// maximum, rescaled sum), so the loads of 8 parts are in flight at once; a
+// sequence of one part reads the latent output the partial kernel wrote.  The
+// merged rows (fp32) go to LDS.  Up-projection: wave w computes output dims
+// 32 w .. 32 w + 31 of the 4 sequences with 16x16x32 products over the 512
+// latent entries (W_V rows as A, loaded before the merge; the merged rows as
+// hi + lo B operands; columns 4..15 repeat the 4 sequences and are dropped).
+constexpr int kSeqU = 4;                  // sequences per workgroup (one per wave)
+constexpr int kRowU = kDC + 4;            // LDS row stride in floats
+__global__ __launch_bounds__(kThreadsL) void mla_merge_upproj_kernel(
+    const float* __restrict__ Olat, const float* __restrict__ ws_o, const float* __restrict__ ws_lse,
+    const int2* __restrict__ part, const uint16_t* __restrict__ WVT, uint16_t* __restrict__ O,
+    float* __restrict__ LSE, int nseq, int H, int Hp) {
+    __shared__ __attribute__((aligned(16))) float cl[kSeqU * kRowU];
+    const int h = blockIdx.x, s0 = blockIdx.y * kSeqU;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l16 = lane & 15, g = lane >> 4;
 
-// ---- 4. up-projection: o[s, h, j] = sum_i W_V^T[h][j][i] olat[s, h, i] ----
-// Workgroup (h, 32 output dims, 32 sequences); wave w sums latent entries
-// 128 w .. 128 w + 127 (D[j][t] over its part of i, hi + lo products), and
-// the four partial tiles are added through LDS.
-__global__ __launch_bounds__(kThreadsL) void mla_upproj_kernel(const float* __restrict__ Olat,
-                                                               const uint16_t* __restrict__ WVT,
-                                                               uint16_t* __restrict__ O, int nseq, int H) {
-    __shared__ __attribute__((aligned(16))) float red[3][64 * 16];
-    const int h = blockIdx.x, j0 = 32 * blockIdx.y, s0 = blockIdx.z * 32;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int s = s0 + l32;
-    const float* lp = Olat + ((int64_t)min(s, nseq - 1) * H + h) * kDC + 128 * wave + 8 * hh;
-    const uint16_t* wp = WVT + ((int64_t)h * kDH + j0 + l32) * kDC + 128 * wave + 8 * hh;
-    f32x4 la[8], lb[8];
-    bf16x8 wa[8];
+    // A operands: W_V^T[h][32 w + 16 jb + l16][32 ks + 8 g .. +7]
+    bf16x8 wa[2][kDC / 32];
+    {
+        const uint16_t* wp = WVT + ((int64_t)h * kDH + 32 * wave + l16) * kDC + 8 * g;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        la[k] = *reinterpret_cast<const f32x4*>(lp + 16 * k);
-        lb[k] = *reinterpret_cast<const f32x4*>(lp + 16 * k + 4);
-        wa[k] = *reinterpret_cast<const bf16x8*>(wp + 16 * k);
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int ks = 0; ks < kDC / 32; ++ks)
+                wa[jb][ks] = *reinterpret_cast<const bf16x8*>(wp + (int64_t)16 * jb * kDC + 32 * ks);
     }
-    f32x16 acc = f32x16{};
+
+    // ---- merge ----
+    {
+        const int s = s0 + wave;                          // wave-uniform
+        f32x4 va = f32x4{}, vb = f32x4{};
+        if (s < nseq) {
+            const int2 pt = part[s];
+            if (pt.y <= 1) {
+                const float* lp = Olat + ((int64_t)s * H + h) * kDC + 8 * lane;
+                va = *reinterpret_cast<const f32x4*>(lp);
+                vb = *reinterpret_cast<const f32x4*>(lp + 4);
+            } else {
+                const int64_t slot0 = pt.x;
+                const int n = pt.y;
+                float m = kNegInf, L = 0.f;
+                // parts in batches of 8: all loads of a batch are issued
+                // before the first of them is used (one memory round trip)
+                constexpr int kB = 8;
+                for (int c0 = 0; c0 < n; c0 += kB) {
+                    float lcv[kB];
+                    f32x4 xa[kB], xb[kB];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        bf16x8 hi, lo;
-        split_bf16x8(la[k], lb[k], hi, lo);
-        acc = mfma32(wa[k], hi, acc);
-        acc = mfma32(wa[k], lo, acc);
-    }
-    if (wave > 0) {
-        float* r = red[wave - 1] + lane * 16;
+                    for (int j = 0; j < kB; ++j) {
+                        const int64_t row = (slot0 + min(c0 + j, n - 1)) * Hp + h;
+                        lcv[j] = ws_lse[row];
+                        const float* vp = ws_o + row * kDC + 8 * lane;
+                        xa[j] = *reinterpret_cast<const f32x4*>(vp);
+                        xb[j] = *reinterpret_cast<const f32x4*>(vp + 4);
+                    }
 #pragma unroll
-        for (int q = 0; q < 16; q += 4) *reinterpret_cast<f32x4*>(r + q) = f32x4{acc[q], acc[q + 1], acc[q + 2], acc[q + 3]};
+                    for (int j = 0; j < kB; ++j) {
+                        // (a part past the last counts with weight 0 and
+                        // leaves the state as it is)
+                        const float lc = c0 + j < n ? lcv[j] : kNegInf;
+                        const float mn = fmaxf(m, lc);
+                        const float mu = mn == kNegInf ? 0.f : mn;
+                        const float r = exp2f_hw((m - mu) * kLog2e), w = exp2f_hw((lc - mu) * kLog2e);
+                        m = mn;
+                        L = fmaf(L, r, w);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            va[e] = fmaf(va[e], r, w * xa[j][e]);
+                            vb[e] = fmaf(vb[e], r, w * xb[j][e]);
+                        }
+                    }
+                }
+                const float inv = L > 0.f ? 1.f / L : 0.f;
+                va *= inv;
+                vb *= inv;
+                if (LSE != nullptr && lane == 0) LSE[(int64_t)s * H + h] = L > 0.f ? m + log2f_hw(L) * kLn2 : kNegInf;
+            }
+        }
+        float* dst = cl + wave * kRowU + 8 * lane;
+        *reinterpret_cast<f32x4*>(dst) = va;
+        *reinterpret_cast<f32x4*>(dst + 4) = vb;
     }
     __syncthreads();
-    if (wave > 0 || s >= nseq) return;
+
+    // ---- up-projection: D[j][s] over i ----
+    f32x4 acc[2] = {f32x4{}, f32x4{}};
+    const float* brow = cl + (l16 % kSeqU) * kRowU + 8 * g;
 #pragma unroll
-    for (int w = 0; w < 3; ++w) {
-        const float* r = red[w] + lane * 16;
+    for (int ks = 0; ks < kDC / 32; ++ks) {
+        const f32x4 xa = *reinterpret_cast<const f32x4*>(brow + 32 * ks);
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(brow + 32 * ks + 4);
+        bf16x8 hi, lo;
+        split_bf16x8(xa, xb, hi, lo);
 #pragma unroll
-        for (int q = 0; q < 16; q += 4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(r + q);
-            acc[q] += v[0];
-            acc[q + 1] += v[1];
-            acc[q + 2] += v[2];
-            acc[q + 3] += v[3];
+        for (int jb = 0; jb < 2; ++jb) {
+            acc[jb] = mfma16(wa[jb][ks], hi, acc[jb]);
+            acc[jb] = mfma16(wa[jb][ks], lo, acc[jb]);
         }
     }
-    uint16_t* out = O + ((int64_t)s * H + h) * kDH + j0;
+    const int s = s0 + l16;
+    if (l16 >= kSeqU || s >= nseq) return;
+    uint16_t* out = O + ((int64_t)s * H + h) * kDH + 32 * wave + 4 * g;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int j = 8 * a + 4 * hh;
-        *reinterpret_cast<u32x2*>(out + j) =
-            u32x2{pack_bf16x2(acc[4 * a], acc[4 * a + 1]), pack_bf16x2(acc[4 * a + 2], acc[4 * a + 3])};
-    }
+    for (int jb = 0; jb < 2; ++jb)
+        *reinterpret_cast<u32x2*>(out + 16 * jb) =
+            u32x2{pack_bf16x2(acc[jb][0], acc[jb][1]), pack_bf16x2(acc[jb][2], acc[jb][3])};
 }
 
 struct MlaLayout {
@@ -574,12 +586,10 @@ hipError_t launch_mla_decode(const MlaArgs& a, void* workspace, hipStream_t stre
                          a.scale * kLog2e);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    launch_kernel<false>(mla_combine_kernel, dim3((unsigned)a.nseq, (unsigned)a.H), dim3(kThreadsC), 0, stream, wo, wl,
-                         (const int2*)part, olat, a.lse, a.H, kHG * hg);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    launch_kernel(mla_upproj_kernel, dim3((unsigned)a.H, kDH / 32, sblocks), dim3(kThreadsL), 0, stream,
-                  (const float*)olat, (const uint16_t*)a.w_uv_t, (uint16_t*)a.o, a.nseq, a.H);
+    launch_kernel(mla_merge_upproj_kernel, dim3((unsigned)a.H, (unsigned)((a.nseq + kSeqU - 1) / kSeqU)),
+                  dim3(kThreadsL), 0, stream,
+                  (const float*)olat, (const float*)wo, (const float*)wl, (const int2*)part, (const uint16_t*)a.w_uv_t,
+                  (uint16_t*)a.o, a.lse, a.nseq, a.H, kHG * hg);
     return hipGetLastError();
 }
 
