@@ -9,15 +9,15 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
 //   dQ = scale dS K,  dK = scale dS^T Q,
 //
-// (D_i equals sum_j P_ij dP_ij because O = P V).  Three kernels, no atomics:
+// (D_i equals sum_j P_ij dP_ij because O = P V).  Two kernels, no atomics:
 //
-//   * bwd_delta_kernel: D for every query row (16 lanes per row, DPP sum).
 //   * bwd_dq_kernel: one workgroup per (batch, query head, 128-row Q block),
 //     walking the K/V blocks the rows can see, like the forward.  Each wave
-//     owns 32 query rows and computes S^T = K Q^T and dP^T = V dO^T on the
-//     matrix cores (so every lane holds one query row: its lse and D are one
-//     value), forms dS^T in registers, and accumulates dQ^T += K^T dS^T with
-//     the K tile read transposed from LDS.
+//     owns 32 query rows; it forms D of its rows from the dO rows it holds
+//     and the O rows (and stores D for the next kernel), computes S^T = K Q^T
+//     and dP^T = V dO^T on the matrix cores (so every lane holds one query
+//     row: its lse and D are one value), forms dS^T in registers, and
+//     accumulates dQ^T += K^T dS^T with the K tile read transposed from LDS.
 //   * bwd_dkdv_kernel: one workgroup per (batch, K/V head, 128-key block),
 //     each wave owning 32 keys, walking the query heads of the GQA group and
 //     their 32-row Q blocks that see the keys.  S = Q K^T and dP = dO V^T put
@@ -143,27 +143,6 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16 (&acc)[kD
         }
 }
 
-// D_i = sum_d dO_id O_id for every query row; one row per 16 lanes.
-__global__ __launch_bounds__(kThreadsB) void bwd_delta_kernel(const uint16_t* __restrict__ O,
-                                                              const uint16_t* __restrict__ dO,
-                                                              float* __restrict__ delta, int64_t rows) {
-    const int64_t row = (int64_t)blockIdx.x * (kThreadsB / 16) + (threadIdx.x >> 4);
-    const int t = threadIdx.x & 15;
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 o = *reinterpret_cast<const u32x4*>(O + row * kD + 8 * t);
-        const u32x4 g = *reinterpret_cast<const u32x4*>(dO + row * kD + 8 * t);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const uint32_t ow = o[w], gw = g[w];
-            acc = fmaf(bf16lo_to_f32(ow), bf16lo_to_f32(gw), acc);
-            acc = fmaf(bf16hi_to_f32(ow), bf16hi_to_f32(gw), acc);
-        }
-    }
-    acc = row_sum16(acc);
-    if (row < rows && t == 0) delta[row] = acc;
-}
-
 // Wave-group barrier waits of the pair-grid dQ kernel that ran out, per
 // device (read and cleared by read_bwd_sync_timeouts).
 __device__ unsigned int g_bwd_sync_timeouts;
@@ -184,9 +163,9 @@ __device__ __forceinline__ float lse_offset(float lse) { return lse == kNegInf ?
 template <bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2, float scale, int n_qblk,
-    int split_bias, int sync_spins) {
+    const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+    float* __restrict__ delta, uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
+    float scale, int n_qblk, int split_bias, int sync_spins) {
     // per wave group two stages of (K tile, V tile): the next block lands
     // while this one is used; pair mode adds the groups' barrier counters
     constexpr int GROUP_LDS = 2 * 2 * kKVBlk * kROWB;
@@ -230,7 +209,8 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) voi
     f32x16 dq[kD / 32];
 
     // One job: query block qb against key blocks [kb0, kb1); with `final` its
-    // dQ is written, else it stays in dq.
+    // dQ is written, else it stays in dq.  The job that starts at key block 0
+    // also writes D of its rows for the dK/dV kernel.
     auto run_job = [&](const int qb, const int kb0, const int kb1, const bool final) __attribute__((always_inline)) {
     const int qw = qb * kQRows + wave * 32;        // first query row of this wave
     const int my_q = qw + l32;
@@ -238,7 +218,20 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) voi
     load_row_operands(qf, Q + bhq * Sq * kD, my_q, Sq, hh);
     load_row_operands(gf, dO + bhq * Sq * kD, my_q, Sq, hh);
     const float lo = my_q < Sq ? lse_offset(LSE[bhq * Sq + my_q]) : __builtin_inff();
-    const float Dq = my_q < Sq ? delta[bhq * Sq + my_q] : 0.f;
+    // D = sum_d dO O of this lane's row: the lane's 64 head-dim elements, then
+    // the other half of the row from lane l ^ 32 (rows past Sq: dO = 0, D = 0)
+    float Dq;
+    {
+        bf16x8 of[kD / 16];
+        load_row_operands(of, O + bhq * Sq * kD, my_q, Sq, hh);
+        float part = 0.f;
+#pragma unroll
+        for (int s_ = 0; s_ < kD / 16; ++s_)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf((float)gf[s_][e], (float)of[s_][e], part);
+        Dq = half_swap_sum(part);
+        if (kb0 == 0 && hh == 0 && my_q < Sq) delta[bhq * Sq + my_q] = Dq;
+    }
 #pragma unroll
     for (int i = 0; i < kD / 32; ++i) dq[i] = f32x16{};
 
@@ -669,11 +662,6 @@ constexpr int kDqSplitBias = 0;
 template <bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
     const float scale_log2 = a.scale * kLog2e;
-    const int64_t rows = (int64_t)a.B * a.Hq * a.Sq;
-    launch_kernel<false>(bwd_delta_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(kThreadsB), 0, stream,
-                       (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const int n_qblk = (a.Sq + kQRows - 1) / kQRows;
     const int n_pairs = (n_qblk + 1) / 2;
     // pair grid for dQ: a causal square problem whose heavy/light query-block
@@ -682,15 +670,17 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
         (int64_t)a.B * a.Hq * n_pairs <= bwd_cus()) {
         launch_kernel<false>((bwd_dq_kernel<CAUSAL, true>), dim3((unsigned)((int64_t)a.B * a.Hq * n_pairs)),
                              dim3(2 * kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                             (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq,
-                             a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, kDqSplitBias, a.sync_spins);
+                             (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
+                             (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, kDqSplitBias,
+                             a.sync_spins);
     } else {
         launch_kernel<false>((bwd_dq_kernel<CAUSAL, false>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)),
                              dim3(kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                             (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta, (uint16_t*)a.dq, a.B, a.Hq,
-                             a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, 0, a.sync_spins);
+                             (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
+                             (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, 0,
+                             a.sync_spins);
     }
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kblk = (a.Sk + kKRows - 1) / kKRows;
     launch_kernel((bwd_dkdv_kernel<CAUSAL>), dim3((unsigned)((int64_t)a.B * a.Hkv * n_kblk)), dim3(kThreadsB), 0,
