@@ -318,9 +318,16 @@ def main():
         st = metrics.summarize([a.elapsed_ms(b) for a, b in evs])
         return st, lead_report(lead, host_s)
 
+    # ---- the fp32 workload on its own (the step times it once per step) ----
+    if not args.no_extra:
+        st_f, _ = time_calls(lambda: binding.fa_fwd(f_q, f_k, f_v, cf.causal, cf.scale, out=f_o, lse=f_l),
+                             max(5, min(K * 3, 60)), False, 0.05)
+        result["per_config"][FP32]["launch_us_alone"] = us(st_f)
+        result["per_config"][FP32]["reps_alone"] = max(5, min(K * 3, 60))
+
     # ---- the 2k and 8k prefill workloads, each on its own, cold caches ----
     if not args.no_extra:
-        for name, reps in ((PREFILL2K, max(5, min(K * 3, 60))), (PREFILL8K, max(5, min(K * 2, 40)))):
+        for name, reps in ((PREFILL2K, max(5, min(K * 3, 60))), (PREFILL8K, max(5, min(K * 3, 60)))):
             log(f"generating {name}")
             c = inputs.workload(name)
             s = c.shape
