@@ -282,6 +282,7 @@ SHAPES = [
     (1, 8, 2, 640, 640, True),     # pair grid, odd number of query blocks
     (1, 4, 4, 256, 256, True),     # pair grid, group A takes all of the heavy block
     (2, 2, 1, 384, 384, True),     # pair grid, MQA, odd
+    (1, 16, 8, 1024, 1024, True),  # pair grid with the XCD head map (8 K/V heads), GQA
 ]
 
 
