@@ -242,10 +242,16 @@ def main():
     def prefill_roofline(kernel, flops, st, prof, note):
         pr = profiling.current_profile(prof)
         tf = flops / (st["mean"] * 1e-3) / 1e12
+        # the shader clock the kernel ran at under the profiler: its active
+        # cycles per XCD over its mean duration (counter and trace passes)
+        sclk = (pr["active_cycles"] / pr["kernel_avg_us"]
+                if pr["active_cycles"] and pr["kernel_avg_us"] else None)
         return {
             "kernel": kernel, "bound": "mfma", "achieved": round(tf, 2), "peak": peak_tf, "unit": "TFLOP/s",
             "frac": round(tf / peak_tf, 4), "traffic": pr["traffic"],
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "effective_sclk_mhz": round(sclk, 0) if sclk else None,
+            "frac_of_peak_at_effective_sclk": round(tf / (peak_tf * sclk / 2400.0), 4) if sclk else None,
             "mfma_busy": pr["mfma_busy"], "profile": pr["profile"], "profile_kernel_avg_us": pr["kernel_avg_us"],
             "algorithmic_flops_per_launch": flops, "launch_us": us(st), "caches": note,
             "launch_timing": "HIP events recorded by the kernel launch itself (hipExtLaunchKernel; "

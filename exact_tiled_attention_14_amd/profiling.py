@@ -235,6 +235,7 @@ def _summarize(args) -> None:
                       f"SQ_INSTS_MFMA {insts:.4g}.  Busy fraction = MFMA busy cycles / (active cycles x {simds} "
                       f"SIMDs) = {frac:.3f}.", ""]
             kv["mfma_busy_fraction"] = f"{frac:.4f}"
+            kv["gui_active_cycles_per_xcd"] = f"{cycles:.0f}"
     if args.source:
         kv["source"] = args.source
         kv["source_sha256"] = source_sha256(args.source)
@@ -264,11 +265,13 @@ def read_profile_values(path: str) -> dict:
 
 def current_profile(path: str) -> dict:
     """The figures of a summary that still describe the current kernel source:
-    ``traffic`` (HBM bytes per launch), ``mfma_busy`` (busy fraction) and
-    ``kernel_avg_us`` (rocprofv3's mean duration), each None when missing or
-    when the kernel source has changed since the profile was taken."""
+    ``traffic`` (HBM bytes per launch), ``mfma_busy`` (busy fraction),
+    ``kernel_avg_us`` (rocprofv3's mean duration) and ``active_cycles``
+    (GRBM_GUI_ACTIVE per XCD per launch), each None when missing or when the
+    kernel source has changed since the profile was taken."""
     vals = read_profile_values(path)
-    out = {"traffic": None, "mfma_busy": None, "kernel_avg_us": None, "profile": os.path.relpath(path, ROOT)}
+    out = {"traffic": None, "mfma_busy": None, "kernel_avg_us": None, "active_cycles": None,
+           "profile": os.path.relpath(path, ROOT)}
     try:
         fresh = "source" in vals and source_sha256(vals["source"]) == vals.get("source_sha256")
     except OSError:
@@ -276,7 +279,7 @@ def current_profile(path: str) -> dict:
     if not fresh:
         return out
     for key, name in (("hbm_bytes_per_launch", "traffic"), ("mfma_busy_fraction", "mfma_busy"),
-                      ("kernel_avg_us", "kernel_avg_us")):
+                      ("kernel_avg_us", "kernel_avg_us"), ("gui_active_cycles_per_xcd", "active_cycles")):
         if key in vals:
             out[name] = float(vals[key])
     return out
