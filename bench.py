@@ -423,7 +423,7 @@ def main():
             total_us = sum(st[n]["mean"] for n in names) * 1e3
             bf16_2k = result["per_config"].get(PREFILL2K, {}).get("launch_us", {}).get("mean")
             result["fp8"] = {
-                "workload": PREFILL2K, "kernel": "fwd_fp8_kernel<causal>", "bound": "mfma",
+                "workload": PREFILL2K, "kernel": "fwd_fp8_kernel<causal,pair>", "bound": "mfma",
                 "achieved": round(tf8, 1), "peak": peak8, "unit": "TFLOP/s", "frac": round(tf8 / peak8, 4),
                 "traffic": profiling.current_profile(PROFILES["fp8"])["traffic"],
                 "algorithmic_flops_per_launch": fl2k,
