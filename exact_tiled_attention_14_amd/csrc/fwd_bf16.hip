@@ -330,12 +330,16 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
                 *reinterpret_cast<u32x2*>(ot + l32 * T::ROWB + 16 * (c ^ (l32 & (CH - 1))) + 8 * hh) = w;
             }
         gsync();
+        // Whole rows go out with the non-temporal hint: nothing in this
+        // kernel reads O back.  (Only for these full-line stores: partial
+        // 8-byte pieces stored this way were far slower.)
         const int rr = ln / CH, cc = ln % CH;
 #pragma unroll
         for (int r8 = 0; r8 < 32 / RPP; ++r8) {
             const int r = r8 * RPP + rr;
             const u32x4 v = *reinterpret_cast<const u32x4*>(ot + r * T::ROWB + 16 * (cc ^ (r & (CH - 1))));
-            if (qw + r < Sq) *reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc) = v;
+            if (qw + r < Sq)
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(O + q_off + (int64_t)(qw + r) * D + 8 * cc));
         }
         if (LSE != nullptr && hh == 0 && my_q < Sq)
             LSE[((int64_t)b * Hq + hq) * Sq + my_q] = sync_fail    ? __builtin_nanf("")
