@@ -450,6 +450,23 @@ def main():
                 "note": "Q alone (rotated), K and V held in FP8 from an earlier quantization",
             }
             log(f"fp8: quantize q alone {q_us:.1f} us")
+            # The same with Q quantized inside the forward (fa_fwd_fp8_qbf16):
+            # one launch, Q read once in bf16, its codes never written.
+            k8h, ksh, v8h, vsh = binding.fa_quantize_fp8_qkv(b_q, b_k, b_v, rot=rot)[2:]
+            st_f, _ = time_calls(lambda: binding.fa_fwd_fp8_qbf16(b_q, k8h, ksh, v8h, vsh, True, rot=rot,
+                                                                  scale=cb.scale, out=b_o, lse=b_l),
+                                 reps, True, 0.1)
+            f_us = st_f["mean"] * 1e3
+            result["fp8"]["forward_q_bf16"] = {
+                "entry_point": "fa_fwd_fp8_qbf16", "kernel": "fwd_fp8_kernel<causal,pair,qbf16>",
+                "us": round(f_us, 2), "TFLOP/s": round(fl2k / (f_us * 1e-6) / 1e12, 1),
+                "vs_bf16_forward": round(bf16_2k / f_us, 3) if bf16_2k else None,
+                "launch_us": us(st_f),
+                "note": "Q in bf16, rotated and quantized inside the forward (bit-identical to quantize + "
+                        "fa_fwd_fp8); K and V held in FP8 from an earlier quantization; caches flushed",
+            }
+            log(f"fp8: forward with Q quantized inside {f_us:.1f} us")
+            del k8h, ksh, v8h, vsh
         del b_q, b_k, b_v, b_o, b_l, g_do, b_dq, b_dk, b_dv, b_ws
         torch.cuda.empty_cache()
 

@@ -51,6 +51,7 @@ SIGNATURES = {
     "fa_quantize_fp8": ([_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp], _i),
     "fa_quantize_fp8_qkv": ([_vp] * 10 + [_i] * 6 + [_vp], _i),
     "fa_fwd_fp8": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
+    "fa_fwd_fp8_qbf16": ([_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _vp], _i),
     "fa_time_next_call": ([_vp, _vp], _i),
     "fa_limit_next_sync_wait": ([_i], _i),
     "fa_sync_timeouts": ([_vp], _i),
@@ -326,6 +327,49 @@ def fa_fwd_fp8(q8, q_scale, k8, k_scale, v8, v_scale, causal: bool, scale: float
                         _ptr(lse), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _stream(q8.device))
     if st != FA_OK:
         raise FAError("fa_fwd_fp8", st)
+    return out, lse
+
+
+def fa_fwd_fp8_qbf16(q, k8, k_scale, v8, v_scale, causal: bool, rot=None, scale: float | None = None, out=None,
+                     lse=None):
+    """FP8 forward with Q given in bf16 [B,Hq,Sq,d] and quantized inside the
+    kernel (128-row blocks, times ``rot`` if given: the rotation K was
+    quantized with); k8/k_scale and v8/v_scale as for :func:`fa_fwd_fp8`.
+    Bit-identical to ``fa_fwd_fp8(*fa_quantize_fp8(q, 128, rot=rot), ...)``.
+    Returns ``(o bf16 [B,Hq,Sq,d], lse fp32 [B,Hq,Sq])``."""
+    lib = load()
+    u8 = torch.uint8
+    _check(q, "q", torch.bfloat16, 4)
+    _check(k8, "k8", u8, 4, q.device)
+    _check(v8, "v8", u8, 5, q.device)
+    B, Hq, Sq, d = q.shape
+    Hkv, Sk = k8.shape[1], k8.shape[2]
+    nk = -(-Sk // 64)
+    if tuple(k8.shape) != (B, Hkv, Sk, d) or tuple(v8.shape) != (B, Hkv, nk, d, 64):
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k8={tuple(k8.shape)} v8={tuple(v8.shape)}")
+    for t, n in ((k_scale, "k_scale"), (v_scale, "v_scale")):
+        _check(t, n, u8, 3, q.device)
+        if tuple(t.shape) != (B, Hkv, nk):
+            raise ValueError(f"{n} must be {(B, Hkv, nk)}")
+    if rot is not None:
+        _check(rot, "rot", torch.bfloat16, 2, q.device)
+        if tuple(rot.shape) != (d, d):
+            raise ValueError("rot must be [d, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, Hq, Sq, d), dtype=torch.bfloat16, device=q.device)
+    else:
+        _check(out, "out", torch.bfloat16, (B, Hq, Sq, d), q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    else:
+        _check(lse, "lse", torch.float32, (B, Hq, Sq), q.device)
+    _on_gpu(q, rot, k8, v8, k_scale, v_scale, out, lse)
+    st = lib.fa_fwd_fp8_qbf16(_ptr(q), _ptr(rot), _ptr(k8), _ptr(v8), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                              _ptr(lse), B, Hq, Hkv, Sq, Sk, d, int(bool(causal)), float(scale), _stream(q.device))
+    if st != FA_OK:
+        raise FAError("fa_fwd_fp8_qbf16", st)
     return out, lse
 
 

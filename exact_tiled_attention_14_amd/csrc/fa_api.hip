@@ -211,7 +211,27 @@ int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_
     if (d != 128) return FA_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * ((Sq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
     fa::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale,
-                     fa::next_sync_spins()};
+                     fa::next_sync_spins(), 0, nullptr};
+    return fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+int fa_fwd_fp8_qbf16(const void* q, const void* rot, const void* k8, const void* v8, const uint8_t* k_scale,
+                     const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     int causal, float scale, void* stream) {
+    TimingScope timing_scope;
+    SpinScope spin_scope;
+    if (!q || !k8 || !v8 || !k_scale || !v_scale || !o) return FA_ERR_INVALID_ARG;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || d < 1) return FA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0 || (causal != 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || (rot && !aligned16(rot)))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return FA_ERR_INVALID_ARG;
+    if (!fits(B, Hq, Sq, d) || !fits(B, Hkv, Sk + 63, d)) return FA_ERR_INVALID_ARG;
+    if (d != 128) return FA_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * ((Sq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    fa::Fp8FwdArgs a{q, k8, v8, nullptr, k_scale, v_scale, o, lse, B, Hq, Hkv, Sq, Sk, causal, scale,
+                     fa::next_sync_spins(), 1, rot};
     return fa::launch_fwd_fp8(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

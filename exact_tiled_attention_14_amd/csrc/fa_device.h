@@ -110,6 +110,72 @@ __device__ __forceinline__ bool group_barrier(uint8_t* ctr_p, int& target, int l
     return timed_out;
 }
 
+// ---- FP8 block encoding, one definition for the quantizer and the forward
+// that quantizes Q itself, so both give the same codes ----
+
+// E8M0 exponent of a block scale 2^e: the smallest e with amax <= 448 2^e.
+// amax = M 2^E with M in [1, 2) and 448 = 1.75 2^8, so e = E - 8, plus one
+// when M > 1.75; clamped to the E8M0 range; amax = 0 gives e = 0.
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+    if (!(amax > 0.f)) return 0;
+    const uint32_t b = __float_as_uint(amax);
+    const int E = (int)((b >> 23) & 255u) - 127;
+    const int e = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+    return min(max(e, -127), 127);
+}
+
+// 2^-e as an fp32 value (e in [-127, 120] for any finite fp32 amax).
+__device__ __forceinline__ float fp8_inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
+
+// Four fp32 values -> four E4M3 bytes (round to nearest even), low byte first.
+__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+    return (uint32_t)r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Stage the 128 x 128 bf16 rotation R (or the identity when rot is NULL) in
+// LDS with NT threads, all loads in flight together; 16-byte chunk c of row n
+// sits at chunk c ^ (n % 16), so operand reads of 32 rows and one chunk
+// spread over all banks.  The caller issues the barrier.
+template <int NT>
+__device__ __forceinline__ void stage_rotation128(const uint16_t* __restrict__ rot, uint16_t* rt, int tid) {
+    constexpr int D = 128;
+    constexpr int NST = D * D / 8 / NT;
+    static_assert(NST * NT * 8 == D * D, "staging split");
+    u32x4 rv[NST];
+    if (rot != nullptr) {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int c = tid + NT * i;
+            rv[i] = *reinterpret_cast<const u32x4*>(rot + (c / (D / 8)) * D + 8 * (c % (D / 8)));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NST; ++i) {
+            const int c = tid + NT * i;
+            const int n = c / (D / 8), ch = c % (D / 8);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int k0 = 8 * ch + 2 * k;
+                rv[i][k] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+        const int c = tid + NT * i;
+        const int n = c / (D / 8), ch = c % (D / 8);
+        *reinterpret_cast<u32x4*>(rt + n * D + 8 * (ch ^ (n & 15))) = rv[i];
+    }
+}
+
 // Row (lane % 32 is the column) index of accumulator register r in lane half h.
 __device__ __forceinline__ constexpr int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

@@ -132,7 +132,7 @@ struct QuantArgs {
 };
 
 struct Fp8FwdArgs {
-    const void* q8;
+    const void* q8;        // E4M3 codes, or bf16 Q when q_bf16 is set
     const void* k8;
     const void* v8;        // d-major 64-key blocks
     const uint8_t* q_scale;
@@ -144,6 +144,8 @@ struct Fp8FwdArgs {
     int causal;
     float scale;
     int sync_spins;        // poll bound of the wave-group barriers (pair grid)
+    int q_bf16;            // q8 is bf16 Q, quantized by the kernel (q_scale unused)
+    const void* rot;       // with q_bf16: bf16 [128, 128] rotation of Q, or NULL
 };
 
 hipError_t launch_quant_fp8(const QuantArgs& a, hipStream_t stream);

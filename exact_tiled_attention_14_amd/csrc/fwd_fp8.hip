@@ -17,6 +17,14 @@
 // d-major 64-key blocks whose key order is the order in which a lane holds P,
 // so both operands of O^T += V^T P^T are plain 32-byte reads.
 //
+// With QB the kernel takes Q in bf16 and quantizes each job's 128-row block
+// itself, exactly as the quantizer does (rotation D = R X^T on the bf16
+// matrix cores with R staged in LDS, block maximum over the four waves, E8M0
+// scale, E4M3 conversion), so the codes and the scale are those the quantizer
+// would have written; the rotation leaves each lane half with alternate
+// groups of four head-dim values, and one lane-half swap per group pair
+// brings the 32 consecutive values the FP8 product's operand takes.
+//
 // LDS tiles: K rows are 128 bytes with 16-byte chunk c stored at
 // c ^ ((row / 4) % 8); V^T rows are 64 bytes with chunk c at c ^ ((row / 8) % 4).
 // Both operand read patterns (16 consecutive rows, one chunk) then hit
@@ -127,15 +135,20 @@ static_assert(kWaves8 == 4, "group_barrier counts four waves per group");
 // 4-wave groups with their own K/V stages and barrier, group A walking key
 // blocks [0, split) of block i, group B all of block p and then the rest of
 // block i, and the two partial softmax states of block i merged through LDS.
-template <bool CAUSAL, bool PAIR>
+template <bool CAUSAL, bool PAIR, bool QB>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
-    int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias, int sync_spins) {
+    const uint16_t* __restrict__ ROT, uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv,
+    int Sq, int Sk, float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias,
+    int sync_spins) {
     constexpr int GROUP_LDS = 4 * kTile8;      // K stages 0, 1 and V stages 0, 1
-    // pair mode: both groups' stages, their barrier counters, the merge's (m, l)
-    __shared__ __attribute__((aligned(1024))) uint8_t lds[PAIR ? 2 * GROUP_LDS + 64 + kWaves8 * 64 * 8 : GROUP_LDS];
+    // pair mode: both groups' stages, their barrier counters, the merge's (m, l);
+    // QB: then the rotation (32 KiB) and the Q block maxima of the groups' waves
+    constexpr int BASE_LDS = PAIR ? 2 * GROUP_LDS + 64 + kWaves8 * 64 * 8 : GROUP_LDS;
+    constexpr int ROT_LDS = (BASE_LDS + 1023) / 1024 * 1024;
+    constexpr int AMAX_LDS = ROT_LDS + kD8 * kD8 * 2;
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[QB ? AMAX_LDS + 2 * kWaves8 * 4 : BASE_LDS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -151,8 +164,9 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     bool sync_fail = false;             // a wave-group barrier of this wave ran out (its rows become NaN)
     if constexpr (PAIR) {
         if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
-        __syncthreads();
     }
+    if constexpr (QB) stage_rotation128<PAIR ? 2 * kThreads8 : kThreads8>(ROT, reinterpret_cast<uint16_t*>(lds + ROT_LDS), tid);
+    if constexpr (PAIR || QB) __syncthreads();
     // barrier of the threads that share this workgroup's (or wave group's) K/V stages
     auto gsync = [&]() __attribute__((always_inline)) {
         if constexpr (PAIR) {
@@ -238,7 +252,6 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     const int q0 = qb * kBM8;
     const int qw = q0 + wave * 32;
     const int my_q = qw + l32;
-    const int sq = QS[bhq * n_qblk + qb];
     const int n_it = kb1 - kb0;
 
     // Q fragment (B operand of S^T = K Q^T): head-dim bytes 64 s + 32 h .. +31.
@@ -246,7 +259,15 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     // written out, and without a select on the values the loads' latency
     // overlaps that of the first K/V loads.
     i32x8 qf[2];
-    {
+    int sq;
+    bf16x8 xq[kD8 / 16];                // QB: this lane's bf16 row, head-dim 16 s + 8 h .. +7
+    if constexpr (QB) {
+        // a row past Sq repeats row Sq - 1 (same block), so the block maximum is unchanged
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(Q) + (bhq * Sq + min(my_q, Sq - 1)) * kD8 + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < kD8 / 16; ++s) xq[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+    } else {
+        sq = QS[bhq * n_qblk + qb];
         const uint8_t* qp = Q + (bhq * Sq + min(my_q, Sq - 1)) * kD8 + 32 * hh;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -304,6 +325,59 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
         dma_v8(Vh + (int64_t)kb0 * kTile8, vbuf, v_lane_off, wave);
     }
     if (n_it > 1) dma_k8(Kh, kbuf + kTile8, k_lane_off, (kb0 + 1) * kBN8, Sk, wave);
+
+    if constexpr (QB) {
+        // ---- quantize the Q block while the first tiles load: D = R X^T for
+        // this wave's 32 rows (lane: rotated entries 32 i + 8 a + 4 h + e of its
+        // row), the block's largest |value| over the group's four waves, its
+        // E8M0 scale, E4M3 codes ----
+        const uint16_t* rt = reinterpret_cast<const uint16_t*>(lds + ROT_LDS);
+        f32x16 acc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < kD8 / 16; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 32 * i + l32;
+                const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rt + n * kD8 + 8 * ((2 * s + hh) ^ (n & 15)));
+                acc[i] = mfma32(ra, xq[s], acc[i]);
+            }
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, fabsf(acc[i][r]));
+        m = wave_max(m);
+        float* const amax = reinterpret_cast<float*>(lds + AMAX_LDS) + kWaves8 * grp;
+        if (lane == 0) amax[wave] = m;
+        gsync();
+        m = fmaxf(fmaxf(amax[0], amax[1]), fmaxf(amax[2], amax[3]));
+        const int e = fp8_scale_exp(m);
+        sq = e + 127;
+        const float inv = fp8_inv_scale(e);
+        uint32_t c[4][4];                // codes of entries 32 i + 8 a + 4 h .. +3
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+                c[i][a] = pack_fp8x4(acc[i][4 * a] * inv, acc[i][4 * a + 1] * inv, acc[i][4 * a + 2] * inv,
+                                     acc[i][4 * a + 3] * inv);
+        // operand s takes head-dim 64 s .. +31 in the lower lane half and
+        // 64 s + 32 .. +31 in the upper: the lower half gets the upper half's
+        // groups of block 2s, the upper half the lower half's of block 2s + 1
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            int w[8];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const auto r = __builtin_amdgcn_permlane32_swap(c[2 * s][a], c[2 * s + 1][a], false, false);
+                w[2 * a] = (int)r[0];
+                w[2 * a + 1] = (int)r[1];
+            }
+            qf[s] = i32x8{w[0], w[1], w[2], w[3], w[4], w[5], w[6], w[7]};
+        }
+    }
     wait_dma8();
     gsync();
 
@@ -489,7 +563,7 @@ int num_cus8() {
 // workgroup, for n query blocks.
 int fp8_split_bias(int n_qblk) { return 2 + 3 * n_qblk / 16; }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool QB>
 hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     const int n_qblk = (a.Sq + kBM8 - 1) / kBM8;
     const int units = a.B * a.Hkv;
@@ -502,10 +576,10 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
         const int n_pairs = (n_qblk + 1) / 2;
         if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
             const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
-            launch_kernel((fwd_fp8_kernel<CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,
+            launch_kernel((fwd_fp8_kernel<CAUSAL, true, QB>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,
                           (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale,
-                          a.v_scale, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs,
-                          xcd_groups, 0, fp8_split_bias(n_qblk), a.sync_spins);
+                          a.v_scale, (const uint16_t*)a.rot, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
+                          scale_log2, n_qblk, n_pairs, xcd_groups, 0, fp8_split_bias(n_qblk), a.sync_spins);
             return hipGetLastError();
         }
     }
@@ -513,17 +587,18 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     // Two workgroups fit on a CU; if the whole grid is resident at once, pair
     // heavy and light causal Q blocks on the same CU.
     const int mirror = (CAUSAL && n_wg <= 2 * (int64_t)cus) ? 1 : 0;
-    launch_kernel((fwd_fp8_kernel<CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads8), 0, stream,
+    launch_kernel((fwd_fp8_kernel<CAUSAL, false, QB>), dim3((unsigned)n_wg), dim3(kThreads8), 0, stream,
                   (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale, a.v_scale,
-                  (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror,
-                  0, a.sync_spins);
+                  (const uint16_t*)a.rot, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk,
+                  n_qblk, xcd_groups, mirror, 0, a.sync_spins);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
-    return a.causal ? launch8<true>(a, stream) : launch8<false>(a, stream);
+    if (a.q_bf16) return a.causal ? launch8<true, true>(a, stream) : launch8<false, true>(a, stream);
+    return a.causal ? launch8<true, false>(a, stream) : launch8<false, false>(a, stream);
 }
 
 hipError_t read_fp8_sync_timeouts(unsigned int* count) {

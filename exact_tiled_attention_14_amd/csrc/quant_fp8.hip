@@ -35,66 +35,6 @@ namespace {
 constexpr int kQD = 128;
 constexpr int kQThreads = 256;
 
-// E8M0 exponent of the block scale: amax = M 2^E with M in [1, 2); since
-// 448 = 1.75 * 2^8, e = E - 8, plus one when M > 1.75.  e is clamped to the
-// E8M0 range; amax = 0 gives e = 0.
-__device__ __forceinline__ int scale_exp(float amax) {
-    if (!(amax > 0.f)) return 0;
-    const uint32_t b = __float_as_uint(amax);
-    const int E = (int)((b >> 23) & 255u) - 127;
-    const int e = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-    return min(max(e, -127), 127);
-}
-
-// 2^-e as an fp32 value (e in [-127, 120] for any finite fp32 amax).
-__device__ __forceinline__ float inv_scale(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
-
-// Four fp32 values -> four E4M3 bytes (round to nearest even), low byte first.
-__device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
-    int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
-    return (uint32_t)r;
-}
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-    return x;
-}
-
-// Stage R (or the identity) in LDS, all loads in flight together; 16-byte
-// chunk c of row n sits at chunk c ^ (n % 16), so the operand reads (32 rows,
-// one chunk) spread over all banks.  The caller issues the barrier.
-__device__ __forceinline__ void stage_rotation(const uint16_t* __restrict__ rot, uint16_t* rt, int tid) {
-    constexpr int NST = kQD * kQD / 8 / kQThreads;
-    static_assert(NST * kQThreads * 8 == kQD * kQD, "staging split");
-    u32x4 rv[NST];
-    if (rot != nullptr) {
-#pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            const int c = tid + kQThreads * i;
-            rv[i] = *reinterpret_cast<const u32x4*>(rot + (c / (kQD / 8)) * kQD + 8 * (c % (kQD / 8)));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            const int c = tid + kQThreads * i;
-            const int n = c / (kQD / 8), ch = c % (kQD / 8);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int k0 = 8 * ch + 2 * k;
-                rv[i][k] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < NST; ++i) {
-        const int c = tid + kQThreads * i;
-        const int n = c / (kQD / 8), ch = c % (kQD / 8);
-        *reinterpret_cast<u32x4*>(rt + n * kQD + 8 * (ch ^ (n & 15))) = rv[i];
-    }
-}
-
 // One block of R rows (64 or 128) of a row-major part.  Wave w computes rows
 // 32 (w % (R / 32)) .. +31 of the block against NB = R / 32 of the four
 // 32-row blocks of the rotation: D = Rot X^T, so lane l holds entries
@@ -192,8 +132,8 @@ __device__ __forceinline__ void rows_unit(uint8_t* __restrict__ X8, uint8_t* __r
     // waves 0, 1 hold rows 0..63, waves 2, 3 rows 64..127; the barrier inside
     // also ends every wave's reads of the rows
     const int half = wave >> 1;
-    const int e = scale_exp(unit_max(half ? 0.f : m, half ? m : 0.f, red, wave, lane, SB, half));
-    const float inv = inv_scale(e);
+    const int e = fp8_scale_exp(unit_max(half ? 0.f : m, half ? m : 0.f, red, wave, lane, SB, half));
+    const float inv = fp8_inv_scale(e);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -258,8 +198,8 @@ __device__ __forceinline__ void v_unit(uint8_t* __restrict__ V8, uint8_t* __rest
     for (int hb = 0; hb < 2; ++hb) {
         const int vb = 2 * j + hb;                 // the V block
         if (vb >= nblk) break;
-        const int e = scale_exp(hb ? a1 : a0);
-        const float inv = inv_scale(e);
+        const int e = fp8_scale_exp(hb ? a1 : a0);
+        const float inv = fp8_inv_scale(e);
         const uint16_t* vrows = vt + 64 * hb * kQD;
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -349,7 +289,7 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantParts parts, c
     if (q.kind == 2) {
         run_part<2>(q, first, rt, tile, red, tid);
     } else {
-        stage_rotation(rot, rt, tid);
+        stage_rotation128<kQThreads>(rot, rt, tid);
         __syncthreads();
         if (q.kind == 0)
             run_part<0>(q, first, rt, tile, red, tid);

@@ -40,8 +40,9 @@
  * Entry points: fa_fwd (prefill, bf16 or fp32), fa_bwd (its gradients),
  * fa_decode (one new token per sequence, paged cache), fa_decode_multi (Sq new
  * tokens per sequence, paged cache), fa_mla_decode (one new token per
- * sequence, paged latent cache), fa_quantize_fp8, fa_quantize_fp8_qkv and
- * fa_fwd_fp8 (FP8 forward with block scales), fa_time_next_call (measurement), plus the
+ * sequence, paged latent cache), fa_quantize_fp8, fa_quantize_fp8_qkv,
+ * fa_fwd_fp8 (FP8 forward with block scales) and fa_fwd_fp8_qbf16 (the same
+ * with Q quantized inside the forward), fa_time_next_call (measurement), plus the
  * *_workspace_size / *_bytes size queries and fa_status_string.
  */
 #ifndef EXACT_TILED_ATTENTION_FA_H
@@ -390,6 +391,31 @@ int fa_quantize_fp8_qkv(const void* q, const void* k, const void* v, const void*
 int fa_fwd_fp8(const void* q8, const void* k8, const void* v8, const uint8_t* q_scale, const uint8_t* k_scale,
                const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
                int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_fp8_qbf16 - fa_fwd_fp8 with Q taken in bf16 and quantized inside the
+ * forward, for K and V already held in FP8 (quantized once, as a quantized
+ * KV cache keeps them).
+ *
+ * Passage: "FlashAttention scaling, multi-GPU training and weight
+ * quantization", section 1 (FP8 support, block quantization, incoherent
+ * processing); the algorithm is that of fa_fwd.
+ *
+ *   q   [B, Hq, Sq, 128] bf16, device, read-only.
+ *   rot [128, 128] bf16 rotation R applied to each row of Q before
+ *       quantization (the R that K was quantized with), or NULL.
+ *   k8, k_scale, v8, v_scale, o, lse: as for fa_fwd_fp8.
+ *
+ * The result is bit-identical to fa_quantize_fp8(q, rot, q8, q_scale, B, Hq,
+ * Sq, 128, 128, FA_FP8_ROWS) followed by fa_fwd_fp8(q8, k8, v8, q_scale, ...):
+ * the kernel forms each 128-row block's codes and E8M0 scale with the same
+ * arithmetic, but never writes them to memory.  Pointers 16-byte aligned
+ * (lse 4-byte); d must be 128, else FA_ERR_UNSUPPORTED.  Runs on `stream`;
+ * allocates nothing.  Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd_fp8_qbf16(const void* q, const void* rot, const void* k8, const void* v8, const uint8_t* k_scale,
+                     const uint8_t* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                     int causal, float scale, void* stream);
 
 /*
  * fa_time_next_call - kernel-boundary timing of the next call on this thread.

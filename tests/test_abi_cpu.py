@@ -30,7 +30,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_bwd_workspace_size", "fa_decode", "fa_decode_multi",
                            "fa_decode_multi_workspace_size", "fa_decode_noalloc", "fa_decode_workspace_size", "fa_fwd",
-                           "fa_fwd_fp8", "fa_limit_next_sync_wait", "fa_mla_decode", "fa_mla_decode_workspace_size",
+                           "fa_fwd_fp8", "fa_fwd_fp8_qbf16", "fa_limit_next_sync_wait", "fa_mla_decode", "fa_mla_decode_workspace_size",
                            "fa_quantize_fp8", "fa_quantize_fp8_bytes", "fa_quantize_fp8_qkv", "fa_status_string",
                            "fa_sync_timeouts",
                            "fa_time_next_call"]
@@ -211,6 +211,22 @@ def _fwd8(lib, q=16, k=32, v=48, qs=1, ks=2, vs=3, o=64, lse=0, B=1, Hq=2, Hkv=1
 ])
 def test_fwd_fp8_rejects_before_launch(lib, kw, status):
     assert _fwd8(lib, **kw) == status
+
+
+def _fwd8q(lib, q=16, rot=0, k=32, v=48, ks=2, vs=3, o=64, lse=0, B=1, Hq=2, Hkv=1, Sq=8, Sk=8, d=128, causal=1,
+           scale=0.1):
+    P = ctypes.c_void_p
+    return lib.fa_fwd_fp8_qbf16(P(q), P(rot) if rot else None, P(k), P(v), P(ks), P(vs), P(o),
+                                P(lse) if lse else None, B, Hq, Hkv, Sq, Sk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), -1), (dict(k=0), -1), (dict(vs=0), -1), (dict(o=0), -1), (dict(B=0), -1), (dict(Sk=0), -1),
+    (dict(Hq=3, Hkv=2), -1), (dict(causal=2), -1), (dict(scale=0.0), -1), (dict(q=24), -1), (dict(rot=72), -1),
+    (dict(lse=98), -1), (dict(d=64), -2),
+])
+def test_fwd_fp8_qbf16_rejects_before_launch(lib, kw, status):
+    assert _fwd8q(lib, **kw) == status
 
 
 def test_quantize_fp8_bytes(lib):

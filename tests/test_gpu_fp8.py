@@ -322,6 +322,84 @@ def test_fp8_forward_headline_shape(B):
             check_lse(lse[b:b + 1, h:h + 1], L, f"fp8 headline b{b} h{h}", slack)
 
 
+# --- Q quantized inside the forward (fa_fwd_fp8_qbf16) ---------------------------------
+
+def _same_bits(a, b):
+    """Bit-for-bit equality of two bf16 or fp32 tensors (NaN patterns included)."""
+    it = torch.int16 if a.dtype == torch.bfloat16 else torch.int32
+    return a.shape == b.shape and torch.equal(a.contiguous().view(it), b.contiguous().view(it))
+
+
+def _two_ways(Bm, c, R):
+    """The forward from bf16 Q two ways: quantize, then fa_fwd_fp8; and
+    fa_fwd_fp8_qbf16 on the same K/V codes."""
+    q = _bf(c.q)
+    q8, qs, k8, ks, v8, vs = Bm.fa_quantize_fp8_qkv(q, _bf(c.k), _bf(c.v), rot=R)
+    o1, l1 = Bm.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, c.causal, c.scale)
+    o2, l2 = Bm.fa_fwd_fp8_qbf16(q, k8, ks, v8, vs, c.causal, rot=R, scale=c.scale)
+    torch.cuda.synchronize()
+    return (o1, l1), (o2, l2)
+
+
+@pytest.mark.parametrize("rotated", [False, True], ids=["norot", "rot"])
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "B{}Hq{}Hkv{}Sq{}Sk{}{}".format(*s[:5], "c" if s[5] else "n"))
+def test_fp8_qbf16_bit_identical_to_quantize_then_forward(B, shape, rotated):
+    """The kernel's own Q codes and block scales are those of the quantizer,
+    so output and lse equal the two-step path's bit for bit (every shape of
+    the forward's parity tests: ragged blocks, rows with no visible key, the
+    pair grid with even and odd block counts, GQA, MQA and the XCD head map)."""
+    Bn, Hq, Hkv, Sq, Sk, causal = shape
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=causal, seed=700 + Sq + Sk)
+    R = _bf(I.make_rotation(128, seed=701)) if rotated else None
+    (o1, l1), (o2, l2) = _two_ways(B, c, R)
+    assert _same_bits(o1, o2), f"qbf16 output differs {shape} rot={rotated}"
+    assert _same_bits(l1, l2), f"qbf16 lse differs {shape} rot={rotated}"
+
+
+def test_fp8_qbf16_special_blocks_bit_identical(B):
+    """Q blocks that are all zero (scale 2^0), tiny, huge, or hold one
+    outlier row: the kernel's block maximum and E8M0 exponent follow the
+    quantizer's in every case."""
+    c = I.make_prefill(1, 4, 2, 640, 640, 128, causal=True, seed=711)
+    q = c.q.copy()
+    q[:, 0, 0:128] = 0.0
+    q[:, 1, 128:256] *= 1e-30
+    q[:, 2, 256:384] *= 1e4
+    q[:, 3, 400] *= 300.0
+    q[:, 0, 512:640] = -q[:, 0, 512:640]
+    c.q = I.round_to_bf16(q.astype(np.float32))
+    for R in (None, _bf(I.make_rotation(128, seed=712))):
+        (o1, l1), (o2, l2) = _two_ways(B, c, R)
+        assert _same_bits(o1, o2) and _same_bits(l1, l2), f"special blocks rot={R is not None}"
+
+
+def test_fp8_qbf16_headline_shape_bit_identical(B):
+    """B2 H16 S2048 causal with the rotation (the pair grid at the benchmark's
+    shape): bit-identical to quantize-then-forward, which the headline FP8
+    test holds to the oracle."""
+    c = I.workload("causal_mha_b2_h16_s2048_d128")
+    R = _bf(I.make_rotation(128, seed=2))
+    (o1, l1), (o2, l2) = _two_ways(B, c, R)
+    assert _same_bits(o1, o2) and _same_bits(l1, l2)
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 2, 150, 150, True), (1, 8, 2, 640, 640, True)], ids=["small", "pair"])
+def test_fp8_qbf16_matches_oracle(B, shape):
+    """fa_fwd_fp8_qbf16 against the oracle directly, with Q and K rotated on
+    the host so that both sides hold identical codes."""
+    Bn, Hq, Hkv, Sq, Sk, causal = shape
+    c = I.make_prefill(Bn, Hq, Hkv, Sq, Sk, 128, causal=causal, seed=720 + Sq)
+    R = I.make_rotation(128, seed=721).astype(np.float64)
+    c.q = I.round_to_bf16((c.q @ R.T).astype(np.float32))
+    c.k = I.round_to_bf16((c.k @ R.T).astype(np.float32))
+    _, _, k8, ks, v8, vs = B.fa_quantize_fp8_qkv(_bf(c.q), _bf(c.k), _bf(c.v))
+    o, lse = B.fa_fwd_fp8_qbf16(_bf(c.q), k8, ks, v8, vs, causal, scale=c.scale)
+    torch.cuda.synchronize()
+    O, L, vd, _ = oracle_fp8(c, None)
+    check_fp8_o(_np(o), O, vd, f"fp8 qbf16 {shape}")
+    check_lse(lse.cpu().numpy().astype(np.float64), L, f"fp8 qbf16 {shape}")
+
+
 def test_fp8_pair_barrier_timeout_is_reported(B):
     """The pair grid's wave-group barriers with their poll bound forced to 0
     from the host: waits run out, the device count says so and rows of the
