@@ -72,6 +72,7 @@ PROFILES = {
     PREFILL2K: _profile("fwd_bf16_causal_mha_b2_h16_s2048_d128"),
     DECODE: _profile("decode_paged_64seq_h32kv8_d128"),
     "fp8": _profile("fwd_fp8_causal_mha_b2_h16_s2048_d128"),
+    "fp8q": _profile("fwd_fp8_qbf16_causal_mha_b2_h16_s2048_d128"),
     "quant": _profile("quant_fp8_qkv_b2_h16_s2048_d128"),
     VERIFY: _profile("decode_multi_paged_64seq_q8_h32kv8_d128"),
     MLA: _profile("mla_decode_64seq_h16_dc512"),
@@ -460,6 +461,7 @@ def main():
             result["fp8"]["forward_q_bf16"] = {
                 "entry_point": "fa_fwd_fp8_qbf16", "kernel": "fwd_fp8_kernel<causal,pair,qbf16>",
                 "us": round(f_us, 2), "TFLOP/s": round(fl2k / (f_us * 1e-6) / 1e12, 1),
+                "traffic": profiling.current_profile(PROFILES["fp8q"])["traffic"],
                 "vs_bf16_forward": round(bf16_2k / f_us, 3) if bf16_2k else None,
                 "launch_us": us(st_f),
                 "note": "Q in bf16, rotated and quantized inside the forward (bit-identical to quantize + "
