@@ -332,6 +332,45 @@ def main():
         result["per_config"][FP32]["launch_us_alone"] = us(st_f)
         result["per_config"][FP32]["reps_alone"] = max(5, min(K * 3, 60))
 
+    # ---- FP8 forward at a long workload (the multi-round grid): rotated Q and
+    # K, V in 64-key blocks; the one-launch quantizer, the forward on the codes
+    # and the forward that quantizes Q itself, each timed on its own ----
+    fp8_long = {}
+
+    def fp8_at(name, q, k, v, scale, fl, bf16_us, reps):
+        rot = to_dev(inputs.bf16_bits(inputs.make_rotation(q.shape[-1], seed=2)))
+        q8, qs, k8, ks, v8, vs = binding.fa_quantize_fp8_qkv(q, k, v, rot=rot)
+        o8 = torch.empty_like(q)
+        l8 = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        st_q, _ = time_calls(lambda: binding.fa_quantize_fp8_qkv(q, k, v, rot=rot), reps, True, 0.1)
+        st_8, _ = time_calls(lambda: binding.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, scale, out=o8, lse=l8),
+                             reps, True, 0.1)
+        st_f, _ = time_calls(lambda: binding.fa_fwd_fp8_qbf16(q, k8, ks, v8, vs, True, rot=rot, scale=scale,
+                                                              out=o8, lse=l8), reps, True, 0.1)
+        peak8 = metrics.MI355X_FP8_DENSE_FLOPS / 1e12
+        t8, tf, tq = st_8["mean"] * 1e3, st_f["mean"] * 1e3, st_q["mean"] * 1e3
+        a8, af = fl / (t8 * 1e-6) / 1e12, fl / (tf * 1e-6) / 1e12
+        out = {
+            "workload": name, "kernel": "fwd_fp8_kernel<causal,grid>", "bound": "mfma", "achieved": round(a8, 1),
+            "peak": peak8, "unit": "TFLOP/s", "frac": round(a8 / peak8, 4), "launch_us": us(st_8), "reps": reps,
+            "forward_q_bf16": {"entry_point": "fa_fwd_fp8_qbf16", "us": round(tf, 2), "achieved": round(af, 1),
+                               "frac": round(af / peak8, 4), "launch_us": us(st_f)},
+            "quantize_qkv_us": round(tq, 2), "bf16_forward_us": round(bf16_us, 2),
+            "vs_bf16_forward": {"codes": round(bf16_us / t8, 3), "q_bf16": round(bf16_us / tf, 3),
+                                "quantize_qkv_plus_forward": round(bf16_us / (tq + t8), 3)},
+            "note": "codes of rotated Q and K and of V from one quantizer launch; caches flushed (512 MiB read) "
+                    "before each launch, outside its events",
+        }
+        del q8, qs, k8, ks, v8, vs, o8, l8
+        torch.cuda.empty_cache()
+        log(f"fp8 {name}: {t8:.1f} us ({a8 / peak8:.3f} of FP8 peak), Q quantized inside {tf:.1f} us, "
+            f"quantize {tq:.1f} us; bf16 {bf16_us:.1f} us")
+        return out
+
+    if not args.no_fp8:
+        fp8_long[HEADLINE] = fp8_at(HEADLINE, p_q, p_k, p_v, ch.scale, flops_p, sp["mean"] * 1e3,
+                                    max(3, min(K, 10)))
+
     # ---- the 2k and 8k prefill workloads, each on its own, cold caches ----
     if not args.no_extra:
         for name, reps in ((PREFILL2K, max(5, min(K * 3, 60))), (PREFILL8K, max(5, min(K * 3, 60)))):
@@ -355,6 +394,8 @@ def main():
             roof.update({"reps": reps, "host_lead": lead_x, "shape": {k_: s[k_] for k_ in ("B", "Hq", "Hkv", "Sq", "Sk", "d")}})
             result["per_config"][name] = roof
             log(f"{name}: {st['mean']*1e3:.1f} us -> {roof['achieved']:.1f} TFLOP/s ({roof['frac']:.3f} of peak)")
+            if name == PREFILL8K and not args.no_fp8:
+                fp8_long[name] = fp8_at(name, q, k, v, scale, fl, st["mean"] * 1e3, max(5, min(K, 20)))
             del q, k, v, o, lse
             torch.cuda.empty_cache()
 
@@ -468,6 +509,7 @@ def main():
                         "fa_fwd_fp8); K and V held in FP8 from an earlier quantization; caches flushed",
             }
             log(f"fp8: forward with Q quantized inside {f_us:.1f} us")
+            result["fp8"]["per_config"] = fp8_long
             del k8h, ksh, v8h, vsh
         del b_q, b_k, b_v, b_o, b_l, g_do, b_dq, b_dk, b_dv, b_ws
         torch.cuda.empty_cache()

@@ -140,33 +140,20 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
-// Stage the 128 x 128 bf16 rotation R (or the identity when rot is NULL) in
-// LDS with NT threads, all loads in flight together; 16-byte chunk c of row n
-// sits at chunk c ^ (n % 16), so operand reads of 32 rows and one chunk
-// spread over all banks.  The caller issues the barrier.
+// Stage the 128 x 128 bf16 rotation R in LDS with NT threads, all loads in
+// flight together; 16-byte chunk c of row n sits at chunk c ^ (n % 16), so
+// operand reads of 32 rows and one chunk spread over all banks.  The caller
+// issues the barrier.
 template <int NT>
 __device__ __forceinline__ void stage_rotation128(const uint16_t* __restrict__ rot, uint16_t* rt, int tid) {
     constexpr int D = 128;
     constexpr int NST = D * D / 8 / NT;
     static_assert(NST * NT * 8 == D * D, "staging split");
     u32x4 rv[NST];
-    if (rot != nullptr) {
 #pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            const int c = tid + NT * i;
-            rv[i] = *reinterpret_cast<const u32x4*>(rot + (c / (D / 8)) * D + 8 * (c % (D / 8)));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < NST; ++i) {
-            const int c = tid + NT * i;
-            const int n = c / (D / 8), ch = c % (D / 8);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int k0 = 8 * ch + 2 * k;
-                rv[i][k] = (k0 == n ? 0x3F80u : 0u) | (k0 + 1 == n ? 0x3F800000u : 0u);
-            }
-        }
+    for (int i = 0; i < NST; ++i) {
+        const int c = tid + NT * i;
+        rv[i] = *reinterpret_cast<const u32x4*>(rot + (c / (D / 8)) * D + 8 * (c % (D / 8)));
     }
 #pragma unroll
     for (int i = 0; i < NST; ++i) {

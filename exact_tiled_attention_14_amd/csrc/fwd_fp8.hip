@@ -165,7 +165,9 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     if constexpr (PAIR) {
         if (tid < 16) reinterpret_cast<int*>(lds + 2 * GROUP_LDS)[tid] = 0;
     }
-    if constexpr (QB) stage_rotation128<PAIR ? 2 * kThreads8 : kThreads8>(ROT, reinterpret_cast<uint16_t*>(lds + ROT_LDS), tid);
+    if constexpr (QB) {
+        if (ROT != nullptr) stage_rotation128<PAIR ? 2 * kThreads8 : kThreads8>(ROT, reinterpret_cast<uint16_t*>(lds + ROT_LDS), tid);
+    }
     if constexpr (PAIR || QB) __syncthreads();
     // barrier of the threads that share this workgroup's (or wave group's) K/V stages
     auto gsync = [&]() __attribute__((always_inline)) {
@@ -260,12 +262,25 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     // overlaps that of the first K/V loads.
     i32x8 qf[2];
     int sq;
-    bf16x8 xq[kD8 / 16];                // QB: this lane's bf16 row, head-dim 16 s + 8 h .. +7
+    // QB: this lane's bf16 row; with a rotation head-dim 16 s + 8 h .. +7 in xq[s]
+    // (the rotation product's operand), without one the entries
+    // 32 i + 8 a + 4 h .. +3 (a = 2 (s % 2) and a + 1, i = s / 2) that the
+    // product would have left in this lane
+    bf16x8 xq[kD8 / 16];
     if constexpr (QB) {
         // a row past Sq repeats row Sq - 1 (same block), so the block maximum is unchanged
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(Q) + (bhq * Sq + min(my_q, Sq - 1)) * kD8 + 8 * hh;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(Q) + (bhq * Sq + min(my_q, Sq - 1)) * kD8;
+        if (ROT != nullptr) {
 #pragma unroll
-        for (int s = 0; s < kD8 / 16; ++s) xq[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s);
+            for (int s = 0; s < kD8 / 16; ++s) xq[s] = *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hh);
+        } else {
+#pragma unroll
+            for (int s = 0; s < kD8 / 16; ++s) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(qp + 32 * (s >> 1) + 16 * (s & 1) + 4 * hh);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(qp + 32 * (s >> 1) + 16 * (s & 1) + 8 + 4 * hh);
+                xq[s] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+        }
     } else {
         sq = QS[bhq * n_qblk + qb];
         const uint8_t* qp = Q + (bhq * Sq + min(my_q, Sq - 1)) * kD8 + 32 * hh;
@@ -333,16 +348,33 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
         // E8M0 scale, E4M3 codes ----
         const uint16_t* rt = reinterpret_cast<const uint16_t*>(lds + ROT_LDS);
         f32x16 acc[4];
+        if (ROT != nullptr) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+            for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 #pragma unroll
-        for (int s = 0; s < kD8 / 16; ++s)
+            for (int s = 0; s < kD8 / 16; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int n = 32 * i + l32;
-                const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rt + n * kD8 + 8 * ((2 * s + hh) ^ (n & 15)));
-                acc[i] = mfma32(ra, xq[s], acc[i]);
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 32 * i + l32;
+                    const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rt + n * kD8 + 8 * ((2 * s + hh) ^ (n & 15)));
+                    acc[i] = mfma32(ra, xq[s], acc[i]);
+                }
+        } else {
+            // the values as they are (as the quantizer takes them without a rotation)
+#pragma unroll
+            for (int s = 0; s < kD8 / 16; ++s) {
+                const u32x4 w = __builtin_bit_cast(u32x4, xq[s]);
+                const int i = s >> 1, a = 2 * (s & 1);
+                acc[i][4 * a + 0] = bf16lo_to_f32(w[0]);
+                acc[i][4 * a + 1] = bf16hi_to_f32(w[0]);
+                acc[i][4 * a + 2] = bf16lo_to_f32(w[1]);
+                acc[i][4 * a + 3] = bf16hi_to_f32(w[1]);
+                acc[i][4 * a + 4] = bf16lo_to_f32(w[2]);
+                acc[i][4 * a + 5] = bf16hi_to_f32(w[2]);
+                acc[i][4 * a + 6] = bf16lo_to_f32(w[3]);
+                acc[i][4 * a + 7] = bf16hi_to_f32(w[3]);
             }
+        }
         float m = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i)

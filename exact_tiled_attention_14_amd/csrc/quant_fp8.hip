@@ -14,8 +14,8 @@
 //   * Row layout: each block of 64 or 128 rows of a [S, 128] slice is
 //     optionally rotated (each row x -> R x on the matrix cores as
 //     D = R X^T, R's rows being the A operand, staged in LDS once per
-//     workgroup; without R the identity is staged, which is exact), then
-//     written row-major.
+//     workgroup; without R the values are taken as they are, in the same
+//     lane order), then written row-major.
 //   * V layout: 64-key blocks of V (no rotation), written d-major: per block
 //     128 rows (one per head-dim index) of 64 bytes, the keys of a row in the
 //     order in which the attention kernel's lanes hold P (see include/fa.h),
@@ -90,7 +90,7 @@ __device__ __forceinline__ float unit_max(float m0, float m1, float* red, int wa
 // stores of a wave cover whole rows.  Wave w computes rows 32 w .. +31
 // against the four 32-row blocks of the rotation: D = Rot X^T, so lane l
 // holds entries n = 8 a + 4 h + e (h = l / 32) of the rotated row l % 32.
-template <int SB>
+template <int SB, bool DIRECT>
 __device__ __forceinline__ void rows_unit(uint8_t* __restrict__ X8, uint8_t* __restrict__ scales, int S, int nunit,
                                           int64_t u, const uint16_t* rt, uint8_t* tile, float* red, int tid,
                                           const u32x4 (&buf)[8]) {
@@ -107,21 +107,36 @@ __device__ __forceinline__ void rows_unit(uint8_t* __restrict__ X8, uint8_t* __r
     }
     __syncthreads();
     const int rr = wave * 32 + l32;                // this lane's row of the unit
-    bf16x8 xc[kQD / 16];
-#pragma unroll
-    for (int s = 0; s < kQD / 16; ++s)
-        xc[s] = *reinterpret_cast<const bf16x8*>(tile + rr * 256 + 16 * ((2 * s + hh) ^ (rr & 15)));
     f32x16 acc[4];
+    if constexpr (DIRECT) {
+        // no rotation: the same entries of the lane's row, read as they are
+        // (a product with the identity would turn -0 into +0)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int s = 0; s < kQD / 16; ++s) {
-        const bf16x8 xb = xc[s];
+            for (int a = 0; a < 4; ++a) {
+                const u32x2 w = *reinterpret_cast<const u32x2*>(tile + rr * 256 + 16 * ((4 * i + a) ^ (rr & 15)) + 8 * hh);
+                acc[i][4 * a + 0] = bf16lo_to_f32(w[0]);
+                acc[i][4 * a + 1] = bf16hi_to_f32(w[0]);
+                acc[i][4 * a + 2] = bf16lo_to_f32(w[1]);
+                acc[i][4 * a + 3] = bf16hi_to_f32(w[1]);
+            }
+    } else {
+        bf16x8 xc[kQD / 16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int n = 32 * i + l32;
-            const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rt + n * kQD + 8 * ((2 * s + hh) ^ (n & 15)));
-            acc[i] = mfma32(ra, xb, acc[i]);
+        for (int s = 0; s < kQD / 16; ++s)
+            xc[s] = *reinterpret_cast<const bf16x8*>(tile + rr * 256 + 16 * ((2 * s + hh) ^ (rr & 15)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+#pragma unroll
+        for (int s = 0; s < kQD / 16; ++s) {
+            const bf16x8 xb = xc[s];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = 32 * i + l32;
+                const bf16x8 ra = *reinterpret_cast<const bf16x8*>(rt + n * kQD + 8 * ((2 * s + hh) ^ (n & 15)));
+                acc[i] = mfma32(ra, xb, acc[i]);
+            }
         }
     }
     float m = 0.f;
@@ -242,7 +257,7 @@ struct QuantParts {
     int n;
 };
 
-template <int KIND>
+template <int KIND, bool DIRECT>
 __device__ __forceinline__ void run_part(const QuantPart& q, int64_t first, uint16_t* rt, uint8_t* tile, float* red,
                                          int tid) {
     // The thread index is made opaque in every call, so the many lane
@@ -254,7 +269,7 @@ __device__ __forceinline__ void run_part(const QuantPart& q, int64_t first, uint
         if constexpr (KIND == 2)
             v_unit(q.x8, q.scales, q.S, q.nunit, u, reinterpret_cast<uint16_t*>(tile), red, t, buf);
         else
-            rows_unit<KIND == 0 ? 128 : 64>(q.x8, q.scales, q.S, q.nunit, u, rt, tile, red, t, buf);
+            rows_unit<KIND == 0 ? 128 : 64, DIRECT>(q.x8, q.scales, q.S, q.nunit, u, rt, tile, red, t, buf);
     };
     auto load = [&](int64_t u, u32x4 (&buf)[8]) __attribute__((always_inline)) {
         int t = tid;
@@ -287,14 +302,19 @@ __global__ __launch_bounds__(kQThreads, 2) void quant_kernel(QuantParts parts, c
     const int64_t first = w - q.wg0;
     if (first >= q.units) return;                        // whole workgroup: no barrier reached
     if (q.kind == 2) {
-        run_part<2>(q, first, rt, tile, red, tid);
+        run_part<2, true>(q, first, rt, tile, red, tid);
+    } else if (rot == nullptr) {
+        if (q.kind == 0)
+            run_part<0, true>(q, first, rt, tile, red, tid);
+        else
+            run_part<1, true>(q, first, rt, tile, red, tid);
     } else {
         stage_rotation128<kQThreads>(rot, rt, tid);
         __syncthreads();
         if (q.kind == 0)
-            run_part<0>(q, first, rt, tile, red, tid);
+            run_part<0, false>(q, first, rt, tile, red, tid);
         else
-            run_part<1>(q, first, rt, tile, red, tid);
+            run_part<1, false>(q, first, rt, tile, red, tid);
     }
 }
 
