@@ -73,6 +73,8 @@ PROFILES = {
     DECODE: _profile("decode_paged_64seq_h32kv8_d128"),
     "fp8": _profile("fwd_fp8_causal_mha_b2_h16_s2048_d128"),
     "fp8q": _profile("fwd_fp8_qbf16_causal_mha_b2_h16_s2048_d128"),
+    ("fp8", PREFILL8K): _profile("fwd_fp8_causal_gqa_h32kv8_s8192_d128_outliers"),
+    ("fp8", HEADLINE): _profile("fwd_fp8_causal_gqa_h32kv8_s32768_d128"),
     "quant": _profile("quant_fp8_qkv_b2_h16_s2048_d128"),
     VERIFY: _profile("decode_multi_paged_64seq_q8_h32kv8_d128"),
     MLA: _profile("mla_decode_64seq_h16_dc512"),
@@ -353,6 +355,7 @@ def main():
         out = {
             "workload": name, "kernel": "fwd_fp8_kernel<causal,grid>", "bound": "mfma", "achieved": round(a8, 1),
             "peak": peak8, "unit": "TFLOP/s", "frac": round(a8 / peak8, 4), "launch_us": us(st_8), "reps": reps,
+            "traffic": profiling.current_profile(PROFILES[("fp8", name)])["traffic"],
             "forward_q_bf16": {"entry_point": "fa_fwd_fp8_qbf16", "us": round(tf, 2), "achieved": round(af, 1),
                                "frac": round(af / peak8, 4), "launch_us": us(st_f)},
             "quantize_qkv_us": round(tq, 2), "bf16_forward_us": round(bf16_us, 2),

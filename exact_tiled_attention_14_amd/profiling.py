@@ -79,6 +79,19 @@ def _run(args) -> None:
             go = torch.empty_like(gq)
             gl = torch.empty(gq.shape[:3], dtype=torch.float32, device=dev)
             launches.append((wl, lambda: binding.fa_fwd(gq, gk, gv, True, c.scale, out=go, lse=gl)))
+    for wl, name in (("fp8_8k", GQA8K), ("fp8_32k", GQA32K)):
+        # the FP8 forward on the same long workloads (codes of rotated Q and K, and V, quantized once)
+        if args.workload == wl:
+            c = inputs.workload(name)
+            gq, gk, gv = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
+            rot = to_dev(inputs.bf16_bits(inputs.make_rotation(c.q.shape[-1], seed=2)))
+            q8l, qsl, k8l, ksl, v8l, vsl = binding.fa_quantize_fp8_qkv(gq, gk, gv, rot=rot)
+            del gk, gv
+            go = torch.empty_like(gq)
+            gl = torch.empty(gq.shape[:3], dtype=torch.float32, device=dev)
+            torch.cuda.synchronize()
+            launches.append((wl, lambda: binding.fa_fwd_fp8(q8l, qsl, k8l, ksl, v8l, vsl, True, c.scale, out=go,
+                                                            lse=gl)))
     if args.workload in ("backward", "all"):
         c = inputs.workload(PREFILL)
         bq, bk, bv = to_dev(c.bits("q")), to_dev(c.bits("k")), to_dev(c.bits("v"))
@@ -314,7 +327,8 @@ def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
-    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "verify", "mla", "gqa8k", "gqa32k", "all"], default="all")
+    r.add_argument("--workload", choices=["prefill", "decode", "backward", "fp8", "verify", "mla", "gqa8k", "gqa32k",
+                                          "fp8_8k", "fp8_32k", "all"], default="all")
     r.add_argument("--reps", type=int, default=5)
     r.add_argument("--copy-mib", type=int, default=1024)
     s = sub.add_parser("summarize")
