@@ -645,9 +645,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
             const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
             // K/V blocks moved from group B to group A: B pays fixed extra costs
             // (a second job start, the light block's output) and its steps run
-            // slower than A's, so the best bias grows with n; measured best at
-            // 3, 5 and 5-8 blocks for n = 8, 16 and 32 query blocks.
-            const int split_bias = 2 + 3 * n_qblk / 16;
+            // slower than A's, so the best bias grows with n: 3, 4 and 6 blocks
+            // for n = 8, 16 and 32 query blocks (one block fewer than A and B's
+            // fixed costs alone suggest, since A's steps speed up once B is done).
+            const int split_bias = 2 + n_qblk / 8;
             launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                           a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0, split_bias,
