@@ -592,8 +592,10 @@ int num_cus8() {
 }
 
 // K/V blocks of the heavy query block moved from group B to group A of a pair
-// workgroup, for n query blocks.
-int fp8_split_bias(int n_qblk) { return 2 + 3 * n_qblk / 16; }
+// workgroup, for n query blocks: 4, 7 and 12 for n = 8, 16 and 32 (more than
+// the bf16 kernel's, since group B quantizes two Q blocks when it takes them
+// in bf16, and the plain form is flat over this range).
+int fp8_split_bias(int n_qblk) { return 2 + 5 * n_qblk / 16; }
 
 template <bool CAUSAL, bool QB>
 hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
