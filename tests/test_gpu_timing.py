@@ -82,6 +82,26 @@ def test_backward_timing_spans_three_kernels(B):
     assert all(torch.equal(x, y) for x, y in zip(r0, r1))
 
 
+def test_fp8_timing_spans_each_call(B):
+    """The one-launch quantizer, the FP8 forward on codes and the FP8 forward
+    that quantizes Q itself, each timed on its own as the bench times them."""
+    c = I.make_prefill(1, 8, 2, 1024, 1024, 128, causal=True, seed=94)
+    q, k, v = _bf(c.bits("q")), _bf(c.bits("k")), _bf(c.bits("v"))
+    R = _bf(I.bf16_bits(I.make_rotation(128, seed=94)))
+    q8, qs, k8, ks, v8, vs = B.fa_quantize_fp8_qkv(q, k, v, rot=R)
+    calls = {
+        "quantize": lambda: B.fa_quantize_fp8_qkv(q, k, v, rot=R),
+        "fp8": lambda: B.fa_fwd_fp8(q8, qs, k8, ks, v8, vs, True, c.scale),
+        "fp8_qbf16": lambda: B.fa_fwd_fp8_qbf16(q, k8, ks, v8, vs, True, rot=R, scale=c.scale),
+    }
+    for name, call in calls.items():
+        r0 = [t.clone() for t in call()]
+        t_kernel, t_marker, r1, _ = _timed(B, call)
+        print(f"{name}: kernel-boundary {t_kernel * 1e3:.1f} us, stream markers {t_marker * 1e3:.1f} us", flush=True)
+        assert 0.0 < t_kernel <= t_marker * 1.02 + 1e-3, name
+        assert all(torch.equal(x, y) for x, y in zip(r0, r1)), name
+
+
 def test_rejected_call_clears_the_hook(B):
     c = I.make_prefill(1, 16, 16, 2048, 2048, 128, causal=False, seed=92)
     q, k, v = _bf(c.bits("q")), _bf(c.bits("k")), _bf(c.bits("v"))
