@@ -638,10 +638,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     const int cus = num_cus();
     // Pair grid: a causal square problem whose query blocks, paired heavy with
     // light, fit one 8-wave workgroup per CU; every workgroup then walks the
-    // same number of K/V blocks.
+    // same number of K/V blocks.  With half the CUs or fewer taken by pairs,
+    // one block per workgroup (twice the workgroups, each on a CU of its own)
+    // finishes first: the heaviest block alone walks fewer K/V blocks than a
+    // pair, and a lone 4-wave workgroup gets a CU's LDS and VALU to itself.
     if constexpr (D == 128 && CAUSAL) {
         const int n_pairs = (n_qblk + 1) / 2;
-        if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
+        const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
+        if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && n_pair_wg <= cus && 2 * n_pair_wg > cus) {
             const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
             // K/V blocks moved from group B to group A: B pays fixed extra costs
             // (a second job start, the light block's output) and its steps run

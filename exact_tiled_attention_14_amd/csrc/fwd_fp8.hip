@@ -605,10 +605,12 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     const float scale_log2 = a.scale * kLog2e;
     const int cus = num_cus8();
     // Pair grid: a causal square problem whose query blocks, paired heavy with
-    // light, fit one 8-wave workgroup per CU.
+    // light, fit one 8-wave workgroup per CU and take more than half the CUs
+    // (with fewer pairs, one block per workgroup finishes first).
     if constexpr (CAUSAL) {
         const int n_pairs = (n_qblk + 1) / 2;
-        if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && (int64_t)a.B * a.Hq * n_pairs <= cus) {
+        const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
+        if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && n_pair_wg <= cus && 2 * n_pair_wg > cus) {
             const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
             launch_kernel((fwd_fp8_kernel<CAUSAL, true, QB>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,
                           (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale,

@@ -409,17 +409,36 @@ def test_binding_errors(B):
     assert e.value.status == B.FA_ERR_WORKSPACE
 
 
-# --- causal square problems that fit one 8-wave workgroup per CU: the pair
+# --- causal square problems whose heavy/light query-block pairs fit one
+# 8-wave workgroup per CU and take more than half of the 256 CUs: the pair
 # grid (heavy block n-1-p and light block p share a workgroup, the heavy one
 # split between its two wave groups and merged at the end) ----------------
 
-@pytest.mark.parametrize("shape", [(1, 2, 2, 1024), (1, 3, 1, 384), (2, 4, 2, 256), (1, 2, 1, 1152),
-                                   (1, 1, 1, 2048), (1, 16, 8, 1024), (1, 5, 5, 640)],
+PAIR_SHAPES = [(1, 36, 36, 1024), (1, 66, 22, 384), (2, 68, 34, 256), (1, 30, 15, 1152),
+               (1, 17, 17, 2048), (1, 40, 8, 1024), (1, 45, 45, 640)]
+
+
+def test_pair_shapes_take_the_pair_grid():
+    for b, hq, hkv, s in PAIR_SHAPES + [(1, 36, 36, 1024), (2, 20, 10, 1024)]:
+        assert 128 < b * hq * ((s // 128 + 1) // 2) <= 256, (b, hq, s)
+
+
+@pytest.mark.parametrize("shape", [(1, 16, 16, 1024), (1, 8, 2, 640), (2, 4, 2, 256)],
                          ids=lambda s: "B{}Hq{}Hkv{}S{}".format(*s))
+def test_underfilled_pair_shapes_match_oracle(B, shape):
+    # too few pairs to fill half the CUs: one query block per workgroup
+    b, hq, hkv, s = shape
+    assert b * hq * ((s // 128 + 1) // 2) <= 128
+    c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=13 * s + hq)
+    o, lse = run_fwd(B, c)
+    O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
+    check_o(o, O, "bf16", f"one-block grid {shape}")
+    check_lse(lse, L, f"one-block grid {shape}")
+
+
+@pytest.mark.parametrize("shape", PAIR_SHAPES, ids=lambda s: "B{}Hq{}Hkv{}S{}".format(*s))
 def test_pair_grid_matches_oracle(B, shape):
     b, hq, hkv, s = shape
-    n = s // 128
-    assert b * hq * ((n + 1) // 2) <= 256       # the pair grid applies (one workgroup per CU)
     c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=11 * s + hq)
     o, lse = run_fwd(B, c)
     O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
@@ -429,7 +448,7 @@ def test_pair_grid_matches_oracle(B, shape):
 
 def test_pair_grid_closed_forms(B):
     # V = 1 gives O = 1; Q = 0 gives the cumulative mean of V and lse = ln(#visible)
-    c = I.make_prefill(1, 2, 2, 1024, 1024, 128, causal=True, seed=9)
+    c = I.make_prefill(1, 36, 36, 1024, 1024, 128, causal=True, seed=9)
     q, k = _bf(c.bits("q")), _bf(c.bits("k"))
     ones = torch.ones_like(q)
     o, _ = B.fa_fwd(q, k, ones, True, c.scale)
@@ -441,13 +460,13 @@ def test_pair_grid_closed_forms(B):
     vv = _np(v)
     cum = np.cumsum(vv, axis=2) / np.arange(1, 1025)[None, None, :, None]
     check_o(_np(o), cum, "bf16", "pair grid q=0")
-    check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(np.arange(1, 1025.0)), (1, 2, 1024)),
+    check_lse(lse.cpu().numpy().astype(np.float64), np.broadcast_to(np.log(np.arange(1, 1025.0)), (1, 36, 1024)),
               "pair grid q=0 lse")
 
 
 def test_pair_grid_reports_no_barrier_timeout(B):
     B.fa_sync_timeouts()                      # clear what earlier calls left
-    c = I.make_prefill(2, 4, 2, 1024, 1024, 128, causal=True, seed=12)
+    c = I.make_prefill(2, 20, 10, 1024, 1024, 128, causal=True, seed=12)
     o, lse = run_fwd(B, c)
     assert np.isfinite(lse).all()
     assert B.fa_sync_timeouts() == 0
@@ -459,7 +478,7 @@ def test_pair_grid_barrier_timeout_is_reported(B):
     NaN, never a plausible result.  Every wait is bounded, so the kernel still
     exits normally; the bound applies to that one call only."""
     B.fa_sync_timeouts()
-    c = I.make_prefill(2, 4, 2, 1024, 1024, 128, causal=True, seed=12)
+    c = I.make_prefill(2, 20, 10, 1024, 1024, 128, causal=True, seed=12)
     q, k, v = _bf(c.bits("q")), _bf(c.bits("k")), _bf(c.bits("v"))
     B.fa_limit_next_sync_wait(0)
     o, lse = B.fa_fwd(q, k, v, True, c.scale)
