@@ -376,7 +376,8 @@ __global__ __launch_bounds__(kThreadsL, 2) void mla_partial_kernel(
         split_bf16x8(row_ok ? qraw[2 * ks] : f32x4{}, row_ok ? qraw[2 * ks + 1] : f32x4{}, qh[ks], ql[ks]);
     for (int it = 0; it < n_steps; it += 2) {
         step(it, crA);
-        step(it + 1, crB);                                 // past the chunk: every token masked
+        if (it + 1 >= n_steps) break;                      // uniform: no barrier is skipped by some waves only
+        step(it + 1, crB);
     }
 
     // every wave holds the same (m, l) per head; output this wave's slice
