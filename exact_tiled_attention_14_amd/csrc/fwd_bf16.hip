@@ -238,7 +238,8 @@ template <int D, bool CAUSAL, bool PAIR>
 __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Sq, int Sk,
-    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias, int sync_spins) {
+    float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias, int sync_spins,
+    int split_only) {
     using T = Tile<D>;
     constexpr int NS = D / 16;          // MFMA steps of one score block
     constexpr int NDB = D / 32;         // 32-wide head-dim blocks of the output
@@ -553,15 +554,17 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
 
     if constexpr (PAIR) {
         // Pair workgroup p of (b, hq): heavy block i = n-1-p and light block p
-        // (n query blocks; i == p for the middle block when n is odd).  Group A
+        // (n query blocks; i == p for the middle block when n is odd, and for
+        // every block of a split-only grid, whose workgroup r takes block
+        // n-1-r alone and halves it between the groups).  Group A
         // takes K/V blocks [0, split) of block i; group B the whole of block p,
         // then [split, 2i + 2) of block i, and the two groups run
         // unsynchronised on their own LDS stages.  An even split gives each
         // group n + 1 blocks, but group B also pays a second job start and the
         // light block's output; `split_bias` blocks move from B to A to even
         // out the finishing times.
-        const int p = rank, i = n_qblk - 1 - p;
-        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : (n_qblk + 1) / 2;
+        const int i = n_qblk - 1 - rank, p = split_only ? i : rank;
+        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : i + 1;
         if (grp == 0) {
             run_job(i, 0, split, false);
         } else {
@@ -639,14 +642,18 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     // Pair grid: a causal square problem whose query blocks, paired heavy with
     // light, fit one 8-wave workgroup per CU; every workgroup then walks the
     // same number of K/V blocks.  With half the CUs or fewer taken by pairs,
-    // one block per workgroup (twice the workgroups, each on a CU of its own)
-    // finishes first: the heaviest block alone walks fewer K/V blocks than a
-    // pair, and a lone 4-wave workgroup gets a CU's LDS and VALU to itself.
+    // a pair walks more K/V blocks than the heaviest block alone, so each
+    // block gets a workgroup of its own (all on CUs of their own): from 8
+    // query blocks on split between the two wave groups and merged like a
+    // pair's heavy block (split-only grid), below that as one 4-wave
+    // workgroup, where the halves are too short to repay the merge.
     if constexpr (D == 128 && CAUSAL) {
         const int n_pairs = (n_qblk + 1) / 2;
         const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
-        if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && n_pair_wg <= cus && 2 * n_pair_wg > cus) {
-            const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+        const bool fills = 2 * n_pair_wg > cus;
+        const int split_only = (!fills && n_qblk >= 8) ? 1 : 0;
+        if (a.Sq == a.Sk && a.Sq % kBM == 0 && n_qblk >= 2 && n_pair_wg <= cus && (fills || split_only)) {
+            const int64_t n_wg = split_only ? (int64_t)a.B * a.Hq * n_qblk : n_pair_wg;
             // K/V blocks moved from group B to group A: B pays fixed extra costs
             // (a second job start, the light block's output) and its steps run
             // slower than A's, so the best bias grows with n: 3, 4 and 6 blocks
@@ -655,8 +662,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
             const int split_bias = 2 + n_qblk / 8;
             launch_kernel((fwd_bf16_kernel<D, CAUSAL, true>), dim3((unsigned)n_wg), dim3(2 * kThreads), 0, stream,
                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_pairs, xcd_groups, 0, split_bias,
-                          a.sync_spins);
+                          a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, split_only ? n_qblk : n_pairs, xcd_groups, 0,
+                          split_bias, a.sync_spins, split_only);
             return hipGetLastError();
         }
     }
@@ -667,7 +674,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     launch_kernel((fwd_bf16_kernel<D, CAUSAL, false>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o,
                        a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk, n_qblk, xcd_groups, mirror, 0,
-                       a.sync_spins);
+                       a.sync_spins, 0);
     return hipGetLastError();
 }
 

@@ -141,7 +141,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
     const uint8_t* __restrict__ QS, const uint8_t* __restrict__ KS, const uint8_t* __restrict__ VS,
     const uint16_t* __restrict__ ROT, uint16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv,
     int Sq, int Sk, float scale_log2, int n_qblk, int n_rank, int xcd_groups, int mirror, int split_bias,
-    int sync_spins) {
+    int sync_spins, int split_only) {
     constexpr int GROUP_LDS = 4 * kTile8;      // K stages 0, 1 and V stages 0, 1
     // pair mode: both groups' stages, their barrier counters, the merge's (m, l);
     // QB: then the rotation (32 KiB) and the Q block maxima of the groups' waves
@@ -522,12 +522,14 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads8 : kThreads8, PAIR ? 1 : 2) voi
 
     if constexpr (PAIR) {
         // Pair workgroup p of (b, hq): heavy block i = n-1-p and light block p
-        // (i == p for the middle block when n is odd).  Group A takes K/V
+        // (i == p for the middle block when n is odd, and for every block of
+        // a split-only grid, whose workgroup r takes block n-1-r alone and
+        // halves it between the groups).  Group A takes K/V
         // blocks [0, split) of block i; group B the whole of block p, then
         // [split, 2i + 2) of block i; `split_bias` blocks move from B to A,
         // since B also pays a second job start and the light block's output.
-        const int p = rank, i = n_qblk - 1 - p;
-        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : (n_qblk + 1) / 2;
+        const int i = n_qblk - 1 - rank, p = split_only ? i : rank;
+        const int split = i != p ? min(n_qblk + 1 + split_bias, 2 * i + 2) : i + 1;
         if (grp == 0) {
             run_job(i, 0, split, false);
         } else {
@@ -605,17 +607,22 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     const float scale_log2 = a.scale * kLog2e;
     const int cus = num_cus8();
     // Pair grid: a causal square problem whose query blocks, paired heavy with
-    // light, fit one 8-wave workgroup per CU and take more than half the CUs
-    // (with fewer pairs, one block per workgroup finishes first).
+    // light, fit one 8-wave workgroup per CU and take more than half the CUs.
+    // With fewer pairs each block gets a workgroup of its own: from 8 query
+    // blocks on halved between the two wave groups (split-only grid), below
+    // that as one 4-wave workgroup.
     if constexpr (CAUSAL) {
         const int n_pairs = (n_qblk + 1) / 2;
         const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
-        if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && n_pair_wg <= cus && 2 * n_pair_wg > cus) {
-            const int64_t n_wg = (int64_t)a.B * a.Hq * n_pairs;
+        const bool fills = 2 * n_pair_wg > cus;
+        const int split_only = (!fills && n_qblk >= 8) ? 1 : 0;
+        if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && n_pair_wg <= cus && (fills || split_only)) {
+            const int64_t n_wg = split_only ? (int64_t)a.B * a.Hq * n_qblk : n_pair_wg;
             launch_kernel((fwd_fp8_kernel<CAUSAL, true, QB>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,
                           (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale,
                           a.v_scale, (const uint16_t*)a.rot, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk,
-                          scale_log2, n_qblk, n_pairs, xcd_groups, 0, fp8_split_bias(n_qblk), a.sync_spins);
+                          scale_log2, n_qblk, split_only ? n_qblk : n_pairs, xcd_groups, 0, fp8_split_bias(n_qblk),
+                          a.sync_spins, split_only);
             return hipGetLastError();
         }
     }
@@ -626,7 +633,7 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     launch_kernel((fwd_fp8_kernel<CAUSAL, false, QB>), dim3((unsigned)n_wg), dim3(kThreads8), 0, stream,
                   (const uint8_t*)a.q8, (const uint8_t*)a.k8, (const uint8_t*)a.v8, a.q_scale, a.k_scale, a.v_scale,
                   (const uint16_t*)a.rot, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, n_qblk,
-                  n_qblk, xcd_groups, mirror, 0, a.sync_spins);
+                  n_qblk, xcd_groups, mirror, 0, a.sync_spins, 0);
     return hipGetLastError();
 }
 

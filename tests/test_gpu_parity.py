@@ -423,10 +423,13 @@ def test_pair_shapes_take_the_pair_grid():
         assert 128 < b * hq * ((s // 128 + 1) // 2) <= 256, (b, hq, s)
 
 
-@pytest.mark.parametrize("shape", [(1, 16, 16, 1024), (1, 8, 2, 640), (2, 4, 2, 256)],
+@pytest.mark.parametrize("shape", [(1, 16, 16, 1024), (1, 8, 2, 2048), (1, 3, 1, 1152), (1, 1, 1, 1024),
+                                   (1, 8, 2, 640), (2, 4, 2, 256)],
                          ids=lambda s: "B{}Hq{}Hkv{}S{}".format(*s))
 def test_underfilled_pair_shapes_match_oracle(B, shape):
-    # too few pairs to fill half the CUs: one query block per workgroup
+    # too few pairs to fill half the CUs: one query block per workgroup, from
+    # 8 blocks on halved between two wave groups (even and odd n, GQA, a
+    # single head), below that one 4-wave workgroup
     b, hq, hkv, s = shape
     assert b * hq * ((s // 128 + 1) // 2) <= 128
     c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=13 * s + hq)
