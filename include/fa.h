@@ -443,19 +443,22 @@ int fa_time_next_call(void* start_event, void* stop_event);
 
 /*
  * fa_limit_next_sync_wait - diagnostic hook: bound every wave-group barrier
- * of the next fa_fwd, fa_fwd_fp8 or fa_bwd call on this thread to `spins`
- * polls instead of the default 2^22.
+ * of the next fa_fwd, fa_fwd_fp8, fa_fwd_fp8_qbf16 or fa_bwd call on this
+ * thread to `spins` polls instead of the default 2^22.
  *
  * The causal prefill (bf16 and FP8), and the dQ part of the causal backward,
  * that pair a heavy and a light query block in one workgroup (section 1 of
- * the FlashAttention scaling page: parallel over the sequence) synchronise
+ * the FlashAttention scaling page: parallel over the sequence), and the
+ * causal prefill that halves one query block between two wave groups when
+ * the pairs would fill half the GPU or less, synchronise
  * each of their two wave groups with a counter in LDS rather than the
  * workgroup barrier, with a bounded wait.  A wait that runs out is recorded
  * (see fa_sync_timeouts) and the rows of the waves it touched are written as
  * NaN (O and lse of the forward, dQ of the backward), so a timed-out call can
  * never pass for a correct one.  Tests use a small bound to see that report
  * while every kernel still exits normally.  The setting is cleared when that
- * fa_fwd, fa_fwd_fp8 or fa_bwd call returns, whatever its status.
+ * fa_fwd, fa_fwd_fp8, fa_fwd_fp8_qbf16 or fa_bwd call returns, whatever its
+ * status.
  *
  * Returns FA_OK, or FA_ERR_INVALID_ARG for spins < 0.
  */
