@@ -475,13 +475,16 @@ def test_pair_grid_reports_no_barrier_timeout(B):
     assert B.fa_sync_timeouts() == 0
 
 
-def test_pair_grid_barrier_timeout_is_reported(B):
+@pytest.mark.parametrize("shape", [(2, 20, 10, 1024), (1, 16, 16, 1024)], ids=["pair", "split_only"])
+def test_pair_grid_barrier_timeout_is_reported(B, shape):
     """The wave-group barriers' poll bound forced to 0 from the host: waits
     run out, the device count says so and the rows of the affected waves are
     NaN, never a plausible result.  Every wait is bounded, so the kernel still
-    exits normally; the bound applies to that one call only."""
+    exits normally; the bound applies to that one call only.  Covers the pair
+    grid and the split-only grid (one query block halved between the groups)."""
     B.fa_sync_timeouts()
-    c = I.make_prefill(2, 20, 10, 1024, 1024, 128, causal=True, seed=12)
+    b, hq, hkv, s = shape
+    c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=12)
     q, k, v = _bf(c.bits("q")), _bf(c.bits("k")), _bf(c.bits("v"))
     B.fa_limit_next_sync_wait(0)
     o, lse = B.fa_fwd(q, k, v, True, c.scale)
