@@ -165,7 +165,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) voi
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     float* __restrict__ delta, uint16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Sq, int Sk, float scale_log2,
-    float scale, int n_qblk, int split_bias, int sync_spins) {
+    float scale, int n_qblk, int split_bias, int sync_spins, int split_only) {
     // per wave group two stages of (K tile, V tile): the next block lands
     // while this one is used; pair mode adds the groups' barrier counters
     constexpr int GROUP_LDS = 2 * 2 * kKVBlk * kROWB;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreadsB : kThreadsB, PAIR ? 1 : 2) voi
     };   // run_job
 
     if constexpr (PAIR) {
-        const int p = rank, i = n_qblk - 1 - p;
+        const int i = n_qblk - 1 - rank, p = split_only ? i : rank;
         const int ni = blocks_of(i);
         const int split = i != p ? min(n_qblk + 1 + split_bias, ni) : (ni + 1) / 2;
         if (grp == 0) {
@@ -665,20 +665,24 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
     const int n_qblk = (a.Sq + kQRows - 1) / kQRows;
     const int n_pairs = (n_qblk + 1) / 2;
     // pair grid for dQ: a causal square problem whose heavy/light query-block
-    // pairs all fit one 8-wave workgroup per CU
-    if (CAUSAL && a.Sq == a.Sk && a.Sq % kQRows == 0 && n_qblk >= 2 &&
-        (int64_t)a.B * a.Hq * n_pairs <= bwd_cus()) {
-        launch_kernel<false>((bwd_dq_kernel<CAUSAL, true>), dim3((unsigned)((int64_t)a.B * a.Hq * n_pairs)),
+    // pairs all fit one 8-wave workgroup per CU; when they would fill half the
+    // CUs or fewer and there are 8 or more query blocks, each block gets a
+    // workgroup of its own, halved between the two wave groups (split-only)
+    const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
+    const int split_only = (2 * n_pair_wg <= bwd_cus() && n_qblk >= 8) ? 1 : 0;
+    if (CAUSAL && a.Sq == a.Sk && a.Sq % kQRows == 0 && n_qblk >= 2 && n_pair_wg <= bwd_cus()) {
+        launch_kernel<false>((bwd_dq_kernel<CAUSAL, true>),
+                             dim3((unsigned)(split_only ? (int64_t)a.B * a.Hq * n_qblk : n_pair_wg)),
                              dim3(2 * kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                              (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
                              (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, kDqSplitBias,
-                             a.sync_spins);
+                             a.sync_spins, split_only);
     } else {
         launch_kernel<false>((bwd_dq_kernel<CAUSAL, false>), dim3((unsigned)((int64_t)a.B * a.Hq * n_qblk)),
                              dim3(kThreadsB), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                              (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse, a.delta,
                              (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Sq, a.Sk, scale_log2, a.scale, n_qblk, 0,
-                             a.sync_spins);
+                             a.sync_spins, 0);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

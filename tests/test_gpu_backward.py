@@ -76,6 +76,8 @@ SHAPES = [
     (1, 8, 2, 640, 640, True),     # several full blocks, GQA; dQ pair grid with a middle block
     (1, 4, 4, 256, 256, True),     # dQ pair grid, two query blocks
     (2, 2, 1, 512, 512, True),     # dQ pair grid, MQA, four query blocks
+    (1, 4, 2, 1024, 1024, True),   # dQ split-only grid (few pairs, 8 query blocks), GQA
+    (1, 2, 1, 1152, 1152, True),   # dQ split-only grid, odd block count, MQA
 ]
 
 
@@ -158,14 +160,17 @@ def test_backward_binding_errors(B):
     assert e.value.status == B.FA_ERR_WORKSPACE
 
 
-def test_backward_pair_barrier_timeout_is_reported(B):
+@pytest.mark.parametrize("shape", [(1, 4, 4, 512), (1, 4, 2, 1024)], ids=["pair", "split_only"])
+def test_backward_pair_barrier_timeout_is_reported(B, shape):
     """The dQ pair grid's wave-group barriers with their poll bound forced to
     0 from the host: waits run out, the device count says so and the rows of
     the affected waves of dQ are NaN, never a plausible result.  Every wait is
     bounded, so the kernels still exit normally; the bound applies to that
-    one call only, and the next call matches the oracle."""
+    one call only, and the next call matches the oracle.  Covers the pair
+    grid and the split-only grid (one query block halved between the groups)."""
     B.fa_sync_timeouts()
-    c = I.make_prefill(1, 4, 4, 512, 512, 128, causal=True, seed=13)
+    b, hq, hkv, s = shape
+    c = I.make_prefill(b, hq, hkv, s, s, 128, causal=True, seed=13)
     do = I.make_grad_out(c.q.shape, seed=13)
     O, L = oracle.sdpa(c.q, c.k, c.v, True, c.scale)
     q, k, v = _bf(c.q), _bf(c.k), _bf(c.v)
