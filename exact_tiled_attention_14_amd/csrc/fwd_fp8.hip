@@ -608,14 +608,15 @@ hipError_t launch8(const Fp8FwdArgs& a, hipStream_t stream) {
     const int cus = num_cus8();
     // Pair grid: a causal square problem whose query blocks, paired heavy with
     // light, fit one 8-wave workgroup per CU and take more than half the CUs.
-    // With fewer pairs each block gets a workgroup of its own: from 8 query
-    // blocks on halved between the two wave groups (split-only grid), below
-    // that as one 4-wave workgroup.
+    // With fewer pairs each block gets a workgroup of its own: from 6 query
+    // blocks on halved between the two wave groups (split-only grid; with its
+    // vector-bound steps this kernel repays the merge two blocks earlier than
+    // the bf16 one), below that as one 4-wave workgroup.
     if constexpr (CAUSAL) {
         const int n_pairs = (n_qblk + 1) / 2;
         const int64_t n_pair_wg = (int64_t)a.B * a.Hq * n_pairs;
         const bool fills = 2 * n_pair_wg > cus;
-        const int split_only = (!fills && n_qblk >= 8) ? 1 : 0;
+        const int split_only = (!fills && n_qblk >= 6) ? 1 : 0;
         if (a.Sq == a.Sk && a.Sq % kBM8 == 0 && n_qblk >= 2 && n_pair_wg <= cus && (fills || split_only)) {
             const int64_t n_wg = split_only ? (int64_t)a.B * a.Hq * n_qblk : n_pair_wg;
             launch_kernel((fwd_fp8_kernel<CAUSAL, true, QB>), dim3((unsigned)n_wg), dim3(2 * kThreads8), 0, stream,

@@ -310,7 +310,8 @@ SHAPES = [
     (2, 34, 1, 384, 384, True),      # pair grid, MQA, odd
     (1, 40, 8, 1024, 1024, True),    # pair grid with the XCD head map (8 K/V heads), GQA
     (1, 8, 2, 640, 640, True),       # too few pairs to fill half the CUs: one block per workgroup
-    (1, 8, 2, 1024, 1024, True),     # too few pairs, 8 blocks: each block halved between two wave groups
+    (1, 4, 4, 768, 768, True),       # too few pairs, 6 blocks: each block halved between two wave groups
+    (1, 8, 2, 1024, 1024, True),     # the same with 8 blocks, GQA
     (1, 2, 1, 1152, 1152, True),     # the same with an odd number of blocks, MQA
 ]
 
